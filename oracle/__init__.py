@@ -1,0 +1,290 @@
+"""CPU oracle for VC-Attention (V-Smooth + ExpCast-FP8).
+
+TEST INFRASTRUCTURE ONLY.  This package is the plain, slow reference that
+the GPU library is checked against.  Only the test suite, the smoke check
+and the CPU-baseline leg of the benchmark may import it; the product path
+never does.  It shares no code with the HIP library: the arithmetic lives in
+``vc_oracle.c`` (plain C, compiled with gcc) and ``brute.py`` (NumPy fp64),
+and this module only marshals NumPy arrays into it.
+
+Every function states the passage of the VC-Attention pages it follows; the
+C source carries the step-by-step definitions.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "vc_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+BLK = 128
+
+CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-fno-fast-math",
+          "-ffp-contract=off", "-Wall", "-Wno-unused-function"]
+
+
+def build(force: bool = False) -> str:
+    """Compile vc_oracle.c into liboracle.so with gcc (no GPU involved)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def lib():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build()
+            L = ctypes.CDLL(_LIB)
+            P = ctypes.c_void_p
+            i32, i64, u64, f32 = ctypes.c_int, ctypes.c_int64, ctypes.c_uint64, ctypes.c_float
+            L.vco_e4m3_decode.restype = ctypes.c_double
+            L.vco_e4m3_decode.argtypes = [ctypes.c_uint8]
+            L.vco_e4m3_encode.restype = ctypes.c_uint8
+            L.vco_e4m3_encode.argtypes = [f32]
+            L.vco_e4m3_encode_array.argtypes = [P, P, i64]
+            L.vco_e4m3_decode_array.argtypes = [P, P, i64]
+            L.vco_splitmix64.restype = u64
+            L.vco_splitmix64.argtypes = [u64, u64]
+            L.vco_head_seed.restype = u64
+            L.vco_head_seed.argtypes = [u64, i32, i32, i32]
+            L.vco_kmeans_init_indices.argtypes = [i32, i32, u64, P]
+            L.vco_k_mean.argtypes = [P, i32, i32, P]
+            L.vco_kmeans.restype = ctypes.c_double
+            L.vco_kmeans.argtypes = [P, i32, i32, i32, i32, u64, P, P, P]
+            L.vco_stable_perm.argtypes = [P, i32, i32, P]
+            L.vco_prepare_head.argtypes = [P, P, P, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P]
+            L.vco_expcast.argtypes = [P, i64, f32, f32, P]
+            L.vco_expcast_rows.argtypes = [P, P, P, i64, P]
+            L.vco_kb.restype = f32
+            L.vco_kb.argtypes = [i32]
+            L.vco_c0.restype = f32
+            L.vco_c0.argtypes = [i32]
+            L.vco_attention_rows.argtypes = [i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P,
+                                             i32, i32, P, P, P]
+            L.vco_num_threads.restype = i32
+            L.vco_prepare.argtypes = [i32, i32, i32, i32, i32, i32, u64, i32, i32, P, P, P, P,
+                                      P, P, P, P, P, P, P, P, P]
+            _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+# --------------------------------------------------------------------------
+# E4M3FN codec (format definition; the "8 log2 v + 56" reading of the
+# MarkTechPost abstract fixes exponent bias 7).
+# --------------------------------------------------------------------------
+
+def e4m3_encode(x) -> np.ndarray:
+    """Saturating round-to-nearest-even fp32 -> E4M3FN byte."""
+    x = _c(x, np.float32)
+    out = np.empty(x.shape, np.uint8)
+    lib().vco_e4m3_encode_array(_p(x), _p(out), x.size)
+    return out
+
+
+def e4m3_decode(b) -> np.ndarray:
+    """E4M3FN byte -> exact value (float64)."""
+    b = _c(b, np.uint8)
+    out = np.empty(b.shape, np.float64)
+    lib().vco_e4m3_decode_array(_p(b), _p(out), b.size)
+    return out
+
+
+# --------------------------------------------------------------------------
+# Seeded draws (SplitMix64, counter-based).
+# --------------------------------------------------------------------------
+
+def splitmix64(seed: int, i: int) -> int:
+    return int(lib().vco_splitmix64(seed & (2**64 - 1), i))
+
+
+def head_seed(seed: int, b: int, h: int, H: int) -> int:
+    return int(lib().vco_head_seed(seed & (2**64 - 1), b, h, H))
+
+
+def kmeans_init_indices(L: int, k: int, seed_bh: int) -> np.ndarray:
+    out = np.empty(k, np.int32)
+    lib().vco_kmeans_init_indices(L, k, seed_bh, _p(out))
+    return out
+
+
+# --------------------------------------------------------------------------
+# V-Smooth preprocessing (agihunt summary, V-Smooth bullet; MarkTechPost
+# abstract; aikraft.ru "Reshenie").
+# --------------------------------------------------------------------------
+
+def k_mean(k_bf16_head: np.ndarray) -> np.ndarray:
+    k = _c(k_bf16_head, np.uint16)
+    L, d = k.shape
+    out = np.empty(d, np.float32)
+    lib().vco_k_mean(_p(k), L, d, _p(out))
+    return out
+
+
+def kmeans(v_bf16_head: np.ndarray, k: int, iters: int, seed_bh: int, history: bool = False):
+    """Lloyd k-means on one head's value rows.  Returns (assign, centroids, J)
+    or, with history=True, (assign, centroids, J_hist[iters+1])."""
+    v = _c(v_bf16_head, np.uint16)
+    L, d = v.shape
+    a = np.empty(L, np.int32)
+    C = np.empty((k, d), np.float32)
+    hist = np.empty(iters + 1, np.float64) if history else None
+    J = lib().vco_kmeans(_p(v), L, d, k, iters, seed_bh, _p(a), _p(C), _p(hist))
+    return (a, C, hist) if history else (a, C, J)
+
+
+def stable_perm(assign: np.ndarray, k: int) -> np.ndarray:
+    a = _c(assign, np.int32)
+    out = np.empty(a.size, np.int32)
+    lib().vco_stable_perm(_p(a), a.size, k, _p(out))
+    return out
+
+
+def nblocks(L: int) -> int:
+    return (L + BLK - 1) // BLK
+
+
+def prepare_head(q, k, v, perm, smooth_k: int = 1, v_mode: int = 0):
+    """Steps a1, a6-a8 for one head given the permutation.  q, k, v: bf16 bits
+    [L, d].  Returns a dict of q8 [Lp,d], k8 [Lp,d], v8 [nb,d,128] (natural
+    slot order), q_scale [nb], k_scale [nb], v_scale [nb,d], v_mean [nb,d],
+    kbar [d]."""
+    q, k, v = (_c(a, np.uint16) for a in (q, k, v))
+    perm = _c(perm, np.int32)
+    L, d = q.shape
+    nb = nblocks(L)
+    Lp = nb * BLK
+    o = dict(q8=np.empty((Lp, d), np.uint8), k8=np.empty((Lp, d), np.uint8),
+             v8=np.empty((nb, d, BLK), np.uint8), q_scale=np.empty(nb, np.float32),
+             k_scale=np.empty(nb, np.float32), v_scale=np.empty((nb, d), np.float32),
+             v_mean=np.empty((nb, d), np.float32), kbar=np.empty(d, np.float32))
+    lib().vco_prepare_head(_p(q), _p(k), _p(v), L, d, smooth_k, v_mode, _p(perm),
+                           _p(o["q8"]), _p(o["k8"]), _p(o["v8"]), _p(o["q_scale"]),
+                           _p(o["k_scale"]), _p(o["v_scale"]), _p(o["v_mean"]), _p(o["kbar"]))
+    return o
+
+
+def prepare(q, k, v, *, kmeans_k=0, kmeans_iters=8, seed=0, smooth_k=1, v_mode=0, perm_in=None):
+    """Whole-tensor prepare over [B,H,L,d] bf16 bits (OpenMP over heads)."""
+    q, k, v = (_c(a, np.uint16) for a in (q, k, v))
+    B, H, L, d = q.shape
+    nb = nblocks(L)
+    Lp = nb * BLK
+    o = dict(q8=np.empty((B, H, Lp, d), np.uint8), k8=np.empty((B, H, Lp, d), np.uint8),
+             v8=np.empty((B, H, nb, d, BLK), np.uint8), q_scale=np.empty((B, H, nb), np.float32),
+             k_scale=np.empty((B, H, nb), np.float32), v_scale=np.empty((B, H, nb, d), np.float32),
+             v_mean=np.empty((B, H, nb, d), np.float32), perm=np.empty((B, H, L), np.int32),
+             kmeans_obj=np.empty((B, H), np.float64))
+    pin = None if perm_in is None else _c(perm_in, np.int32)
+    lib().vco_prepare(B, H, L, d, kmeans_k, kmeans_iters, seed & (2**64 - 1), smooth_k, v_mode,
+                      _p(q), _p(k), _p(v), _p(pin), _p(o["q8"]), _p(o["k8"]), _p(o["v8"]),
+                      _p(o["q_scale"]), _p(o["k_scale"]), _p(o["v_scale"]), _p(o["v_mean"]),
+                      _p(o["perm"]), _p(o["kmeans_obj"]))
+    return o
+
+
+# --------------------------------------------------------------------------
+# ExpCast-FP8 (MarkTechPost abstract: one fused multiply-add from the
+# log2-domain score, beta = -0.35; aikraft.ru: p = 2^z written as E4M3).
+# --------------------------------------------------------------------------
+
+def KB(z_off: int = 8) -> np.float32:
+    return np.float32(lib().vco_kb(z_off))
+
+
+def C0(d: int) -> np.float32:
+    return np.float32(lib().vco_c0(d))
+
+
+def expcast(S, c8, krow) -> np.ndarray:
+    """byte = min(max(rne(fma(S, c8, krow)), 0), 126); c8, krow scalars or
+    arrays broadcastable to S."""
+    S = _c(S, np.float32)
+    if np.ndim(c8) == 0 and np.ndim(krow) == 0:
+        out = np.empty(S.shape, np.uint8)
+        lib().vco_expcast(_p(S), S.size, float(np.float32(c8)), float(np.float32(krow)), _p(out))
+        return out
+    c8a = _c(np.broadcast_to(np.float32(c8) if np.ndim(c8) == 0 else c8, S.shape), np.float32)
+    kra = _c(np.broadcast_to(np.float32(krow) if np.ndim(krow) == 0 else krow, S.shape), np.float32)
+    out = np.empty(S.shape, np.uint8)
+    lib().vco_expcast_rows(_p(S), _p(c8a), _p(kra), S.size, _p(out))
+    return out
+
+
+def expcast_z(z, z_off: int = 8) -> np.ndarray:
+    """ExpCast byte of p = 2^(z + z_off) for a log2-domain score z <= 0
+    (running max already subtracted): fma(z, 8, KB)."""
+    return expcast(z, np.float32(8.0), KB(z_off))
+
+
+# --------------------------------------------------------------------------
+# Blockwise attention (steps a9-a14).
+# --------------------------------------------------------------------------
+
+def attention_head(prep: dict, L: int, z_off: int = 8, rows=None, want_bytes=False):
+    """Quantised VC-Attention for one head from prepare_head() output.
+    rows: (r0, r1) or None for all.  Returns O [r1-r0, d] fp32 (and, with
+    want_bytes, the ExpCast bytes and S values [r1-r0, Lp] of every block)."""
+    q8 = _c(prep["q8"], np.uint8)
+    k8 = _c(prep["k8"], np.uint8)
+    v8 = _c(prep["v8"], np.uint8)
+    qs, ks = _c(prep["q_scale"], np.float32), _c(prep["k_scale"], np.float32)
+    vs, vm = _c(prep["v_scale"], np.float32), _c(prep["v_mean"], np.float32)
+    d = q8.shape[1]
+    Lp = k8.shape[0]
+    r0, r1 = (0, L) if rows is None else rows
+    out = np.empty((r1 - r0, d), np.float32)
+    by = np.empty((r1 - r0, Lp), np.uint8) if want_bytes else None
+    S = np.empty((r1 - r0, Lp), np.float32) if want_bytes else None
+    lib().vco_attention_rows(0, L, d, z_off, _p(q8), _p(k8), _p(v8), _p(qs), _p(ks), _p(vs),
+                             _p(vm), None, None, None, r0, r1, _p(out), _p(by), _p(S))
+    return (out, by, S) if want_bytes else out
+
+
+def attention_exact_blockwise(qf, kf_perm, v_perm, v_mean):
+    """Mode 1 of the blockwise loop: no quantisation, exact exp2, in double.
+    qf [L,d], kf_perm [L,d] keys in permuted order, v_perm [L,d] values in
+    permuted order, v_mean [nb,d] any per-block vector (the algebra must hold
+    for any mean).  Returns O [L,d] (fp32)."""
+    qf = _c(qf, np.float64)
+    L, d = qf.shape
+    nb = nblocks(L)
+    Lp = nb * BLK
+    kf = np.zeros((Lp, d), np.float64)
+    kf[:L] = kf_perm
+    vp = np.zeros((Lp, d), np.float64)
+    vp[:L] = v_perm
+    vm = _c(v_mean, np.float32)
+    rf = np.zeros((nb, d, BLK), np.float64)
+    for b in range(nb):
+        n = min(BLK, L - b * BLK)
+        rf[b, :, :n] = (vp[b * BLK:b * BLK + n] - vm[b].astype(np.float64)).T
+    out = np.empty((L, d), np.float32)
+    lib().vco_attention_rows(1, L, d, 8, None, None, None, None, None, None, _p(vm),
+                             _p(qf), _p(kf), _p(rf), 0, L, _p(out), None, None)
+    return out
+
+
+def num_threads() -> int:
+    return int(lib().vco_num_threads())
+
+
+from .brute import attention_f64, bf16_to_f32  # noqa: E402,F401

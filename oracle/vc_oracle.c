@@ -1,0 +1,556 @@
+/*
+ * vc_oracle.c -- CPU oracle for VC-Attention (V-Smooth + ExpCast-FP8).
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the plain, slow, obviously-correct
+ * reference that the GPU library is checked against.  Only the test suite,
+ * the smoke check and the CPU-baseline leg of the benchmark may load it.  It
+ * shares no code, header or constant table with the HIP library.
+ *
+ * Sources (web pages on VC-Attention, cited by page title and section):
+ *  [AGI]  "VC-Attention: Training-Free Low-Bit Attention Speeds Video
+ *         Diffusion Up to 3.6x" (agihunt summary): the V-Smooth and
+ *         ExpCast-FP8 bullet points.
+ *  [MTP]  "Nunchux AI Introduces VC-Attention ..." (yifor blog; the embedded
+ *         MarkTechPost English abstract and the section headed by the puzzle
+ *         emoji, "V-Smooth and ExpCast-FP8, two targeted designs").
+ *  [AIK]  aikraft.ru news item, section "Reshenie" (Solution).
+ *  [TRT]  TensorRT-LLM tech blog "Accelerating Video Generation with GEMM
+ *         Quantization, Attention Quantization and Skip Softmax Attention",
+ *         sections "Quantized Attention" and "Sparse Attention with Skip
+ *         Softmax".
+ *
+ * What is computed (all free choices are fixed here; each is a reading of the
+ * pages and is listed in the design doc):
+ *  - E4M3 is the OCP E4M3FN format (bias 7, max 448, no infinities): [MTP]
+ *    states that an E4M3 byte read as an integer is about 8*log2(v)+56, which
+ *    holds only with exponent bias 7.
+ *  - V-Smooth: tokens of one (batch, head) are grouped by a lightweight,
+ *    seeded k-means over the value rows ([AGI] V-Smooth bullet; [AIK]
+ *    "Reshenie"), sorted by cluster into 128-token blocks; each block keeps
+ *    its exact mean and only the residual is quantised ([AGI], [MTP]).
+ *  - ExpCast-FP8: the E4M3 byte of a probability is written directly from the
+ *    log2-domain score with one fused multiply-add, byte = round(8 z + 56 +
+ *    beta), beta = -0.35, clamped at zero ([MTP] abstract; [AIK]).
+ *  - Mean restore: the block mean is added back weighted by the row sum that
+ *    the online softmax keeps anyway ([AGI] V-Smooth bullet).
+ *  - Online (flash) softmax over 128-key blocks ([TRT] "Quantized Attention"
+ *    and "Sparse Attention with Skip Softmax" notation m~, m).
+ *
+ * Floating point: reductions are done in double and rounded once; the
+ * values this oracle promises to reproduce bit-for-bit (codes, scales,
+ * means, ExpCast bytes) are produced by IEEE single-precision operations
+ * written out one at a time.  Build with -O2 -fno-fast-math
+ * -ffp-contract=off so that no operation is fused or reordered.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define VCO_BLK 128
+
+/* ------------------------------------------------------------------------ */
+/* E4M3FN codec, written from the format definition: sign bit, 4 exponent    */
+/* bits with bias 7, 3 mantissa bits; exponent field 0 is subnormal          */
+/* (value = m * 2^-9); 0x7F / 0xFF are NaN; the largest finite is 0x7E = 448. */
+/* ------------------------------------------------------------------------ */
+
+double vco_e4m3_decode(uint8_t b)
+{
+    int s = (b >> 7) & 1;
+    int e = (b >> 3) & 15;
+    int m = b & 7;
+    double v;
+    if ((b & 0x7F) == 0x7F) return NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9);
+    else
+        v = ldexp(1.0 + m / 8.0, e - 7);
+    return s ? -v : v;
+}
+
+/* Round-to-nearest, ties-to-even, of a non-negative double that is an exact
+ * multiple of 1/2 away from any tie it may sit on. */
+static double vco_rne(double x)
+{
+    double f = floor(x);
+    double r = x - f;
+    if (r > 0.5) return f + 1.0;
+    if (r < 0.5) return f;
+    return (fmod(f, 2.0) == 0.0) ? f : f + 1.0;
+}
+
+/* Saturating round-to-nearest-even encoder (finite inputs only). */
+uint8_t vco_e4m3_encode(float xf)
+{
+    double x = (double)xf; /* exact */
+    uint8_t s = (x < 0.0 || (x == 0.0 && signbit(xf))) ? 0x80 : 0x00;
+    double a = fabs(x);
+    if (a >= 448.0) return s | 0x7E;
+    if (a < ldexp(1.0, -6)) {
+        /* subnormal range: value = m * 2^-9, m in 0..7; m = 8 is the
+         * smallest normal 0x08, so the code is simply the rounded m. */
+        double m = vco_rne(a * 512.0); /* exact scaling */
+        return s | (uint8_t)m;
+    }
+    int e = (int)floor(log2(a));
+    /* guard log2 rounding near powers of two */
+    while (ldexp(1.0, e) > a) e--;
+    while (ldexp(1.0, e + 1) <= a) e++;
+    double frac = (a / ldexp(1.0, e) - 1.0) * 8.0; /* exact: in [0, 8) */
+    double q = vco_rne(frac);
+    if (q >= 8.0) { q = 0.0; e += 1; }
+    int code = ((e + 7) << 3) | (int)q;
+    if (code > 0x7E) code = 0x7E; /* saturate (cannot exceed for a < 448) */
+    return s | (uint8_t)code;
+}
+
+void vco_e4m3_encode_array(const float* x, uint8_t* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; i++) out[i] = vco_e4m3_encode(x[i]);
+}
+
+void vco_e4m3_decode_array(const uint8_t* b, double* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; i++) out[i] = vco_e4m3_decode(b[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* SplitMix64 (Steele, Lea & Flood, OOPSLA 2014; finaliser "Mix13" of        */
+/* D. Stafford as in Vigna's public-domain reference).  Output i (0-based)    */
+/* of the stream started at `seed` is mix(seed + (i+1)*gamma): a counter-     */
+/* based generator, so any output can be computed independently.             */
+/* ------------------------------------------------------------------------ */
+
+#define VCO_GAMMA 0x9E3779B97F4A7C15ULL
+
+uint64_t vco_splitmix64(uint64_t seed, uint64_t i)
+{
+    uint64_t z = seed + (i + 1) * VCO_GAMMA;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+    return z ^ (z >> 31);
+}
+
+/* Seed of head (b, h): output number b*H+h of the stream seeded by `seed`. */
+uint64_t vco_head_seed(uint64_t seed, int b, int h, int H)
+{
+    return vco_splitmix64(seed, (uint64_t)b * (uint64_t)H + (uint64_t)h);
+}
+
+/* k distinct seeded token indices: token range [0, L) is cut into k
+ * contiguous strata [floor(c L / k), floor((c+1) L / k)); centroid c starts
+ * at a uniformly drawn token of stratum c.  Requires 1 <= k <= L. */
+void vco_kmeans_init_indices(int L, int k, uint64_t seed_bh, int32_t* idx)
+{
+    for (int c = 0; c < k; c++) {
+        int64_t lo = ((int64_t)c * L) / k;
+        int64_t hi = ((int64_t)(c + 1) * L) / k;
+        uint64_t r = vco_splitmix64(seed_bh, (uint64_t)c);
+        idx[c] = (int32_t)(lo + (int64_t)(r % (uint64_t)(hi - lo)));
+    }
+}
+
+static inline float vco_bf16(uint16_t u)
+{
+    uint32_t w = ((uint32_t)u) << 16;
+    float f;
+    memcpy(&f, &w, 4);
+    return f;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Step a1 (QK smoothing, K half): per-channel mean of K over all L tokens.  */
+/* The pages evaluate "after QK smoothing"; subtracting one vector from every */
+/* key adds a per-query constant to each score row, which softmax ignores.   */
+/* ------------------------------------------------------------------------ */
+
+void vco_k_mean(const uint16_t* k, int L, int d, float* kbar)
+{
+    for (int c = 0; c < d; c++) {
+        double s = 0.0;
+        for (int j = 0; j < L; j++) s += (double)vco_bf16(k[(int64_t)j * d + c]);
+        kbar[c] = (float)(s / (double)L);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Steps a2-a4: Lloyd k-means on x_j = fp32(V_j) of one head.                 */
+/*  assign: argmin_c sum_ch (x - C_c)^2 in double, ties -> lowest c;          */
+/*  update: C_c = fp32(double sum / n_c); an empty cluster keeps C_c.         */
+/* J_hist (iters+1 entries, may be NULL): J_hist[0] is the objective of the   */
+/* initial centroids under their own best assignment; J_hist[t] is the       */
+/* objective after t full (assign, update) rounds, measured with the t-th    */
+/* assignment and the t-th updated centroids.  Returns J_hist[iters].        */
+/* ------------------------------------------------------------------------ */
+
+static double vco_dist2(const float* x, const float* c, int d)
+{
+    double s = 0.0;
+    for (int i = 0; i < d; i++) {
+        double t = (double)x[i] - (double)c[i];
+        s += t * t;
+    }
+    return s;
+}
+
+static void vco_assign(const float* x, int L, int d, const float* C, int k, int32_t* a)
+{
+    for (int j = 0; j < L; j++) {
+        double best = INFINITY;
+        int bi = 0;
+        for (int c = 0; c < k; c++) {
+            double t = vco_dist2(x + (int64_t)j * d, C + (int64_t)c * d, d);
+            if (t < best) { best = t; bi = c; }
+        }
+        a[j] = bi;
+    }
+}
+
+static double vco_objective(const float* x, int L, int d, const float* C, const int32_t* a)
+{
+    double J = 0.0;
+    for (int j = 0; j < L; j++) J += vco_dist2(x + (int64_t)j * d, C + (int64_t)a[j] * d, d);
+    return J;
+}
+
+double vco_kmeans(const uint16_t* v, int L, int d, int k, int iters, uint64_t seed_bh,
+                  int32_t* assign, float* centroids, double* J_hist)
+{
+    float* x = (float*)malloc(sizeof(float) * (size_t)L * d);
+    int32_t* idx = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
+    double* sum = (double*)malloc(sizeof(double) * (size_t)k * d);
+    int64_t* cnt = (int64_t*)malloc(sizeof(int64_t) * (size_t)k);
+    for (int64_t i = 0; i < (int64_t)L * d; i++) x[i] = vco_bf16(v[i]);
+    vco_kmeans_init_indices(L, k, seed_bh, idx);
+    for (int c = 0; c < k; c++) memcpy(centroids + (int64_t)c * d, x + (int64_t)idx[c] * d, sizeof(float) * d);
+    if (J_hist) {
+        vco_assign(x, L, d, centroids, k, assign);
+        J_hist[0] = vco_objective(x, L, d, centroids, assign);
+    }
+    double J = 0.0;
+    for (int it = 0; it < iters; it++) {
+        vco_assign(x, L, d, centroids, k, assign);
+        memset(sum, 0, sizeof(double) * (size_t)k * d);
+        memset(cnt, 0, sizeof(int64_t) * (size_t)k);
+        for (int j = 0; j < L; j++) {
+            int c = assign[j];
+            cnt[c]++;
+            for (int i = 0; i < d; i++) sum[(int64_t)c * d + i] += (double)x[(int64_t)j * d + i];
+        }
+        for (int c = 0; c < k; c++)
+            if (cnt[c] > 0)
+                for (int i = 0; i < d; i++)
+                    centroids[(int64_t)c * d + i] = (float)(sum[(int64_t)c * d + i] / (double)cnt[c]);
+        J = vco_objective(x, L, d, centroids, assign);
+        if (J_hist) J_hist[it + 1] = J;
+    }
+    if (iters == 0) {
+        vco_assign(x, L, d, centroids, k, assign);
+        J = vco_objective(x, L, d, centroids, assign);
+    }
+    free(x); free(idx); free(sum); free(cnt);
+    return J;
+}
+
+/* Step a5: stable argsort of the assignment.  perm[i] = original token that
+ * lands in permuted slot i; slots are ordered by cluster id, then token id. */
+void vco_stable_perm(const int32_t* a, int L, int k, int32_t* perm)
+{
+    int64_t* start = (int64_t*)calloc((size_t)k + 1, sizeof(int64_t));
+    for (int j = 0; j < L; j++) start[a[j] + 1]++;
+    for (int c = 0; c < k; c++) start[c + 1] += start[c];
+    for (int j = 0; j < L; j++) perm[start[a[j]]++] = j;
+    free(start);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Scales.  A = amax of what the scale covers.                                */
+/*  mode 0: s = fp32(A/448), inv = fp32(448/A)  (IEEE single division)       */
+/*  mode 1: s = 2^e with e the least integer such that A <= 448 * 2^e;       */
+/*          inv = 2^-e exactly.                                              */
+/*  A < 2^-100 (in particular A == 0): s = inv = 0 and all codes are 0.      */
+/* ------------------------------------------------------------------------ */
+
+static void vco_scale(float A, int mode, float* s, float* inv)
+{
+    /* amax below 2^-100 (zero included) makes the whole group quantise to 0 */
+    if (!((double)A >= ldexp(1.0, -100))) { *s = 0.0f; *inv = 0.0f; return; }
+    if (mode == 0) {
+        volatile float num = 448.0f;
+        *s = A / num;
+        *inv = num / A;
+        return;
+    }
+    int e = -120;
+    while (!((double)A <= 448.0 * ldexp(1.0, e))) e++;
+    *s = (float)ldexp(1.0, e);
+    *inv = (float)ldexp(1.0, -e);
+}
+
+static inline uint8_t vco_quant(float x, float inv)
+{
+    volatile float y = x * inv; /* one IEEE single multiply */
+    return vco_e4m3_encode(y);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Steps a6-a8 for one head, given the permutation.                           */
+/*  q,k,v : bf16 bits [L, d] of this head                                     */
+/*  perm  : [L]                                                               */
+/*  q8,k8 : [Lp, d] codes (Q in original order, K' = K - kbar in perm order)  */
+/*  v8    : [nb, d, 128] residual codes, natural slot order inside a block    */
+/*  q_scale,k_scale : [nb]; v_scale,v_mean : [nb, d]                          */
+/* Padded slots (>= L) get code 0 and take no part in any mean or amax.       */
+/* ------------------------------------------------------------------------ */
+
+void vco_prepare_head(const uint16_t* q, const uint16_t* k, const uint16_t* v, int L, int d,
+                      int smooth_k, int v_mode, const int32_t* perm,
+                      uint8_t* q8, uint8_t* k8, uint8_t* v8, float* q_scale, float* k_scale,
+                      float* v_scale, float* v_mean, float* kbar_out)
+{
+    int nb = (L + VCO_BLK - 1) / VCO_BLK;
+    float* kbar = (float*)calloc((size_t)d, sizeof(float));
+    if (smooth_k) vco_k_mean(k, L, d, kbar);
+    if (kbar_out) memcpy(kbar_out, kbar, sizeof(float) * d);
+    float* buf = (float*)malloc(sizeof(float) * VCO_BLK * d);
+
+    for (int b = 0; b < nb; b++) {
+        int i0 = b * VCO_BLK;
+        int n = (L - i0 < VCO_BLK) ? L - i0 : VCO_BLK;
+
+        /* Q: original order, one scalar scale per block */
+        float A = 0.0f;
+        for (int i = 0; i < n; i++)
+            for (int c = 0; c < d; c++) {
+                float t = fabsf(vco_bf16(q[(int64_t)(i0 + i) * d + c]));
+                if (t > A) A = t;
+            }
+        float s, inv;
+        vco_scale(A, 0, &s, &inv);
+        q_scale[b] = s;
+        for (int i = 0; i < VCO_BLK; i++)
+            for (int c = 0; c < d; c++)
+                q8[(int64_t)(i0 + i) * d + c] =
+                    (i < n) ? vco_quant(vco_bf16(q[(int64_t)(i0 + i) * d + c]), inv) : 0;
+
+        /* K: permuted order, K' = fp32(K - kbar) */
+        A = 0.0f;
+        for (int i = 0; i < n; i++)
+            for (int c = 0; c < d; c++) {
+                volatile float t = vco_bf16(k[(int64_t)perm[i0 + i] * d + c]) - kbar[c];
+                buf[i * d + c] = t;
+                if (fabsf(t) > A) A = fabsf(t);
+            }
+        vco_scale(A, 0, &s, &inv);
+        k_scale[b] = s;
+        for (int i = 0; i < VCO_BLK; i++)
+            for (int c = 0; c < d; c++)
+                k8[(int64_t)(i0 + i) * d + c] = (i < n) ? vco_quant(buf[i * d + c], inv) : 0;
+
+        /* V: permuted order, exact block mean, residual, per-channel scale */
+        for (int c = 0; c < d; c++) {
+            double sum = 0.0;
+            for (int i = 0; i < n; i++) sum += (double)vco_bf16(v[(int64_t)perm[i0 + i] * d + c]);
+            float mu = (float)(sum / (double)n);
+            float Ac = 0.0f;
+            for (int i = 0; i < n; i++) {
+                volatile float r = vco_bf16(v[(int64_t)perm[i0 + i] * d + c]) - mu;
+                buf[i * d + c] = r;
+                if (fabsf(r) > Ac) Ac = fabsf(r);
+            }
+            float sv, iv;
+            vco_scale(Ac, v_mode, &sv, &iv);
+            v_mean[(int64_t)b * d + c] = mu;
+            v_scale[(int64_t)b * d + c] = sv;
+            for (int i = 0; i < VCO_BLK; i++)
+                v8[((int64_t)b * d + c) * VCO_BLK + i] = (i < n) ? vco_quant(buf[i * d + c], iv) : 0;
+        }
+    }
+    free(buf);
+    free(kbar);
+}
+
+/* ------------------------------------------------------------------------ */
+/* ExpCast-FP8 ([MTP] abstract, [AIK]): y = fma(S, c8, krow) with            */
+/* c8 = 8 c_b and krow = KB - 8 m; byte = min(max(rne(y), 0), 126).          */
+/* ------------------------------------------------------------------------ */
+
+static inline uint8_t vco_expcast1(float S, float c8, float krow)
+{
+    float y = fmaf(S, c8, krow);
+    double r = (y > 0.0f) ? vco_rne((double)y) : 0.0;
+    if (r > 126.0) r = 126.0;
+    return (uint8_t)r;
+}
+
+void vco_expcast(const float* S, int64_t n, float c8, float krow, uint8_t* out)
+{
+    for (int64_t i = 0; i < n; i++) out[i] = vco_expcast1(S[i], c8, krow);
+}
+
+/* Per-row arrays of (c8, krow), as a kernel would use them. */
+void vco_expcast_rows(const float* S, const float* c8, const float* krow, int64_t n, uint8_t* out)
+{
+    for (int64_t i = 0; i < n; i++) out[i] = vco_expcast1(S[i], c8[i], krow[i]);
+}
+
+/* KB = fp32(56 + beta + 8 z_off), beta = -0.35; C0 = fp32(log2(e)/sqrt(d)). */
+float vco_kb(int z_off) { return (float)(56.0 - 0.35 + 8.0 * (double)z_off); }
+float vco_c0(int d) { return (float)(1.4426950408889634074 / sqrt((double)d)); }
+
+/* ------------------------------------------------------------------------ */
+/* Steps a9-a14: blockwise attention for query rows [r0, r1) of one head.    */
+/*                                                                          */
+/* mode 0 (quantised, the method):                                          */
+/*   S_j   = fp32(exact sum_c qhat_c khat_jc)                                */
+/*   c_b   = fp32(fp32(s_q s_k,b) C0)                                        */
+/*   t     = fp32(max_valid S * c_b);  m' = max(m, t)                        */
+/*   krow  = fp32(KB - 8 m');  byte_j = ExpCast(S_j, 8 c_b, krow)            */
+/*   p_j   = decode(byte_j);  l_b = sum_j p_j                                */
+/*   acc_c = fp32(exact sum_j p_j rhat_jc)                                   */
+/*   alpha = 2^(m - m')   (0 on the first block)                             */
+/*   O     = alpha O + s_v,b (.) acc + l_b mu_b;  l = alpha l + l_b          */
+/* mode 1 (exact algebra, for checking the blockwise bookkeeping):          */
+/*   qhat, khat, rhat are the real values (scales 1), S is a double sum,      */
+/*   p_j = 2^(S_j C0 - m') in double; the rest as in mode 0.  With mode 1 the */
+/*   result equals softmax(Q K^T / sqrt(d)) V up to double rounding.         */
+/*                                                                          */
+/* Inputs for mode 0: q8,k8 [Lp,d], v8 [nb,d,128], scales and means as      */
+/* produced by vco_prepare_head.  For mode 1 pass qf [L,d], kf [Lp,d]         */
+/* (keys already in permuted order), rf [nb,d,128], v_mean; scales ignored.  */
+/* out: [r1-r0, d] fp32.  bytes_out (may be NULL): [r1-r0, Lp] ExpCast bytes */
+/* of the final pass, for byte-level checks.  S_out likewise (may be NULL).  */
+/* ------------------------------------------------------------------------ */
+
+void vco_attention_rows(int mode, int L, int d, int z_off,
+                        const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                        const float* q_scale, const float* k_scale,
+                        const float* v_scale, const float* v_mean,
+                        const double* qf, const double* kf, const double* rf,
+                        int r0, int r1, float* out, uint8_t* bytes_out, float* S_out)
+{
+    int nb = (L + VCO_BLK - 1) / VCO_BLK;
+    int64_t Lp = (int64_t)nb * VCO_BLK;
+    double dec[256]; /* decode table, filled from vco_e4m3_decode */
+    for (int t = 0; t < 256; t++) dec[t] = vco_e4m3_decode((uint8_t)t);
+    float C0 = vco_c0(d);
+    double C0d = 1.4426950408889634074 / sqrt((double)d);
+    float KB = vco_kb(z_off);
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int i = r0; i < r1; i++) {
+        double* qrow = (double*)malloc(sizeof(double) * d);
+        double* O = (double*)calloc((size_t)d, sizeof(double));
+        double* Sd = (double*)malloc(sizeof(double) * VCO_BLK);
+        float* S = (float*)malloc(sizeof(float) * VCO_BLK);
+        double* p = (double*)malloc(sizeof(double) * VCO_BLK);
+        for (int c = 0; c < d; c++)
+            qrow[c] = (mode == 0) ? dec[q8[(int64_t)i * d + c]] : qf[(int64_t)i * d + c];
+        double m = -INFINITY, l = 0.0;
+        for (int b = 0; b < nb; b++) {
+            int n = (L - b * VCO_BLK < VCO_BLK) ? L - b * VCO_BLK : VCO_BLK;
+            double m_new, ell = 0.0;
+            /* scores */
+            for (int j = 0; j < n; j++) {
+                int64_t kr = (int64_t)(b * VCO_BLK + j) * d;
+                double acc = 0.0;
+                for (int c = 0; c < d; c++)
+                    acc += qrow[c] * ((mode == 0) ? dec[k8[kr + c]] : kf[kr + c]);
+                Sd[j] = acc;
+                S[j] = (float)acc;
+            }
+            if (mode == 0) {
+                volatile float sqk = q_scale[i / VCO_BLK] * k_scale[b];
+                volatile float cb = sqk * C0;
+                float mx = -INFINITY;
+                for (int j = 0; j < n; j++) if (S[j] > mx) mx = S[j];
+                volatile float t = mx * cb;
+                float mnf = ((float)m > t) ? (float)m : t;
+                if (m == -INFINITY) mnf = t;
+                m_new = mnf;
+                volatile float e8 = 8.0f * mnf;
+                volatile float krow = KB - e8;
+                volatile float c8 = 8.0f * cb;
+                for (int j = 0; j < VCO_BLK; j++) {
+                    uint8_t by = (j < n) ? vco_expcast1(S[j], c8, krow) : 0;
+                    if (bytes_out) bytes_out[(int64_t)(i - r0) * Lp + b * VCO_BLK + j] = by;
+                    if (S_out) S_out[(int64_t)(i - r0) * Lp + b * VCO_BLK + j] = (j < n) ? S[j] : 0.0f;
+                    p[j] = dec[by];
+                    if (j < n) ell += p[j];
+                }
+            } else {
+                double mx = -INFINITY;
+                for (int j = 0; j < n; j++) if (Sd[j] * C0d > mx) mx = Sd[j] * C0d;
+                m_new = (m > mx) ? m : mx;
+                for (int j = 0; j < n; j++) { p[j] = exp2(Sd[j] * C0d - m_new); ell += p[j]; }
+            }
+            double alpha = (m == -INFINITY) ? 0.0 : exp2(m - m_new);
+            for (int c = 0; c < d; c++) {
+                int64_t vr = ((int64_t)b * d + c) * VCO_BLK;
+                double acc = 0.0;
+                for (int j = 0; j < n; j++)
+                    acc += p[j] * ((mode == 0) ? dec[v8[vr + j]] : rf[vr + j]);
+                double sv = (mode == 0) ? (double)v_scale[(int64_t)b * d + c] : 1.0;
+                double accr = (mode == 0) ? (double)(float)acc : acc;
+                O[c] = alpha * O[c] + sv * accr + ell * (double)v_mean[(int64_t)b * d + c];
+            }
+            l = alpha * l + ell;
+            m = m_new;
+        }
+        for (int c = 0; c < d; c++) out[(int64_t)(i - r0) * d + c] = (float)(O[c] / l);
+        free(qrow); free(O); free(Sd); free(S); free(p);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Whole-tensor drivers over B*H heads (OpenMP over heads).                  */
+/* ------------------------------------------------------------------------ */
+
+int vco_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* Full prepare.  perm_in may be NULL (k-means); perm_out receives the used
+ * permutation.  kmeans_obj may be NULL.  kmeans_k <= 0 means nb. */
+void vco_prepare(int B, int H, int L, int d, int kmeans_k, int kmeans_iters, uint64_t seed,
+                 int smooth_k, int v_mode, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                 const int32_t* perm_in, uint8_t* q8, uint8_t* k8, uint8_t* v8, float* q_scale,
+                 float* k_scale, float* v_scale, float* v_mean, int32_t* perm_out,
+                 double* kmeans_obj)
+{
+    int nb = (L + VCO_BLK - 1) / VCO_BLK;
+    int64_t Lp = (int64_t)nb * VCO_BLK;
+    int kk = (kmeans_k > 0) ? kmeans_k : nb;
+    int nh = B * H;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int bh = 0; bh < nh; bh++) {
+        int b = bh / H, h = bh % H;
+        int64_t off = (int64_t)bh * L * d;
+        int32_t* perm = perm_out + (int64_t)bh * L;
+        if (perm_in) {
+            memcpy(perm, perm_in + (int64_t)bh * L, sizeof(int32_t) * L);
+            if (kmeans_obj) kmeans_obj[bh] = NAN;
+        } else {
+            int32_t* a = (int32_t*)malloc(sizeof(int32_t) * L);
+            float* C = (float*)malloc(sizeof(float) * (size_t)kk * d);
+            double J = vco_kmeans(v + off, L, d, kk, kmeans_iters, vco_head_seed(seed, b, h, H), a, C, NULL);
+            vco_stable_perm(a, L, kk, perm);
+            if (kmeans_obj) kmeans_obj[bh] = J;
+            free(a); free(C);
+        }
+        vco_prepare_head(q + off, k + off, v + off, L, d, smooth_k, v_mode, perm,
+                         q8 + (int64_t)bh * Lp * d, k8 + (int64_t)bh * Lp * d,
+                         v8 + (int64_t)bh * nb * d * VCO_BLK, q_scale + (int64_t)bh * nb,
+                         k_scale + (int64_t)bh * nb, v_scale + (int64_t)bh * nb * d,
+                         v_mean + (int64_t)bh * nb * d, NULL);
+    }
+}

@@ -1,0 +1,186 @@
+"""Benchmark of the VC-Attention hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input: the
+V-Smooth prepare (seeded k-means, 8 Lloyd rounds, K smoothing, permutation,
+Q/K/V-residual FP8 quantisation) followed by the fused FP8 attention kernel.
+The default workload is the Wan2.2-shaped 720p case (B=1, H=40, L=75,600,
+d=128).  Inputs are resident in HBM before timing starts.
+
+Prints one JSON line.  `value` is attention FLOP (4 B H L^2 d) per step
+divided by the step time; the attention kernel alone, the BF16 kernel on the
+same inputs and the prepare stage are reported beside it, with the dominant
+kernel's roofline and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+FP8_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 matrix peak
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense BF16 matrix peak
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--config", type=int, default=2, help="workload index (0 tiny .. 4 cfg)")
+    p.add_argument("--cpu-rows", type=int, default=-1, help="query rows of the CPU oracle sample (-1: auto)")
+    p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--no-bf16", action="store_true")
+    p.add_argument("--v-scale-mode", type=int, default=0)
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(the workload shards by (batch, head) with no exchange; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from bit_attention_video_smooth_amd import api, synth
+
+    torch.cuda.set_device(0)
+    cfg = synth.CONFIGS[args.config]
+    B, H, L, d = cfg.B, cfg.H, cfg.L, cfg.d
+    flop = cfg.attn_flop
+    t0 = time.time()
+    qn, kn, vn = synth.make_inputs(cfg, args.config, threads=16)
+    print("inputs generated in %.1fs" % (time.time() - t0), file=sys.stderr, flush=True)
+    dev = lambda a: torch.from_numpy(a).view(torch.bfloat16).cuda()
+    q, k, v = dev(qn), dev(kn), dev(vn)
+    P = api.alloc_prepared(B, H, L, d)
+    ws = api.workspace(B, H, L, d)
+    out = torch.empty((B, H, L, d), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        api.prepare(q, k, v, seed=args.config, v_scale_mode=args.v_scale_mode, out=P, ws=ws)
+        if ev is not None:
+            ev[1].record(stream)
+        api.attention(P, out=out)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms_step = total_ms / args.steps
+    prep_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    attn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    print("step %.3f ms (prepare %.3f, attention %.3f)" % (ms_step, prep_ms, attn_ms), file=sys.stderr, flush=True)
+
+    # prepare without k-means (permutation reused, as across adjacent steps)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(args.steps):
+        api.prepare(q, k, v, perm_in=P.perm, out=P, ws=ws, v_scale_mode=args.v_scale_mode)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    quant_ms = ev[0].elapsed_time(ev[1]) / args.steps
+    E = B * H * L * d
+    nb = api.nblocks(L)
+    quant_bytes = 3 * E * 2 + 3 * E * 1 + B * H * nb * d * 8 + B * H * L * 4
+    bf16 = None
+    if not args.no_bf16:
+        ob = torch.empty((B, H, L, d), dtype=torch.float32, device="cuda")
+        api.attention_bf16(q, k, v, out=ob)
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        n16 = max(1, args.steps // 2)
+        for _ in range(n16):
+            api.attention_bf16(q, k, v, out=ob)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        bf16_ms = ev[0].elapsed_time(ev[1]) / n16
+        bf16 = {"ms": bf16_ms, "tflops": flop / bf16_ms / 1e9,
+                "frac_bf16_peak": flop / bf16_ms / 1e9 / BF16_PEAK_TFLOPS,
+                "fp8_speedup_over_bf16": bf16_ms / attn_ms}
+        print("bf16 attention %.3f ms" % bf16_ms, file=sys.stderr, flush=True)
+
+    attn_tflops = flop / attn_ms / 1e9
+    res = {
+        "metric": "FP8 attention TFLOP/s (4*B*H*L^2*d) & % FP8 MFMA peak, Wan2.2-shaped L=75,600",
+        "value": flop / ms_step / 1e9,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic (seeded video-token tensors, bf16)",
+        "config": {"workload": "%s: B=%d H=%d L=%d d=%d, V-Smooth k-means (k=%d, 8 rounds) + FP8 ExpCast attention"
+                               % (cfg.name, B, H, L, d, nb, ), "B": B, "H": H, "L": L, "d": d,
+                   "v_scale_mode": args.v_scale_mode},
+        "frac_fp8_peak_step": flop / ms_step / 1e9 / FP8_PEAK_TFLOPS,
+        "attention": {"ms": attn_ms, "tflops": attn_tflops, "frac_fp8_peak": attn_tflops / FP8_PEAK_TFLOPS},
+        "prepare": {"ms_with_kmeans": prep_ms, "ms_without_kmeans": quant_ms,
+                    "quant_algorithmic_bytes": quant_bytes,
+                    "quant_gbs": quant_bytes / quant_ms / 1e6},
+        "bf16_attention": bf16,
+        "roofline": {"bound": "mfma", "achieved": attn_tflops, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": attn_tflops / FP8_PEAK_TFLOPS, "traffic": None},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(cfg, qn, kn, vn, args.cpu_rows)
+    print(json.dumps(res))
+
+
+def cpu_baseline(cfg, qn, kn, vn, rows):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload:
+    one head prepared with the identity permutation, then blockwise
+    attention for `rows` query rows against all L keys; throughput is that
+    sample's attention FLOP over the oracle's attention time."""
+    import numpy as np
+
+    import oracle
+    L, d = cfg.L, cfg.d
+    perm = np.arange(L, dtype=np.int32)
+    t0 = time.time()
+    P = oracle.prepare_head(qn[0, 0], kn[0, 0], vn[0, 0], perm)
+    t_prep = time.time() - t0
+    if rows <= 0:  # size the sample to about 12 s of oracle time
+        probe = min(L, 4 * oracle.num_threads())
+        t0 = time.time()
+        oracle.attention_head(P, L, 8, rows=(0, probe))
+        per_row = (time.time() - t0) / probe
+        rows = int(max(probe, min(L, 12.0 / max(per_row, 1e-9))))
+    rows = min(rows, L)
+    t0 = time.time()
+    oracle.attention_head(P, L, 8, rows=(0, rows))
+    t_attn = time.time() - t0
+    fl = 4.0 * rows * L * d
+    return {"value": fl / t_attn / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "head (0,0) of %s: oracle prepare (identity permutation, %.2fs) then blockwise "
+                      "ExpCast attention for %d query rows x %d keys (%.2fs); k-means not included"
+                      % (cfg.name, t_prep, rows, L, t_attn)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,147 @@
+"""Torch-tensor conveniences over the C ABI: allocate outputs, call the
+library, return tensors.  No arithmetic of the method happens here."""
+from __future__ import annotations
+
+import dataclasses
+
+import torch
+
+from . import _lib
+
+BLK = 128
+
+
+def nblocks(L: int) -> int:
+    return (L + BLK - 1) // BLK
+
+
+@dataclasses.dataclass
+class Prepared:
+    shape: tuple
+    q8: torch.Tensor
+    k8: torch.Tensor
+    v8: torch.Tensor
+    q_scale: torch.Tensor
+    k_scale: torch.Tensor
+    v_scale: torch.Tensor
+    v_mean: torch.Tensor
+    perm: torch.Tensor
+    kmeans_obj: torch.Tensor
+
+    def c(self) -> _lib.vc_prepared:
+        return _lib.vc_prepared(*(t.data_ptr() for t in (
+            self.q8, self.k8, self.v8, self.q_scale, self.k_scale, self.v_scale, self.v_mean,
+            self.perm, self.kmeans_obj)))
+
+
+def alloc_prepared(B, H, L, d, device="cuda") -> Prepared:
+    nb = nblocks(L)
+    Lp = nb * BLK
+    u8 = dict(dtype=torch.uint8, device=device)
+    f32 = dict(dtype=torch.float32, device=device)
+    return Prepared((B, H, L, d),
+                    torch.empty((B, H, Lp, d), **u8), torch.empty((B, H, Lp, d), **u8),
+                    torch.empty((B, H, nb, d, BLK), **u8),
+                    torch.empty((B, H, nb), **f32), torch.empty((B, H, nb), **f32),
+                    torch.empty((B, H, nb, d), **f32), torch.empty((B, H, nb, d), **f32),
+                    torch.empty((B, H, L), dtype=torch.int32, device=device),
+                    torch.empty((B, H), dtype=torch.float64, device=device))
+
+
+def workspace(B, H, L, d, *, kmeans_k=0, kmeans_iters=8, device="cuda") -> torch.Tensor:
+    n = _lib.vsmooth_workspace_bytes(_lib.shape_of(B, H, L, d),
+                                     _lib.make_params(kmeans_k, kmeans_iters))
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def prepare(q, k, v, *, perm_in=None, kmeans_k=0, kmeans_iters=8, seed=0, smooth_k=1,
+            v_scale_mode=0, out: Prepared | None = None, ws: torch.Tensor | None = None,
+            stream=None) -> Prepared:
+    """vsmooth_prepare on bf16 [B,H,L,d] device tensors."""
+    B, H, L, d = q.shape
+    for t in (q, k, v):
+        assert t.dtype == torch.bfloat16 and t.is_contiguous() and t.shape == q.shape
+    if perm_in is not None:
+        assert perm_in.dtype == torch.int32 and perm_in.is_contiguous() and tuple(perm_in.shape) == (B, H, L)
+    shape = _lib.shape_of(B, H, L, d)
+    params = _lib.make_params(kmeans_k, kmeans_iters, seed, smooth_k, v_scale_mode)
+    out = out if out is not None else alloc_prepared(B, H, L, d, q.device)
+    if ws is None:
+        ws = workspace(B, H, L, d, kmeans_k=kmeans_k, kmeans_iters=kmeans_iters, device=q.device)
+    _lib.vsmooth_prepare(shape, params, q, k, v, perm_in, out.c(), ws, ws.numel(), stream)
+    return out
+
+
+def attention(prep: Prepared, *, z_off=8, out_dtype=torch.float32, out=None, stream=None):
+    """vc_attention_fwd: O [B,H,L,d] in fp32 or bf16."""
+    B, H, L, d = prep.shape
+    if out is None:
+        out = torch.empty((B, H, L, d), dtype=out_dtype, device=prep.q8.device)
+    od = 1 if out.dtype == torch.bfloat16 else 0
+    _lib.vc_attention_fwd(_lib.shape_of(B, H, L, d), _lib.vc_attn_params(z_off, od), prep.c(), out,
+                          stream)
+    return out
+
+
+def attention_dump(prep: Prepared, bh: int, q_tile: int, *, z_off=8, stream=None):
+    """vc_attention_fwd_dump: returns (O fp32, S [256, Lp] fp32, P [256, Lp] u8)."""
+    B, H, L, d = prep.shape
+    Lp = nblocks(L) * BLK
+    dev = prep.q8.device
+    out = torch.empty((B, H, L, d), dtype=torch.float32, device=dev)
+    s = torch.zeros((256, Lp), dtype=torch.float32, device=dev)
+    p = torch.zeros((256, Lp), dtype=torch.uint8, device=dev)
+    _lib.vc_attention_fwd_dump(_lib.shape_of(B, H, L, d), _lib.vc_attn_params(z_off, 0), prep.c(), out,
+                               bh, q_tile, s, p, stream)
+    return out, s, p
+
+
+def attention_bf16(q, k, v, *, out_dtype=torch.float32, out=None, stream=None):
+    """vc_attention_fwd_bf16 on bf16 [B,H,L,d] device tensors."""
+    B, H, L, d = q.shape
+    for t in (q, k, v):
+        assert t.dtype == torch.bfloat16 and t.is_contiguous() and t.shape == q.shape
+    if out is None:
+        out = torch.empty((B, H, L, d), dtype=out_dtype, device=q.device)
+    od = 1 if out.dtype == torch.bfloat16 else 0
+    _lib.vc_attention_fwd_bf16(_lib.shape_of(B, H, L, d), q, k, v, out, od, stream)
+    return out
+
+
+def expcast(S, c8, krow, stream=None):
+    n = S.numel()
+    out = torch.empty(S.shape, dtype=torch.uint8, device=S.device)
+    _lib.vc_debug_expcast(S, c8, krow, n, out, stream)
+    return out
+
+
+def e4m3_encode(x, stream=None):
+    out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    _lib.vc_debug_e4m3_encode(x, x.numel(), out, stream)
+    return out
+
+
+def mfma_fp8(a, b, stream=None):
+    n = a.shape[0]
+    c = torch.empty((n, 16, 16), dtype=torch.float32, device=a.device)
+    _lib.vc_debug_mfma_fp8(a, b, c, n, stream)
+    return c
+
+
+# Slot order of a 128-key block in the V residual layout (vc_attention.h):
+# slot pos holds key kk with pos = 32*((kk%16)//4) + 4*(kk//16) + (kk%4).
+def key_of_slot():
+    import numpy as np
+    pos = np.arange(BLK)
+    return 16 * ((pos % 32) // 4) + 4 * (pos // 32) + (pos % 4)
+
+
+def v_codes_natural(v8):
+    """Reorder the V residual codes [..., 128 slots] into natural key order."""
+    import numpy as np
+    kos = key_of_slot()
+    inv = np.empty(BLK, np.int64)
+    inv[kos] = np.arange(BLK)
+    if isinstance(v8, torch.Tensor):
+        return v8[..., torch.as_tensor(inv, device=v8.device)]
+    return v8[..., inv]

@@ -1,0 +1,282 @@
+// vc_abi.hip -- the C ABI of the VC-Attention library (declared in
+// include/vc_attention.h): host-side argument checks, workspace carving and
+// kernel dispatch.  Nothing here allocates device memory or synchronises.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "vc_attention.h"
+#include "vc_internal.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int ok() {
+    g_err.clear();
+    return VC_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_ptr(const void* p, const char* name) {
+    if (p == nullptr) return fail(VC_ERR_INVALID, "%s is NULL", name);
+    if (!aligned16(p)) return fail(VC_ERR_INVALID, "%s is not 16-byte aligned", name);
+    return VC_OK;
+}
+
+int check_shape(const vc_shape* s) {
+    if (s == nullptr) return fail(VC_ERR_INVALID, "shape is NULL");
+    if (s->B < 1 || s->H < 1 || s->L < 1)
+        return fail(VC_ERR_INVALID, "shape B=%d H=%d L=%d must all be >= 1", s->B, s->H, s->L);
+    if (s->d != 64 && s->d != 128) return fail(VC_ERR_UNSUPPORTED, "head dim d=%d (supported: 64, 128)", s->d);
+    const int64_t nb = ((int64_t)s->L + 127) / 128;
+    const int64_t elems = (int64_t)s->B * s->H * nb * 128 * s->d;
+    if ((int64_t)s->B * s->H > (1 << 20) || elems > ((int64_t)1 << 40))
+        return fail(VC_ERR_INVALID, "shape too large");
+    if ((int64_t)s->B * s->H * ((s->L + vc::ATTN_BM - 1) / vc::ATTN_BM) > 0x7FFFFFFF)
+        return fail(VC_ERR_INVALID, "shape too large for one launch");
+    return VC_OK;
+}
+
+int nblk(const vc_shape* s) { return (s->L + 127) / 128; }
+
+int hip_status(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(VC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+int check_params(const vc_shape* s, const vsmooth_params* p, int* kk) {
+    if (p == nullptr) return fail(VC_ERR_INVALID, "params is NULL");
+    if (p->block != 128) return fail(VC_ERR_UNSUPPORTED, "block=%d (only 128 is supported)", p->block);
+    if (p->kmeans_iters < 0 || p->kmeans_iters > 1000)
+        return fail(VC_ERR_INVALID, "kmeans_iters=%d out of range [0, 1000]", p->kmeans_iters);
+    if (p->smooth_k != 0 && p->smooth_k != 1) return fail(VC_ERR_INVALID, "smooth_k must be 0 or 1");
+    if (p->v_scale_mode != 0 && p->v_scale_mode != 1)
+        return fail(VC_ERR_INVALID, "v_scale_mode must be 0 or 1");
+    if (p->reserved != 0) return fail(VC_ERR_INVALID, "reserved must be 0");
+    const int k = p->kmeans_k > 0 ? p->kmeans_k : nblk(s);
+    if (k > s->L) return fail(VC_ERR_INVALID, "kmeans_k=%d exceeds L=%d", k, s->L);
+    if (k > 16384) return fail(VC_ERR_INVALID, "kmeans_k=%d exceeds 16384", k);
+    *kk = k;
+    return VC_OK;
+}
+
+size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t prepare_ws(const vc_shape* s, bool kmeans, int k) {
+    const size_t BH = (size_t)s->B * s->H;
+    const int ns = vc::k_mean_splits((int)BH, s->L);
+    size_t b = a256(BH * ns * s->d * sizeof(double)) + a256(BH * s->d * sizeof(float));
+    if (kmeans) b += vc::kmeans_workspace_bytes(s->B, s->H, s->L, s->d, k);
+    return b;
+}
+
+int check_prepared(const vc_prepared* p, bool need_obj) {
+    if (p == nullptr) return fail(VC_ERR_INVALID, "prepared is NULL");
+    int r;
+    if ((r = check_ptr(p->q8, "q8")) || (r = check_ptr(p->k8, "k8")) || (r = check_ptr(p->v8, "v8")) ||
+        (r = check_ptr(p->q_scale, "q_scale")) || (r = check_ptr(p->k_scale, "k_scale")) ||
+        (r = check_ptr(p->v_scale, "v_scale")) || (r = check_ptr(p->v_mean, "v_mean")))
+        return r;
+    (void)need_obj;
+    return VC_OK;
+}
+
+int attention_common(const vc_shape* shape, const vc_attn_params* params, const vc_prepared* in,
+                     void* out, int32_t bh, int32_t q_tile, float* s_dump, uint8_t* p_dump,
+                     bool dump, hipStream_t stream) {
+    int r;
+    if ((r = check_shape(shape))) return r;
+    if (params == nullptr) return fail(VC_ERR_INVALID, "params is NULL");
+    if (params->z_off < 0 || params->z_off > 8) return fail(VC_ERR_INVALID, "z_off=%d out of [0, 8]", params->z_off);
+    if (params->out_dtype != 0 && params->out_dtype != 1)
+        return fail(VC_ERR_INVALID, "out_dtype must be 0 (fp32) or 1 (bf16)");
+    if ((r = check_prepared(in, false))) return r;
+    if ((r = check_ptr(out, "out"))) return r;
+    vc::AttnArgs a{};
+    a.q8 = in->q8; a.k8 = in->k8; a.v8 = in->v8;
+    a.q_scale = in->q_scale; a.k_scale = in->k_scale; a.v_scale = in->v_scale; a.v_mean = in->v_mean;
+    a.out = out;
+    a.L = shape->L;
+    a.nb = nblk(shape);
+    a.BH = shape->B * shape->H;
+    a.nqt = (shape->L + vc::ATTN_BM - 1) / vc::ATTN_BM;
+    a.C0 = (float)(1.4426950408889634074 / sqrt((double)shape->d));
+    a.KB = (float)(56.0 - 0.35 + 8.0 * (double)params->z_off);
+    a.dump_bh = -1;
+    a.dump_qt = -1;
+    if (dump) {
+        if (bh < 0 || bh >= a.BH) return fail(VC_ERR_INVALID, "bh=%d out of range", bh);
+        if (q_tile < 0 || q_tile >= a.nqt) return fail(VC_ERR_INVALID, "q_tile=%d out of range", q_tile);
+        if ((r = check_ptr(s_dump, "s_dump")) || (r = check_ptr(p_dump, "p_dump"))) return r;
+        a.dump_bh = bh;
+        a.dump_qt = q_tile;
+        a.s_dump = s_dump;
+        a.p_dump = p_dump;
+    }
+    return hip_status(vc::launch_attn_fp8(a, shape->d, params->out_dtype, dump, stream), "vc_attention_fwd");
+}
+
+}  // namespace
+
+extern "C" {
+
+int vc_version(void) { return VC_ATTENTION_VERSION; }
+
+const char* vc_last_error(void) { return g_err.c_str(); }
+
+int vc_prepared_sizes(const vc_shape* s, size_t bytes[9]) {
+    int r;
+    if ((r = check_shape(s))) return r;
+    if (bytes == nullptr) return fail(VC_ERR_INVALID, "bytes is NULL");
+    const size_t BH = (size_t)s->B * s->H, nb = nblk(s), Lp = nb * 128, d = s->d;
+    bytes[0] = BH * Lp * d;
+    bytes[1] = BH * Lp * d;
+    bytes[2] = BH * nb * d * 128;
+    bytes[3] = BH * nb * 4;
+    bytes[4] = BH * nb * 4;
+    bytes[5] = BH * nb * d * 4;
+    bytes[6] = BH * nb * d * 4;
+    bytes[7] = BH * (size_t)s->L * 4;
+    bytes[8] = BH * 8;
+    return ok();
+}
+
+int vsmooth_workspace_bytes(const vc_shape* shape, const vsmooth_params* params, size_t* bytes) {
+    int r, k;
+    if ((r = check_shape(shape))) return r;
+    if ((r = check_params(shape, params, &k))) return r;
+    if (bytes == nullptr) return fail(VC_ERR_INVALID, "bytes is NULL");
+    *bytes = prepare_ws(shape, true, k);
+    return ok();
+}
+
+int vsmooth_prepare(const vc_shape* shape, const vsmooth_params* params, const void* q, const void* k,
+                    const void* v, const int32_t* perm_in, const vc_prepared* out, void* ws,
+                    size_t ws_bytes, hipStream_t stream) {
+    int r, kk;
+    if ((r = check_shape(shape))) return r;
+    if ((r = check_params(shape, params, &kk))) return r;
+    if ((r = check_ptr(q, "q")) || (r = check_ptr(k, "k")) || (r = check_ptr(v, "v"))) return r;
+    if ((r = check_prepared(out, false))) return r;
+    if ((r = check_ptr(out->perm, "perm"))) return r;
+    if (perm_in != nullptr && (r = check_ptr(perm_in, "perm_in"))) return r;
+    if (out->kmeans_obj != nullptr && (r = check_ptr(out->kmeans_obj, "kmeans_obj"))) return r;
+    const bool km = perm_in == nullptr;
+    const size_t need = prepare_ws(shape, km, kk);
+    if (ws == nullptr || ws_bytes < need)
+        return fail(VC_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws_bytes, need);
+    if (!aligned16(ws)) return fail(VC_ERR_INVALID, "ws is not 16-byte aligned");
+
+    const size_t BH = (size_t)shape->B * shape->H;
+    const int ns = vc::k_mean_splits((int)BH, shape->L);
+    uint8_t* wp = static_cast<uint8_t*>(ws);
+    vc::PrepareArgs a{};
+    a.B = shape->B; a.H = shape->H; a.L = shape->L; a.d = shape->d; a.nb = nblk(shape);
+    a.smooth_k = params->smooth_k;
+    a.v_mode = params->v_scale_mode;
+    a.q = q; a.k = k; a.v = v;
+    a.perm = out->perm;
+    a.q8 = out->q8; a.k8 = out->k8; a.v8 = out->v8;
+    a.q_scale = out->q_scale; a.k_scale = out->k_scale; a.v_scale = out->v_scale; a.v_mean = out->v_mean;
+    a.kpartial = reinterpret_cast<double*>(wp);
+    wp += a256(BH * ns * shape->d * sizeof(double));
+    a.kbar = reinterpret_cast<float*>(wp);
+    wp += a256(BH * shape->d * sizeof(float));
+
+    hipError_t e;
+    if (km) {
+        vc::KmeansArgs m{};
+        m.B = shape->B; m.H = shape->H; m.L = shape->L; m.d = shape->d;
+        m.k = kk;
+        m.iters = params->kmeans_iters;
+        m.seed = params->seed;
+        m.v = v;
+        m.perm = out->perm;
+        m.obj = out->kmeans_obj;
+        vc::kmeans_carve(m, wp);
+        e = vc::launch_kmeans(m, stream);
+        if (e != hipSuccess) return hip_status(e, "k-means");
+    } else {
+        // plain kernels rather than memcpy/memset nodes, so the call can be graph-captured
+        e = vc::launch_copy_perm(perm_in, out->perm, BH * (size_t)shape->L, out->kmeans_obj, BH, stream);
+        if (e != hipSuccess) return hip_status(e, "perm copy");
+    }
+    return hip_status(vc::launch_prepare_quant(a, stream), "vsmooth_prepare");
+}
+
+int vc_attention_fwd(const vc_shape* shape, const vc_attn_params* params, const vc_prepared* in,
+                     void* out, hipStream_t stream) {
+    return attention_common(shape, params, in, out, -1, -1, nullptr, nullptr, false, stream);
+}
+
+int vc_attention_fwd_dump(const vc_shape* shape, const vc_attn_params* params, const vc_prepared* in,
+                          void* out, int32_t bh, int32_t q_tile, float* s_dump, uint8_t* p_dump,
+                          hipStream_t stream) {
+    return attention_common(shape, params, in, out, bh, q_tile, s_dump, p_dump, true, stream);
+}
+
+int vc_attention_fwd_bf16(const vc_shape* shape, const void* q, const void* k, const void* v, void* out,
+                          int32_t out_dtype, hipStream_t stream) {
+    int r;
+    if ((r = check_shape(shape))) return r;
+    if ((r = check_ptr(q, "q")) || (r = check_ptr(k, "k")) || (r = check_ptr(v, "v")) ||
+        (r = check_ptr(out, "out")))
+        return r;
+    if (out_dtype != 0 && out_dtype != 1) return fail(VC_ERR_INVALID, "out_dtype must be 0 or 1");
+    vc::AttnBf16Args a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.out = out;
+    a.L = shape->L;
+    a.nkb = nblk(shape);
+    a.BH = shape->B * shape->H;
+    a.nqt = (shape->L + vc::ATTN_BM - 1) / vc::ATTN_BM;
+    a.C0 = (float)(1.4426950408889634074 / sqrt((double)shape->d));
+    return hip_status(vc::launch_attn_bf16(a, shape->d, out_dtype, stream), "vc_attention_fwd_bf16");
+}
+
+int vc_debug_expcast(const float* S, const float* c8, const float* krow, int64_t n, uint8_t* bytes,
+                     hipStream_t stream) {
+    if (n < 0 || n > ((int64_t)1 << 40)) return fail(VC_ERR_INVALID, "n=%lld out of range", (long long)n);
+    if (n == 0) return ok();
+    int r;
+    if ((r = check_ptr(S, "S")) || (r = check_ptr(c8, "c8")) || (r = check_ptr(krow, "krow")) ||
+        (r = check_ptr(bytes, "bytes")))
+        return r;
+    return hip_status(vc::launch_debug_expcast(S, c8, krow, n, bytes, stream), "vc_debug_expcast");
+}
+
+int vc_debug_e4m3_encode(const float* x, int64_t n, uint8_t* codes, hipStream_t stream) {
+    if (n < 0 || n > ((int64_t)1 << 40)) return fail(VC_ERR_INVALID, "n=%lld out of range", (long long)n);
+    if (n == 0) return ok();
+    int r;
+    if ((r = check_ptr(x, "x")) || (r = check_ptr(codes, "codes"))) return r;
+    return hip_status(vc::launch_debug_e4m3(x, n, codes, stream), "vc_debug_e4m3_encode");
+}
+
+int vc_debug_mfma_fp8(const uint8_t* a, const uint8_t* b, float* c, int32_t n_tiles, hipStream_t stream) {
+    if (n_tiles < 0) return fail(VC_ERR_INVALID, "n_tiles < 0");
+    if (n_tiles == 0) return ok();
+    int r;
+    if ((r = check_ptr(a, "a")) || (r = check_ptr(b, "b")) || (r = check_ptr(c, "c"))) return r;
+    return hip_status(vc::launch_debug_mfma_fp8(a, b, c, n_tiles, stream), "vc_debug_mfma_fp8");
+}
+
+}  // extern "C"

@@ -1,0 +1,62 @@
+// vc_debug.hip -- checking aids: the ExpCast byte map and the E4M3 encoder
+// exactly as the production kernels use them, and one FP8 matrix-core
+// product per tile (to see how the hardware rounds a 128-term FP8 sum).
+#include "vc_device.hpp"
+#include "vc_internal.hpp"
+
+namespace vc {
+
+__global__ void debug_expcast_kernel(const float* __restrict__ S, const float* __restrict__ c8,
+                                     const float* __restrict__ krow, int64_t n,
+                                     uint8_t* __restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) {
+        const uint32_t b = expcast_byte_into(S[i], c8[i], krow[i], 0, 0u) & 0xFFu;
+        out[i] = (uint8_t)(b < 126u ? b : 126u);  // the attention kernel never reaches the clamp
+    }
+}
+
+__global__ void debug_e4m3_kernel(const float* __restrict__ x, int64_t n, uint8_t* __restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) out[i] = (uint8_t)e4m3_rne(x[i]);
+}
+
+// one wave per tile: c = A B^T with A, B [16][128] E4M3 codes
+__global__ void debug_mfma_fp8_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
+                                      float* __restrict__ C, int n) {
+    const int t = blockIdx.x;
+    if (t >= n) return;
+    const int lane = threadIdx.x, r = lane & 15, g = lane >> 4;
+    const uint4* pa = reinterpret_cast<const uint4*>(A + ((size_t)t * 16 + r) * 128 + 32 * g);
+    const uint4* pb = reinterpret_cast<const uint4*>(B + ((size_t)t * 16 + r) * 128 + 32 * g);
+    uint4 a0 = pa[0], a1 = pa[1], b0 = pb[0], b1 = pb[1];
+    v8i va = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+    v8i vb = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+    v4f z = {0.f, 0.f, 0.f, 0.f};
+    v4f c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(va, vb, z, 0, 0, 0, 0, 0, 0);
+    // lane (col = lane & 15, g) holds rows 4 g + i of column col
+#pragma unroll
+    for (int i = 0; i < 4; i++) C[((size_t)t * 16 + 4 * g + i) * 16 + r] = c[i];
+}
+
+hipError_t launch_debug_expcast(const float* S, const float* c8, const float* krow, int64_t n,
+                                uint8_t* out, hipStream_t st) {
+    if (n > 0)
+        hipLaunchKernelGGL(debug_expcast_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                           S, c8, krow, n, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_debug_e4m3(const float* x, int64_t n, uint8_t* out, hipStream_t st) {
+    if (n > 0)
+        hipLaunchKernelGGL(debug_e4m3_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, x,
+                           n, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_debug_mfma_fp8(const uint8_t* a, const uint8_t* b, float* c, int n, hipStream_t st) {
+    if (n > 0) hipLaunchKernelGGL(debug_mfma_fp8_kernel, dim3(n), dim3(64), 0, st, a, b, c, n);
+    return hipGetLastError();
+}
+
+}  // namespace vc

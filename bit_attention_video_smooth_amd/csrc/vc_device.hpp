@@ -1,0 +1,103 @@
+// vc_device.hpp -- device helpers shared by the VC-Attention HIP kernels
+// (gfx950 / CDNA4).  Number formats and small wave-level primitives only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vc {
+
+constexpr int BLK = 128;  // tokens per hardware block (V-Smooth group and KV tile)
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+#define VC_LDS __attribute__((address_space(3)))
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+// two floats -> packed bf16 pair (round to nearest even; v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+    v2bf v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// OCP E4M3FN (sign, 4 exponent bits with bias 7, 3 mantissa bits; 0x7E = 448
+// is the largest finite code), saturating round-to-nearest-even, written from
+// the format definition.  Finite inputs only.
+__device__ __forceinline__ uint32_t e4m3_rne(float x) {
+    uint32_t u = __float_as_uint(x);
+    uint32_t s = (u >> 24) & 0x80u;
+    uint32_t a = u & 0x7FFFFFFFu;
+    uint32_t code;
+    if (a >= 0x43E00000u) {  // |x| >= 448
+        code = 0x7Eu;
+    } else if (a < 0x3C800000u) {  // |x| < 2^-6: subnormal grid of step 2^-9
+        code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);  // 0..8, exact scaling
+    } else {
+        uint32_t e = (a >> 23) - 120u;  // fp32 biased exponent -> E4M3 biased exponent
+        uint32_t q = (a >> 20) & 7u;
+        uint32_t rem = a & 0xFFFFFu;
+        uint32_t up = (rem > 0x80000u) | ((rem == 0x80000u) & (q & 1u));
+        code = ((e << 3) | q) + up;  // a carry out of q bumps the exponent
+        code = code > 0x7Eu ? 0x7Eu : code;
+    }
+    return s | code;
+}
+
+// ExpCast-FP8: y = fma(S, c8, krow) rounded to the nearest integer (ties to
+// even) and saturated to [0, 255]; callers keep y below 126.5.
+__device__ __forceinline__ uint32_t expcast_byte_into(float S, float c8, float krow, int sel,
+                                                      uint32_t acc) {
+    float y = __builtin_fmaf(S, c8, krow);
+    return __builtin_amdgcn_cvt_pk_u8_f32(__builtin_rintf(y), sel, acc);
+}
+
+// max over lanes {l, l^16, l^32, l^48} (one query's four lane groups)
+__device__ __forceinline__ float max_over_groups(float v) {
+    auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(p16[0]), __uint_as_float(p16[1]));
+    auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+// XCD-aware remap of a 1-D workgroup id: the hardware deals workgroups to
+// the 8 XCDs round-robin; give each XCD a contiguous range of logical ids so
+// that neighbouring tiles of one head share that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int pid, int n) {
+    constexpr int NX = 8;
+    int per = (n + NX - 1) / NX;
+    int tall = n % NX;
+    if (tall == 0) tall = NX;
+    int x = pid % NX, loc = pid / NX;
+    return (x < tall) ? x * per + loc : tall * per + (x - tall) * (per - 1) + loc;
+}
+
+// Slot order of keys inside a 128-key block as the PV matrix-core step reads
+// them (see the V layout in vc_attention.h): slot pos holds key kk with
+// pos = 32*((kk%16)/4) + 4*(kk/16) + (kk%4).
+__host__ __device__ constexpr int vslot_of_key(int kk) {
+    return 32 * ((kk % 16) / 4) + 4 * (kk / 16) + (kk % 4);
+}
+__host__ __device__ constexpr int vkey_of_slot(int pos) {
+    return 16 * ((pos % 32) / 4) + 4 * (pos / 32) + (pos % 4);
+}
+
+}  // namespace vc

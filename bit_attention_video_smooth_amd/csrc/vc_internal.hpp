@@ -1,0 +1,78 @@
+// vc_internal.hpp -- argument bundles between the C ABI layer and the kernel
+// launchers (host side).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace vc {
+
+struct PrepareArgs {
+    int B, H, L, d, nb;
+    int smooth_k, v_mode;
+    const void *q, *k, *v;
+    const int32_t* perm;  // [B,H,L]
+    uint8_t *q8, *k8, *v8;
+    float *q_scale, *k_scale, *v_scale, *v_mean;
+    double* kpartial;  // workspace [B*H, nsplit, d]
+    float* kbar;       // workspace [B*H, d]
+};
+
+struct KmeansArgs {
+    int B, H, L, d, k, iters;
+    uint64_t seed;
+    const void* v;         // bf16 [B,H,L,d]
+    int32_t* perm;         // out [B,H,L]
+    double* obj;           // out [B,H] or null
+    // workspace
+    float* cent;           // [BH, kpad, d] fp32 centroids
+    uint16_t* cent_hi;     // [BH, kpad, d] bf16 high part
+    uint16_t* cent_lo;     // [BH, kpad, d] bf16 low part
+    float* cnorm;          // [BH, kpad]
+    int32_t* assign;       // [BH, L]
+    int32_t* counts;       // [BH, k]
+    int32_t* offsets;      // [BH, k]
+    int32_t* chunk_cnt;    // [BH, nchunk, k]
+    double* obj_part;      // [BH, nchunkJ]
+    int kpad, nchunk;
+};
+
+struct AttnArgs {
+    const uint8_t *q8, *k8, *v8;
+    const float *q_scale, *k_scale, *v_scale, *v_mean;
+    void* out;
+    int L, nb, BH, nqt;
+    float C0, KB;
+    int dump_bh, dump_qt;
+    float* s_dump;
+    uint8_t* p_dump;
+};
+
+struct AttnBf16Args {
+    const uint16_t *q, *k, *v;
+    void* out;
+    int L, nkb, BH, nqt;
+    float C0;
+};
+
+int k_mean_splits(int BH, int L);
+size_t kmeans_workspace_bytes(int B, int H, int L, int d, int k);
+void kmeans_carve(KmeansArgs& a, void* ws);
+
+// copies perm_in -> perm and, if obj is non-null, fills obj[0..nobj) with NaN
+hipError_t launch_copy_perm(const int32_t* src, int32_t* dst, size_t n, double* obj, size_t nobj,
+                            hipStream_t st);
+hipError_t launch_prepare_quant(const PrepareArgs& a, hipStream_t st);
+hipError_t launch_kmeans(const KmeansArgs& a, hipStream_t st);
+hipError_t launch_attn_fp8(const AttnArgs& a, int d, int out_bf16, bool dump, hipStream_t st);
+hipError_t launch_attn_bf16(const AttnBf16Args& a, int d, int out_bf16, hipStream_t st);
+hipError_t launch_debug_expcast(const float* S, const float* c8, const float* krow, int64_t n,
+                                uint8_t* out, hipStream_t st);
+hipError_t launch_debug_e4m3(const float* x, int64_t n, uint8_t* out, hipStream_t st);
+hipError_t launch_debug_mfma_fp8(const uint8_t* a, const uint8_t* b, float* c, int n,
+                                 hipStream_t st);
+
+constexpr int ATTN_BM = 256;  // queries per workgroup of the attention kernels
+
+}  // namespace vc

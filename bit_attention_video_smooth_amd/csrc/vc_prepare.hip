@@ -1,0 +1,293 @@
+// vc_prepare.hip -- V-Smooth preprocessing kernels for gfx950.
+//
+// Follows the VC-Attention pages: agihunt summary (V-Smooth bullet: tokens
+// of a hardware block quantise together, only the residual after the block
+// mean is quantised), MarkTechPost abstract (block mean, 128-token blocks
+// after sorting), aikraft.ru "Reshenie" (lightweight k-means groups similar
+// tokens; the mean is kept exactly).  Q/K per-block FP8 scales follow the
+// block-scale notion of the TensorRT-LLM blog, "Quantized Attention".
+//
+// All kernels here are HBM-bound streaming passes: one workgroup per
+// 128-token block, 16-byte coalesced loads, reductions in fp64 (exact for
+// bf16 inputs of realistic dynamic range, hence independent of order), and
+// every value that is promised bit-exact is produced by one IEEE fp32
+// operation at a time (the file is built with -ffp-contract=off).
+#include "vc_device.hpp"
+#include "vc_internal.hpp"
+
+namespace vc {
+
+// ------------------------------------------------------------------------
+// a1: per-channel K mean, split over token chunks.  partial[bh][split][D].
+// ------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void k_colsum_partial(const uint16_t* __restrict__ k,
+                                                        double* __restrict__ partial, int L,
+                                                        int nsplit) {
+    constexpr int CPR = D / 8;        // 16-byte chunks per row
+    constexpr int RPI = 256 / CPR;    // rows per iteration
+    __shared__ double red[RPI][D + 1];
+    const int split = blockIdx.x, bh = blockIdx.y;
+    const int t = threadIdx.x, cc = t % CPR, rs = t / CPR;
+    const int chunk = (L + nsplit - 1) / nsplit;
+    const int r0 = split * chunk, r1 = min(L, r0 + chunk);
+    const uint16_t* base = k + (size_t)bh * L * D;
+    double acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) acc[e] = 0.0;
+    for (int r = r0 + rs; r < r1; r += RPI) {
+        uint4 w = *reinterpret_cast<const uint4*>(base + (size_t)r * D + cc * 8);
+        uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            acc[2 * e] += (double)bf16_to_f32(ww[e] & 0xFFFFu);
+            acc[2 * e + 1] += (double)bf16_to_f32(ww[e] >> 16);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; e++) red[rs][cc * 8 + e] = acc[e];
+    __syncthreads();
+    for (int c = t; c < D; c += 256) {
+        double s = 0.0;
+        for (int i = 0; i < RPI; i++) s += red[i][c];
+        partial[((size_t)bh * nsplit + split) * D + c] = s;
+    }
+}
+
+template <int D>
+__global__ void k_mean_finalize(const double* __restrict__ partial, float* __restrict__ kbar, int L,
+                                int nsplit, int smooth) {
+    const int bh = blockIdx.x, c = threadIdx.x;
+    if (c >= D) return;
+    double s = 0.0;
+    if (smooth)
+        for (int i = 0; i < nsplit; i++) s += partial[((size_t)bh * nsplit + i) * D + c];
+    kbar[(size_t)bh * D + c] = smooth ? (float)(s / (double)L) : 0.0f;
+}
+
+// Scale of a quantisation group from its amax A (same rule for every group):
+// mode 0: s = fp32(A / 448), inv = fp32(448 / A); mode 1: s = 2^e with e the
+// least integer such that A <= 448 * 2^e, inv = 2^-e.  A < 2^-100: both 0.
+__device__ __forceinline__ void group_scale(float A, int mode, float& s, float& inv) {
+    if (!(A >= 0x1p-100f)) {
+        s = 0.0f;
+        inv = 0.0f;
+        return;
+    }
+    if (mode == 0) {
+        s = __fdiv_rn(A, 448.0f);
+        inv = __fdiv_rn(448.0f, A);
+        return;
+    }
+    int E;
+    float f = frexpf(A, &E);  // A = f * 2^E, f in [0.5, 1)
+    int e = E - 9 + (f > 0.875f ? 1 : 0);  // 448 = 0.875 * 2^9
+    s = ldexpf(1.0f, e);
+    inv = ldexpf(1.0f, -e);
+}
+
+__device__ __forceinline__ float block_max_256(float v, float* red4) {
+    v = wave_max(v);
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) red4[w] = v;
+    __syncthreads();
+    float r = fmaxf(fmaxf(red4[0], red4[1]), fmaxf(red4[2], red4[3]));
+    return r;
+}
+
+// ------------------------------------------------------------------------
+// a7 / a8: per-block scalar-scale FP8 of Q (original order, GATHER=false) or
+// of K - kbar (permuted order, GATHER=true).  Grid (nb, B*H), 256 threads.
+// ------------------------------------------------------------------------
+template <int D, bool GATHER>
+__global__ __launch_bounds__(256) void quant_qk_kernel(const uint16_t* __restrict__ x,
+                                                       const int32_t* __restrict__ perm,
+                                                       const float* __restrict__ kbar,
+                                                       uint8_t* __restrict__ codes,
+                                                       float* __restrict__ scale, int L, int nb) {
+    constexpr int CPR = D / 8;
+    constexpr int NCH = BLK * CPR / 256;  // chunks per thread
+    __shared__ float red4[4];
+    const int b = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
+    const int i0 = b * BLK;
+    const size_t Lp = (size_t)nb * BLK;
+    const uint16_t* xb = x + (size_t)bh * L * D;
+    float vals[NCH][8];
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NCH; j++) {
+        const int ci = t + 256 * j, row = ci / CPR, cc = ci % CPR;
+        const int slot = i0 + row;
+        if (slot < L) {
+            const int src = GATHER ? perm[(size_t)bh * L + slot] : slot;
+            uint4 w = *reinterpret_cast<const uint4*>(xb + (size_t)src * D + cc * 8);
+            uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                float lo = bf16_to_f32(ww[e] & 0xFFFFu), hi = bf16_to_f32(ww[e] >> 16);
+                if (GATHER) {
+                    lo = __fsub_rn(lo, kbar[(size_t)bh * D + cc * 8 + 2 * e]);
+                    hi = __fsub_rn(hi, kbar[(size_t)bh * D + cc * 8 + 2 * e + 1]);
+                }
+                vals[j][2 * e] = lo;
+                vals[j][2 * e + 1] = hi;
+                amax = fmaxf(amax, fmaxf(fabsf(lo), fabsf(hi)));
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; e++) vals[j][e] = 0.0f;
+        }
+    }
+    const float A = block_max_256(amax, red4);
+    float s, inv;
+    group_scale(A, 0, s, inv);
+    if (t == 0) scale[(size_t)bh * nb + b] = s;
+    uint8_t* cb = codes + ((size_t)bh * Lp + i0) * D;
+#pragma unroll
+    for (int j = 0; j < NCH; j++) {
+        const int ci = t + 256 * j, row = ci / CPR, cc = ci % CPR;
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            lo |= e4m3_rne(__fmul_rn(vals[j][e], inv)) << (8 * e);
+            hi |= e4m3_rne(__fmul_rn(vals[j][4 + e], inv)) << (8 * e);
+        }
+        *reinterpret_cast<uint2*>(cb + (size_t)row * D + cc * 8) = make_uint2(lo, hi);
+    }
+}
+
+// ------------------------------------------------------------------------
+// a6: V-Smooth residual quantisation of one permuted 128-token block.
+// Exact block mean per channel (fp64 sum, rounded once), residual in fp32,
+// per-channel scale, E4M3 codes written block-transposed in PV slot order.
+// Grid (nb, B*H), 256 threads.
+// ------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict__ v,
+                                                      const int32_t* __restrict__ perm,
+                                                      uint8_t* __restrict__ codes,
+                                                      float* __restrict__ vscale,
+                                                      float* __restrict__ vmean, int L, int nb,
+                                                      int mode) {
+    constexpr int CPR = D / 8;
+    constexpr int NCH = BLK * CPR / 256;
+    constexpr int TPC = 256 / D;         // threads per channel
+    constexpr int KPT = BLK / TPC;       // keys (slots) per thread
+    __shared__ float T[D][BLK + 1];
+    const int b = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
+    const int i0 = b * BLK;
+    const int n = min(BLK, L - i0);
+    const uint16_t* vb = v + (size_t)bh * L * D;
+#pragma unroll
+    for (int j = 0; j < NCH; j++) {
+        const int ci = t + 256 * j, row = ci / CPR, cc = ci % CPR;
+        float f[8];
+        if (row < n) {
+            const int src = perm[(size_t)bh * L + i0 + row];
+            uint4 w = *reinterpret_cast<const uint4*>(vb + (size_t)src * D + cc * 8);
+            uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                f[2 * e] = bf16_to_f32(ww[e] & 0xFFFFu);
+                f[2 * e + 1] = bf16_to_f32(ww[e] >> 16);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; e++) f[e] = 0.0f;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; e++) T[cc * 8 + e][row] = f[e];
+    }
+    __syncthreads();
+    const int c = t / TPC, part = t % TPC;
+    double sum = 0.0;
+    for (int kk = part * KPT; kk < part * KPT + KPT; kk++)
+        if (kk < n) sum += (double)T[c][kk];
+#pragma unroll
+    for (int o = 1; o < TPC; o <<= 1) sum += __shfl_xor(sum, o);
+    const float mu = (float)(sum / (double)n);
+    float amax = 0.0f;
+    for (int kk = part * KPT; kk < part * KPT + KPT; kk++)
+        if (kk < n) amax = fmaxf(amax, fabsf(__fsub_rn(T[c][kk], mu)));
+#pragma unroll
+    for (int o = 1; o < TPC; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+    float s, inv;
+    group_scale(amax, mode, s, inv);
+    const size_t gi = ((size_t)bh * nb + b) * D + c;
+    if (part == 0) {
+        vmean[gi] = mu;
+        vscale[gi] = s;
+    }
+    uint8_t* out = codes + gi * BLK;
+#pragma unroll
+    for (int q = 0; q < KPT / 16; q++) {
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            uint32_t acc = 0;
+#pragma unroll
+            for (int y = 0; y < 4; y++) {
+                const int pos = part * KPT + q * 16 + e * 4 + y;
+                const int kk = vkey_of_slot(pos);
+                uint32_t code = 0;
+                if (kk < n) code = e4m3_rne(__fmul_rn(__fsub_rn(T[c][kk], mu), inv));
+                acc |= code << (8 * y);
+            }
+            w[e] = acc;
+        }
+        *reinterpret_cast<uint4*>(out + part * KPT + q * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+}
+
+__global__ void copy_perm_kernel(const int32_t* __restrict__ src, int32_t* __restrict__ dst, size_t n,
+                                 double* __restrict__ obj, size_t nobj) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) dst[i] = src[i];
+    if (obj != nullptr && i < nobj) obj[i] = __longlong_as_double(0x7FF8000000000000LL);
+}
+
+hipError_t launch_copy_perm(const int32_t* src, int32_t* dst, size_t n, double* obj, size_t nobj,
+                            hipStream_t st) {
+    const size_t m = n > nobj ? n : nobj;
+    hipLaunchKernelGGL(copy_perm_kernel, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, st, src, dst, n,
+                       obj, nobj);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------
+// Launchers.
+// ------------------------------------------------------------------------
+int k_mean_splits(int BH, int L) {
+    int by_len = (L + 1023) / 1024;
+    int want = (2048 + BH - 1) / BH;
+    int s = by_len < want ? by_len : want;
+    return s < 1 ? 1 : s;
+}
+
+template <int D>
+static hipError_t launch_prepare_quant_t(const PrepareArgs& a, hipStream_t st) {
+    const int BH = a.B * a.H;
+    const int nsplit = k_mean_splits(BH, a.L);
+    if (a.smooth_k) {
+        hipLaunchKernelGGL((k_colsum_partial<D>), dim3(nsplit, BH), dim3(256), 0, st,
+                           (const uint16_t*)a.k, a.kpartial, a.L, nsplit);
+    }
+    hipLaunchKernelGGL((k_mean_finalize<D>), dim3(BH), dim3(D), 0, st, a.kpartial, a.kbar, a.L,
+                       nsplit, a.smooth_k);
+    hipLaunchKernelGGL((quant_qk_kernel<D, false>), dim3(a.nb, BH), dim3(256), 0, st,
+                       (const uint16_t*)a.q, (const int32_t*)nullptr, (const float*)nullptr,
+                       a.q8, a.q_scale, a.L, a.nb);
+    hipLaunchKernelGGL((quant_qk_kernel<D, true>), dim3(a.nb, BH), dim3(256), 0, st,
+                       (const uint16_t*)a.k, a.perm, (const float*)a.kbar, a.k8, a.k_scale, a.L,
+                       a.nb);
+    hipLaunchKernelGGL((quant_v_kernel<D>), dim3(a.nb, BH), dim3(256), 0, st,
+                       (const uint16_t*)a.v, a.perm, a.v8, a.v_scale, a.v_mean, a.L, a.nb,
+                       a.v_mode);
+    return hipGetLastError();
+}
+
+hipError_t launch_prepare_quant(const PrepareArgs& a, hipStream_t st) {
+    return a.d == 128 ? launch_prepare_quant_t<128>(a, st) : launch_prepare_quant_t<64>(a, st);
+}
+
+}  // namespace vc

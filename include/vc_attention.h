@@ -1,0 +1,181 @@
+/*
+ * vc_attention.h -- C ABI of the VC-Attention library for AMD Instinct
+ * MI355X (gfx950): V-Smooth preprocessing and fused low-bit flash attention
+ * with ExpCast-FP8, plus a BF16 flash-attention kernel on the same scaffold.
+ *
+ * The method follows the VC-Attention pages:
+ *   - agihunt summary "VC-Attention: Training-Free Low-Bit Attention Speeds
+ *     Video Diffusion Up to 3.6x", V-Smooth and ExpCast-FP8 bullet points;
+ *   - yifor blog "Nunchux AI Introduces VC-Attention ...", the MarkTechPost
+ *     abstract and the section "V-Smooth and ExpCast-FP8, two targeted
+ *     designs";
+ *   - aikraft.ru news item, section "Reshenie" (Solution);
+ *   - TensorRT-LLM blog on video generation, sections "Quantized Attention"
+ *     and "Sparse Attention with Skip Softmax" (online-softmax notation).
+ *
+ * Conventions for every entry point:
+ *   - All tensors are device pointers to contiguous, row-major memory owned
+ *     by the caller.  The library allocates nothing, frees nothing and keeps
+ *     no state between calls; the workspace of vsmooth_prepare is caller
+ *     memory too.
+ *   - Every pointer the kernels read or write must be 16-byte aligned.
+ *   - Work is enqueued on `stream` and the call returns without waiting.
+ *     Concurrent calls on different streams are independent.
+ *   - Arguments are checked on the host before anything is launched; on an
+ *     error nothing is enqueued and the call returns a negative code whose
+ *     text vc_last_error() gives (thread-local storage, never NULL).
+ *   - Inputs holding NaN or infinities give undefined results.
+ *
+ * Sizes: d is 64 or 128; L >= 1; blocks are 128 tokens; nb = ceil(L/128);
+ * Lp = 128*nb (the length padded to whole blocks).
+ */
+#ifndef VC_ATTENTION_H
+#define VC_ATTENTION_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VC_ATTENTION_VERSION 1
+
+enum {
+    VC_OK = 0,
+    VC_ERR_INVALID = -1,     /* null or misaligned pointer, bad shape or parameter */
+    VC_ERR_UNSUPPORTED = -2, /* head dim other than 64/128, block size other than 128 */
+    VC_ERR_WORKSPACE = -3,   /* workspace smaller than vsmooth_workspace_bytes() */
+    VC_ERR_HIP = -4          /* a HIP launch or runtime call failed */
+};
+
+/* Library version (VC_ATTENTION_VERSION). */
+int vc_version(void);
+
+/* Text of the last error on the calling thread ("" if none). */
+const char* vc_last_error(void);
+
+/* Attention problem: batch B, heads H, tokens L, head dim d.  Q, K and V are
+ * [B, H, L, d]; attention is non-causal self-attention over all L tokens. */
+typedef struct vc_shape {
+    int32_t B, H, L, d;
+} vc_shape;
+
+/* V-Smooth parameters (agihunt V-Smooth bullet; MarkTechPost abstract). */
+typedef struct vsmooth_params {
+    int32_t block;        /* tokens per hardware block; must be 128 */
+    int32_t kmeans_k;     /* clusters of the lightweight k-means; <= 0 means nb */
+    int32_t kmeans_iters; /* Lloyd rounds (assign + update); >= 0 */
+    int32_t smooth_k;     /* 1: subtract the per-channel mean of K over the L
+                             tokens before quantising K (QK smoothing; the
+                             softmax is unchanged by it); 0: off */
+    int32_t v_scale_mode; /* residual scale per (block, channel):
+                             0: s = fp32(amax / 448);
+                             1: s = 2^e, the least power of two with amax <= 448 s */
+    int32_t reserved;     /* must be 0 */
+    uint64_t seed;        /* seeds the k-means initial centroids (SplitMix64) */
+} vsmooth_params;
+
+/* Output of vsmooth_prepare, input of vc_attention_fwd (all device memory).
+ * The residual codes use a block-transposed layout: for block b and channel
+ * c, v8[((bh*nb + b)*d + c)*128 + pos] holds the code of the key in slot
+ * k = 128 b + kk of the permuted order, where
+ *     pos = 32*((kk % 16) / 4) + 4*(kk / 16) + (kk % 4),
+ * the order in which the PV matrix-core step consumes keys. */
+typedef struct vc_prepared {
+    uint8_t* q8;        /* [B,H,Lp,d] E4M3 codes of Q, original token order */
+    uint8_t* k8;        /* [B,H,Lp,d] E4M3 codes of K - kbar, permuted order */
+    uint8_t* v8;        /* [B,H,nb,d,128] E4M3 codes of V - block mean (above) */
+    float* q_scale;     /* [B,H,nb] one scale per 128-token block of Q */
+    float* k_scale;     /* [B,H,nb] one scale per 128-token block of permuted K */
+    float* v_scale;     /* [B,H,nb,d] residual scale per (block, channel) */
+    float* v_mean;      /* [B,H,nb,d] exact (fp32) block mean of V */
+    int32_t* perm;      /* [B,H,L] perm[i] = original token in permuted slot i */
+    double* kmeans_obj; /* [B,H] k-means objective, or NULL */
+} vc_prepared;
+
+/* Byte sizes of the nine vc_prepared buffers, in the struct's order
+ * (kmeans_obj counted as B*H doubles). */
+int vc_prepared_sizes(const vc_shape* shape, size_t bytes[9]);
+
+/* Workspace that vsmooth_prepare needs for this shape and parameters. */
+int vsmooth_workspace_bytes(const vc_shape* shape, const vsmooth_params* params, size_t* bytes);
+
+/* V-Smooth preprocessing (agihunt V-Smooth bullet; MarkTechPost abstract:
+ * block mean removed, only the residual quantised; aikraft "Reshenie":
+ * lightweight k-means groups similar tokens into blocks, the mean is kept
+ * exactly).  Steps, per (batch, head):
+ *   1. kbar = mean of K over tokens (if smooth_k);
+ *   2. perm = perm_in, or the stable sort by cluster of a seeded Lloyd
+ *      k-means over the value rows (kmeans_iters rounds; objective written
+ *      to out->kmeans_obj when non-NULL);
+ *   3. Q codes per 128-token block in original order, K - kbar codes per
+ *      block in permuted order, one fp32 scale amax/448 per block;
+ *   4. per permuted block: exact mean of V, residual r = V - mean, per
+ *      channel scale (v_scale_mode), E4M3 codes of r (round to nearest even).
+ * q, k, v: bf16 [B,H,L,d].  perm_in: NULL or int32 [B,H,L] (each row a
+ * permutation of 0..L-1; copied to out->perm).  ws: ws_bytes >=
+ * vsmooth_workspace_bytes().  Padded slots (>= L) get code 0. */
+int vsmooth_prepare(const vc_shape* shape, const vsmooth_params* params, const void* q,
+                    const void* k, const void* v, const int32_t* perm_in,
+                    const vc_prepared* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Attention parameters. */
+typedef struct vc_attn_params {
+    int32_t z_off;     /* ExpCast offset in 0..8: the running row maximum is
+                          written as the code of 2^z_off (8 by default) */
+    int32_t out_dtype; /* 0: fp32 output, 1: bf16 output */
+} vc_attn_params;
+
+/* Fused VC-Attention forward (agihunt ExpCast-FP8 bullet; MarkTechPost
+ * abstract: one fused multiply-add writes the E4M3 byte of p = 2^z,
+ * byte = round(8 z + 56 + beta), beta = -0.35, clamped at zero).  Per query
+ * row and per 128-key block b in ascending order:
+ *   S = Q8 K8^T on FP8 matrix cores (exact products, fp32 result);
+ *   c_b = fp32(fp32(s_q s_k,b) * log2(e)/sqrt(d));
+ *   m' = max(m, fp32(max S * c_b));  P = ExpCast(S, 8 c_b, KB - 8 m')
+ *   with KB = fp32(56 - 0.35 + 8 z_off);
+ *   l_b = row sum of P;  acc = P V8_b on FP8 matrix cores;
+ *   O = 2^(m - m') O + s_v,b * acc + l_b * mean_b;  l = 2^(m - m') l + l_b.
+ * Output O / l, [B,H,L,d] in the original token order. */
+int vc_attention_fwd(const vc_shape* shape, const vc_attn_params* params,
+                     const vc_prepared* in, void* out, hipStream_t stream);
+
+/* Same as vc_attention_fwd, and also writes, for the 256-query tile
+ * `q_tile` (queries 256*q_tile ...) of head `bh` = b*H + h, the fp32
+ * scores S [256, Lp] and the ExpCast bytes P [256, Lp] of every block
+ * (rows past L are left untouched).  A checking aid. */
+int vc_attention_fwd_dump(const vc_shape* shape, const vc_attn_params* params,
+                          const vc_prepared* in, void* out, int32_t bh, int32_t q_tile,
+                          float* s_dump, uint8_t* p_dump, hipStream_t stream);
+
+/* BF16 flash attention on the same scaffold (the FP32 reference path the
+ * pages compare against, here on BF16 matrix cores): softmax(Q K^T /
+ * sqrt(d)) V with an exp2 online softmax and bf16 probabilities.
+ * q, k, v: bf16 [B,H,L,d]; out: [B,H,L,d] fp32 (out_dtype 0) or bf16 (1). */
+int vc_attention_fwd_bf16(const vc_shape* shape, const void* q, const void* k, const void* v,
+                          void* out, int32_t out_dtype, hipStream_t stream);
+
+/* ExpCast-FP8 alone, with the device function the attention kernel uses:
+ * bytes[i] = min(max(rne(fma(S[i], c8[i], krow[i])), 0), 126).  A checking
+ * aid for the byte map (MarkTechPost abstract). */
+int vc_debug_expcast(const float* S, const float* c8, const float* krow, int64_t n,
+                     uint8_t* bytes, hipStream_t stream);
+
+/* E4M3 encoding alone, with the device function the preprocessing kernels
+ * use: saturating round-to-nearest-even (OCP E4M3FN, bias 7). */
+int vc_debug_e4m3_encode(const float* x, int64_t n, uint8_t* codes, hipStream_t stream);
+
+/* One FP8 matrix-core product per 16x16 tile: for t < n_tiles,
+ * c[t][i][j] = sum_k A[t][i][k] * B[t][j][k] over k < 128, A and B E4M3
+ * codes [n_tiles,16,128], c fp32 [n_tiles,16,16].  A checking aid that
+ * exposes how the hardware rounds the 128-term sum. */
+int vc_debug_mfma_fp8(const uint8_t* a, const uint8_t* b, float* c, int32_t n_tiles,
+                      hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VC_ATTENTION_H */

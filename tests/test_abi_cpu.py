@@ -1,0 +1,142 @@
+"""Host-only checks of the C ABI: the library loads, exports every symbol the
+header declares, and rejects bad arguments before launching anything (no
+GPU is touched by these calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from bit_attention_video_smooth_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vc_attention.h")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?(?:int|char\s*\*|const char\s*\*)\s*\*?\s*(\w+)\s*\(", txt, re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libvcattn.so is not built; run __graft_entry__.build()")
+    return _lib.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert set(names) == set(_lib.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n)
+
+
+def test_version(lib):
+    assert _lib.vc_version() == 1
+
+
+def test_prepared_sizes(lib):
+    s = _lib.shape_of(2, 3, 300, 64)
+    b = _lib.vc_prepared_sizes(s)
+    nb, Lp = 3, 384
+    assert b == [6 * Lp * 64, 6 * Lp * 64, 6 * nb * 64 * 128, 6 * nb * 4, 6 * nb * 4,
+                 6 * nb * 64 * 4, 6 * nb * 64 * 4, 6 * 300 * 4, 6 * 8]
+
+
+def test_workspace_bytes_positive(lib):
+    n = _lib.vsmooth_workspace_bytes(_lib.shape_of(1, 40, 75600, 128), _lib.make_params())
+    assert n > 40 * 75600 * 4  # at least the assignment array
+
+
+@pytest.mark.parametrize("B,H,L,d,code", [(1, 1, 100, 96, _lib.VC_ERR_UNSUPPORTED),
+                                          (0, 1, 100, 64, _lib.VC_ERR_INVALID),
+                                          (1, 1, 0, 64, _lib.VC_ERR_INVALID),
+                                          (1, -2, 10, 128, _lib.VC_ERR_INVALID)])
+def test_bad_shape_rejected(lib, B, H, L, d, code):
+    with pytest.raises(_lib.VCError) as e:
+        _lib.vc_prepared_sizes(_lib.shape_of(B, H, L, d))
+    assert e.value.code == code
+    assert _lib.vc_last_error() != ""
+
+
+def test_bad_params_rejected(lib):
+    s = _lib.shape_of(1, 1, 256, 64)
+    p = _lib.make_params()
+    p.block = 64
+    with pytest.raises(_lib.VCError) as e:
+        _lib.vsmooth_workspace_bytes(s, p)
+    assert e.value.code == _lib.VC_ERR_UNSUPPORTED
+    for field, val in [("kmeans_iters", -1), ("v_scale_mode", 2), ("smooth_k", 3), ("kmeans_k", 257),
+                       ("reserved", 1)]:
+        p = _lib.make_params()
+        setattr(p, field, val)
+        with pytest.raises(_lib.VCError) as e:
+            _lib.vsmooth_workspace_bytes(s, p)
+        assert e.value.code == _lib.VC_ERR_INVALID, field
+
+
+FAKE = 0x10000  # aligned, never dereferenced: validation fails first
+
+
+def _prep(**over):
+    f = dict(q8=FAKE, k8=FAKE, v8=FAKE, q_scale=FAKE, k_scale=FAKE, v_scale=FAKE, v_mean=FAKE,
+             perm=FAKE, kmeans_obj=None)
+    f.update(over)
+    return _lib.vc_prepared(*[f[n] for n, _ in _lib.vc_prepared._fields_])
+
+
+def test_prepare_rejects_null_and_misaligned(lib):
+    s = _lib.shape_of(1, 1, 256, 64)
+    p = _lib.make_params()
+    with pytest.raises(_lib.VCError) as e:
+        _lib.vsmooth_prepare(s, p, 0, FAKE, FAKE, None, _prep(), FAKE, 1 << 30, 0)
+    assert e.value.code == _lib.VC_ERR_INVALID and "q" in str(e.value)
+    with pytest.raises(_lib.VCError) as e:
+        _lib.vsmooth_prepare(s, p, FAKE + 4, FAKE, FAKE, None, _prep(), FAKE, 1 << 30, 0)
+    assert e.value.code == _lib.VC_ERR_INVALID and "aligned" in str(e.value)
+    with pytest.raises(_lib.VCError) as e:
+        _lib.vsmooth_prepare(s, p, FAKE, FAKE, FAKE, None, _prep(v8=0), FAKE, 1 << 30, 0)
+    assert e.value.code == _lib.VC_ERR_INVALID
+
+
+def test_prepare_rejects_small_workspace(lib):
+    s = _lib.shape_of(1, 2, 1000, 128)
+    p = _lib.make_params()
+    need = _lib.vsmooth_workspace_bytes(s, p)
+    with pytest.raises(_lib.VCError) as e:
+        _lib.vsmooth_prepare(s, p, FAKE, FAKE, FAKE, None, _prep(), FAKE, need - 1, 0)
+    assert e.value.code == _lib.VC_ERR_WORKSPACE
+
+
+def test_attention_rejects_bad_params(lib):
+    s = _lib.shape_of(1, 1, 256, 64)
+    for z, od in [(9, 0), (-1, 0), (8, 2)]:
+        with pytest.raises(_lib.VCError) as e:
+            _lib.vc_attention_fwd(s, _lib.vc_attn_params(z, od), _prep(), FAKE, 0)
+        assert e.value.code == _lib.VC_ERR_INVALID
+    with pytest.raises(_lib.VCError):
+        _lib.vc_attention_fwd(s, _lib.vc_attn_params(8, 0), _prep(q_scale=0), FAKE, 0)
+    with pytest.raises(_lib.VCError) as e:
+        _lib.vc_attention_fwd_dump(s, _lib.vc_attn_params(8, 0), _prep(), FAKE, 5, 0, FAKE, FAKE, 0)
+    assert e.value.code == _lib.VC_ERR_INVALID
+
+
+def test_bf16_rejects(lib):
+    with pytest.raises(_lib.VCError) as e:
+        _lib.vc_attention_fwd_bf16(_lib.shape_of(1, 1, 64, 80), FAKE, FAKE, FAKE, FAKE, 0, 0)
+    assert e.value.code == _lib.VC_ERR_UNSUPPORTED
+    with pytest.raises(_lib.VCError):
+        _lib.vc_attention_fwd_bf16(_lib.shape_of(1, 1, 64, 64), FAKE, FAKE, FAKE, FAKE, 3, 0)
+
+
+def test_debug_entry_points_validate(lib):
+    with pytest.raises(_lib.VCError):
+        _lib.vc_debug_expcast(FAKE, FAKE, 0, 10, FAKE, 0)
+    with pytest.raises(_lib.VCError):
+        _lib.vc_debug_e4m3_encode(FAKE, -1, FAKE, 0)
+    _lib.vc_debug_e4m3_encode(FAKE, 0, FAKE, 0)  # n == 0 is a no-op
+    with pytest.raises(_lib.VCError):
+        _lib.vc_debug_mfma_fp8(FAKE, 0, FAKE, 1, 0)

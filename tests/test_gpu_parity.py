@@ -1,0 +1,236 @@
+"""GPU parity: the HIP library (called through its C ABI) against the CPU
+oracle on the same seeded inputs.  Bars (VC-Attention target): codes,
+scales, means and ExpCast bytes bit-exact; output rel-L2 <= 1e-3 and
+max-abs <= 1e-2 * max|O_ref|; k-means objective within 1%."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_attention_video_smooth_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+REL_L2 = 1e-3
+MAXABS = 1e-2
+
+
+@pytest.fixture(scope="module")
+def api():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    from bit_attention_video_smooth_amd import api as a
+    a._lib.load()
+    return a
+
+
+def dev_bf16(u16):
+    return torch.from_numpy(np.ascontiguousarray(u16)).view(torch.bfloat16).cuda()
+
+
+def rel_l2(a, b):
+    return float(np.linalg.norm((a - b).ravel()) / np.linalg.norm(b.ravel()))
+
+
+def _inputs(B, H, L, d, seed, grid=None):
+    cfg = synth.custom(B, H, L, d, grid=grid)
+    return synth.make_inputs(cfg, seed)
+
+
+SHAPES = [(1, 2, 1024, 64, (4, 16, 16)), (1, 3, 300, 128, None), (2, 2, 129, 64, None),
+          (1, 1, 1, 128, None), (1, 2, 4000, 128, None), (1, 1, 520, 64, None)]
+
+
+# ----------------------------------------------------------- primitives ----
+
+def test_e4m3_encoder_bit_exact(api):
+    hi16 = np.arange(0, 0x43E0 + 1, dtype=np.uint32)
+    lows = np.array([0, 1, 0x7FFF, 0x8000, 0x8001, 0xFFFF, 0x4000, 0xC000], np.uint32)
+    u = (hi16[:, None] << 16 | lows[None, :]).ravel()
+    u = np.concatenate([u, u | np.uint32(0x80000000)])
+    x = u.view(np.float32)
+    x = np.concatenate([x[np.abs(x) <= 448], np.random.default_rng(1).uniform(-500, 500, 1 << 20).astype(np.float32),
+                        np.float32([448.0, 464.0, 1e30, -1e30, 0.0, -0.0])])
+    got = api.e4m3_encode(torch.from_numpy(x).cuda()).cpu().numpy()
+    ref = oracle.e4m3_encode(x)
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, (x[bad[:8]], got[bad[:8]], ref[bad[:8]])
+
+
+def test_expcast_bit_exact(api):
+    rng = np.random.default_rng(2)
+    n = 1 << 21
+    S = (rng.normal(0, 3000, n)).astype(np.float32)
+    c8 = (8 * rng.uniform(1e-4, 1e-2, n)).astype(np.float32)
+    m = (S * c8 / 8).astype(np.float32)  # a running max around the score
+    krow = (np.float32(119.65) - np.float32(8) * (m + rng.uniform(0, 20, n).astype(np.float32))).astype(np.float32)
+    # exact ties y = k + 0.5 and the clamp at zero
+    k = np.arange(-20, 127)
+    S[:k.size] = 0.0
+    krow[:k.size] = (k + 0.5).astype(np.float32)
+    S[k.size:2 * k.size] = 1.0
+    c8[k.size:2 * k.size] = 1.0
+    krow[k.size:2 * k.size] = (k - 0.5).astype(np.float32)
+    got = api.expcast(torch.from_numpy(S).cuda(), torch.from_numpy(c8).cuda(),
+                      torch.from_numpy(krow).cuda()).cpu().numpy()
+    ref = oracle.expcast(S, c8, krow)
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, (S[bad[:5]], c8[bad[:5]], krow[bad[:5]], got[bad[:5]], ref[bad[:5]])
+
+
+def test_fp8_matrix_core_sum_is_correctly_rounded(api):
+    """One 16x16x128 FP8 product with a zero accumulator: compare with the
+    exact sum rounded once to fp32 (the oracle's definition of S)."""
+    rng = np.random.default_rng(3)
+    n = 512
+    codes = np.concatenate([np.arange(0, 0x7F), np.arange(0x80, 0xFF)]).astype(np.uint8)
+    a = rng.choice(codes, size=(n, 16, 128)).astype(np.uint8)
+    b = rng.choice(codes, size=(n, 16, 128)).astype(np.uint8)
+    c = api.mfma_fp8(torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda()).cpu().numpy()
+    da, db = oracle.e4m3_decode(a), oracle.e4m3_decode(b)
+    exact = np.einsum("tik,tjk->tij", da, db)
+    ref = exact.astype(np.float32)
+    frac = float(np.mean(c == ref))
+    err = np.abs(c.astype(np.float64) - exact) / np.maximum(np.abs(exact), 1e-30)
+    print("fp8 mfma: bit-exact fraction %.6f, max rel err %.3g" % (frac, err.max()))
+    assert frac == 1.0
+
+
+# -------------------------------------------------------------- prepare ----
+
+def _oracle_prep(q, k, v, perm, b, h, smooth_k=1, v_mode=0):
+    return oracle.prepare_head(q[b, h], k[b, h], v[b, h], perm[b, h], smooth_k, v_mode)
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("v_mode,smooth_k", [(0, 1), (1, 1), (0, 0)])
+def test_prepare_bit_exact(api, shape, v_mode, smooth_k):
+    B, H, L, d, grid = shape
+    q, k, v = _inputs(B, H, L, d, 10 + L, grid)
+    perm = synth.random_perms(B, H, L, 7)
+    P = api.prepare(dev_bf16(q), dev_bf16(k), dev_bf16(v), perm_in=torch.from_numpy(perm).cuda(),
+                    smooth_k=smooth_k, v_scale_mode=v_mode)
+    torch.cuda.synchronize()
+    g = {n: getattr(P, n).cpu().numpy() for n in ("q8", "k8", "q_scale", "k_scale", "v_scale", "v_mean", "perm")}
+    g["v8"] = api.v_codes_natural(P.v8).cpu().numpy()
+    assert np.array_equal(g["perm"], perm)
+    for b in range(B):
+        for h in range(H):
+            o = _oracle_prep(q, k, v, perm, b, h, smooth_k, v_mode)
+            for n in ("q8", "k8", "v8", "q_scale", "k_scale", "v_scale", "v_mean"):
+                x, y = g[n][b, h], o[n]
+                if not np.array_equal(x.view(np.uint8), y.view(np.uint8)):
+                    idx = np.argwhere(x != y)[:5]
+                    pytest.fail("%s mismatch at %s: gpu %s oracle %s" % (n, idx.tolist(), x[tuple(idx.T)], y[tuple(idx.T)]))
+
+
+# ------------------------------------------------------------ attention ----
+
+def _oracle_out(q, k, v, perm, z_off=8, v_mode=0, rows=None):
+    B, H, L, d = q.shape
+    r0, r1 = (0, L) if rows is None else rows
+    out = np.empty((B, H, r1 - r0, d), np.float32)
+    for b in range(B):
+        for h in range(H):
+            o = _oracle_prep(q, k, v, perm, b, h, 1, v_mode)
+            out[b, h] = oracle.attention_head(o, L, z_off, rows=rows)
+    return out
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("z_off", [8, 0])
+def test_attention_matches_oracle(api, shape, z_off):
+    B, H, L, d, grid = shape
+    q, k, v = _inputs(B, H, L, d, 20 + L, grid)
+    perm = synth.random_perms(B, H, L, 8)
+    P = api.prepare(dev_bf16(q), dev_bf16(k), dev_bf16(v), perm_in=torch.from_numpy(perm).cuda())
+    out = api.attention(P, z_off=z_off).cpu().numpy()
+    ref = _oracle_out(q, k, v, perm, z_off)
+    r = rel_l2(out, ref)
+    ma = float(np.abs(out - ref).max() / np.abs(ref).max())
+    print("attention %s z_off=%d: rel-L2 %.3g max-abs/max %.3g" % (shape[:4], z_off, r, ma))
+    assert r <= REL_L2 and ma <= MAXABS
+
+
+def test_attention_bf16_output(api):
+    B, H, L, d, grid = SHAPES[0]
+    q, k, v = _inputs(B, H, L, d, 5, grid)
+    perm = synth.random_perms(B, H, L, 9)
+    P = api.prepare(dev_bf16(q), dev_bf16(k), dev_bf16(v), perm_in=torch.from_numpy(perm).cuda())
+    o32 = api.attention(P).cpu().numpy()
+    o16 = api.attention(P, out_dtype=torch.bfloat16).float().cpu().numpy()
+    ref = torch.from_numpy(o32).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(o16, ref)
+
+
+@pytest.mark.parametrize("shape", [SHAPES[0], SHAPES[1], SHAPES[4]])
+def test_attention_scores_and_bytes_bit_exact(api, shape):
+    B, H, L, d, grid = shape
+    q, k, v = _inputs(B, H, L, d, 30 + L, grid)
+    perm = synth.random_perms(B, H, L, 10)
+    P = api.prepare(dev_bf16(q), dev_bf16(k), dev_bf16(v), perm_in=torch.from_numpy(perm).cuda())
+    nqt = (L + 255) // 256
+    for bh, qt in {(0, 0), (B * H - 1, nqt - 1)}:
+        b, h = divmod(bh, H)
+        out, S, Pb = api.attention_dump(P, bh, qt)
+        S, Pb = S.cpu().numpy(), Pb.cpu().numpy()
+        r0, r1 = qt * 256, min(L, qt * 256 + 256)
+        o = _oracle_prep(q, k, v, perm, b, h)
+        ro, rby, rS = oracle.attention_head(o, L, 8, rows=(r0, r1), want_bytes=True)
+        n = r1 - r0
+        s_eq = np.mean(S[:n] == rS)
+        b_eq = np.mean(Pb[:n] == rby)
+        print("dump bh=%d qt=%d: S equal %.6f, bytes equal %.6f" % (bh, qt, s_eq, b_eq))
+        assert s_eq == 1.0 and b_eq == 1.0
+
+
+# ----------------------------------------------------------------- BF16 ----
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_bf16_attention_within_rounding_bound(api, shape):
+    """O = sum bf16(p) v / sum p: each output element is off the exact result
+    by at most 2^-8 * max_j |v_jc| (bf16 rounding of p, unit 2^-9, plus fp32
+    accumulation), checked against fp64 softmax attention."""
+    B, H, L, d, grid = shape
+    q, k, v = _inputs(B, H, L, d, 40 + L, grid)
+    out = api.attention_bf16(dev_bf16(q), dev_bf16(k), dev_bf16(v)).cpu().numpy()
+    f = oracle.bf16_to_f32
+    worst = 0.0
+    for b in range(B):
+        for h in range(H):
+            vf = f(v[b, h]).astype(np.float64)
+            ref = oracle.attention_f64(f(q[b, h]), f(k[b, h]), vf)
+            bound = 2.0 ** -8 * np.abs(vf).max(axis=0) + 1e-6
+            ratio = (np.abs(out[b, h] - ref) / bound).max()
+            worst = max(worst, ratio)
+            assert rel_l2(out[b, h], ref) < 5e-3
+    print("bf16 %s: worst error / bound %.3f" % (shape[:4], worst))
+    assert worst <= 1.0
+
+
+# -------------------------------------------------------------- k-means ----
+
+@pytest.mark.parametrize("B,H,L,d,k,grid", [(1, 2, 1024, 64, 8, (4, 16, 16)), (1, 2, 4096, 128, 32, (4, 32, 32)),
+                                           (2, 1, 3000, 64, 24, None)])
+def test_kmeans_objective_within_1pct(api, B, H, L, d, k, grid):
+    q, kk, v = _inputs(B, H, L, d, 50 + L, grid)
+    P = api.prepare(dev_bf16(q), dev_bf16(kk), dev_bf16(v), kmeans_k=k, kmeans_iters=8, seed=123)
+    obj = P.kmeans_obj.cpu().numpy()
+    perm = P.perm.cpu().numpy()
+    for b in range(B):
+        for h in range(H):
+            assert np.array_equal(np.sort(perm[b, h]), np.arange(L))
+            a, C, J = oracle.kmeans(v[b, h], k, 8, oracle.head_seed(123, b, h, H))
+            print("k-means b=%d h=%d: gpu J %.6g oracle J %.6g ratio %.5f" % (b, h, obj[b, h], J, obj[b, h] / J))
+            assert abs(obj[b, h] / J - 1) <= 0.01
+
+
+def test_kmeans_permutation_attention_in_band(api):
+    cfg = synth.CONFIGS[0]
+    q, k, v = synth.make_inputs(cfg, 0)
+    P = api.prepare(dev_bf16(q), dev_bf16(k), dev_bf16(v), seed=0)
+    out = api.attention(P).cpu().numpy()
+    f = oracle.bf16_to_f32
+    for h in range(cfg.H):
+        ref = oracle.attention_f64(f(q[0, h]), f(k[0, h]), f(v[0, h]))
+        assert rel_l2(out[0, h], ref) < 6e-2

@@ -30,12 +30,18 @@ def flags():
             "-I", os.path.join(ROOT, "include"), "-I", CSRC,
             # packed fp32 instructions stay off (the host pass ignores the flag)
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-mllvm", "-disable-promote-alloca-to-lds",
             "-Wno-unused-result"]
+
+
+# NaN inputs are outside the library's contract; without NaN semantics the
+# compiler drops the quieting moves it otherwise puts around every max.
+EXTRA = {"vc_attn_fp8.hip": ["-fno-honor-nans"], "vc_attn_bf16.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-    cmd = [hipcc(), *flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *flags(), *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:

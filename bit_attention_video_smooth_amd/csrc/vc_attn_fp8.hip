@@ -20,9 +20,15 @@
 //    B operand (written so by the preprocessing kernel);
 //  * the row sum of the ExpCast bytes is one more FP8 product (a row of
 //    ones times P^T), exact, off the vector ALU;
-//  * K8/V8 tiles of the next block stream into LDS with direct-to-LDS
-//    16-byte loads (double buffered, XOR-swizzled 16-byte chunks) while the
-//    current block is computed;
+//  * K8/V8 tiles stream into a three-stage LDS ring with direct-to-LDS
+//    16-byte loads (XOR-swizzled 16-byte chunks) two blocks ahead; each
+//    stage is its own LDS object so the compiler's wait insertion can tell
+//    a stage being filled from the stage being read;
+//  * the two wave groups of a workgroup (one wave of each per SIMD) run the
+//    same four-slot program per block -- QK^T (matrix), softmax (vector),
+//    PV (matrix), epilogue (vector) -- offset by one slot, with a
+//    workgroup barrier between slots, so every matrix-core slot of one group
+//    overlaps a vector-ALU slot of the other on the same SIMD;
 //  * workgroups are remapped so that the query tiles of one head run on
 //    one XCD and share its L2.
 #include "vc_device.hpp"
@@ -32,33 +38,57 @@ namespace vc {
 
 namespace {
 
-constexpr int NW = 8;    // waves per workgroup
+constexpr int NW = 8;    // waves per workgroup (two groups of four)
 constexpr int QW = 32;   // queries per wave
 static_assert(NW * QW == ATTN_BM, "tile");
 
 template <int D>
 struct Fp8Tile {
-    static constexpr int K_TILE = BLK * D;  // bytes of one K8 block  [128 keys][D]
-    static constexpr int V_TILE = D * BLK;  // bytes of one V8 block  [D][128 slots]
-    static constexpr int STAGE = K_TILE + V_TILE + 2 * D * 4;
-    static constexpr int KCH = D / 16;      // 16-byte chunks per K row
+    static constexpr int K_TILE = BLK * D;      // bytes of one K8 block  [128 keys][D]
+    static constexpr int V_TILE = D * BLK;      // bytes of one V8 block  [D][128 slots]
+    static constexpr int SV_OFF = K_TILE + V_TILE;
+    // each loading wave keeps a private 1 KiB copy of the block's per-channel
+    // scales and means and a 256-byte window of K scales (readers use wave 0's)
+    static constexpr int KS_OFF = SV_OFF + 4 * 1024;
+    static constexpr int STAGE = KS_OFF + 4 * 256;
+    static constexpr int KCH = D / 16;          // 16-byte chunks per K row
+    static constexpr int NCHK = K_TILE / 16;    // 16-byte chunks per K (or V) tile
+    static constexpr int LPT = NCHK / 256;      // chunks per loading thread (group 0 loads)
+    static constexpr int NCT = D / 16;          // 16-channel output tiles
 };
 
-__device__ __forceinline__ void lds_dma16(const void* g, uint8_t* lds_wave_base) {
-    __builtin_amdgcn_global_load_lds(g, (VC_LDS void*)lds_wave_base, 16, 0, 0);
+// End of a slot: this wave's LDS reads are complete, then all waves meet.
+// The scheduling fences keep every instruction inside its slot.
+__device__ __forceinline__ void slot_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// XOR swizzle of the 16-byte chunks of LDS tile rows.  LDS has 64 banks of
+// 4 bytes (256 bytes): two 128-byte rows (or four 64-byte rows) share one
+// bank line, so the chunk index is XORed with the row's line number, and the
+// 16 rows one matrix-core operand read touches land on 16 distinct chunk
+// positions of the bank space.
+__host__ __device__ constexpr int chunk_swizzle(int r, int nch) {
+    return nch == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3);
 }
 
 // A/B operand of one 16-row tile: row `r` of a tile with `pitch`-byte rows of
-// `nch` 16-byte chunks, XOR-swizzled by (r mod nch); lane group g takes
-// bytes [32 g, 32 g + 32) of the logical row.
-__device__ __forceinline__ v8i lds_operand(const uint8_t* tile, int r, int pitch, int nch, int g) {
-    const int sw = r & (nch - 1) & 7;
-    const uint8_t* row = tile + r * pitch;
-    uint4 a = *reinterpret_cast<const uint4*>(row + (((2 * g) ^ sw) << 4));
-    uint4 b = *reinterpret_cast<const uint4*>(row + (((2 * g + 1) ^ sw) << 4));
+// `nch` 16-byte chunks (swizzled as above); lane group g takes bytes
+// [32 g, 32 g + 32) of the logical row.
+typedef VC_LDS uint8_t lds_u8;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ v8i lds_operand(const lds_u8* tile, int r, int pitch, int nch, int g) {
+    const int sw = chunk_swizzle(r, nch);
+    const lds_u8* row = tile + r * pitch;
+    const u32x4 a = *reinterpret_cast<const VC_LDS u32x4*>(row + (((2 * g) ^ sw) << 4));
+    const u32x4 b = *reinterpret_cast<const VC_LDS u32x4*>(row + (((2 * g + 1) ^ sw) << 4));
     v8i o;
-    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
-    o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+    o[0] = a[0]; o[1] = a[1]; o[2] = a[2]; o[3] = a[3];
+    o[4] = b[0]; o[5] = b[1]; o[6] = b[2]; o[7] = b[3];
     return o;
 }
 
@@ -66,108 +96,175 @@ __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
-template <int D>
-__device__ __forceinline__ void issue_block_load(const AttnArgs& a, uint8_t* stage, int bh, int kb,
-                                                 int w, int lane) {
-    using T = Fp8Tile<D>;
-    const size_t Lp = (size_t)a.nb * BLK;
-    const uint8_t* gK = a.k8 + ((size_t)bh * Lp + (size_t)kb * BLK) * D;
-    const uint8_t* gV = a.v8 + ((size_t)bh * a.nb + kb) * (size_t)D * BLK;
-    constexpr int NCHK = T::K_TILE / 16;
-    // K8 tile: LDS chunk p = r*KCH + cp holds global chunk (r, cp ^ (r & (KCH-1) & 7))
-#pragma unroll
-    for (int i = 0; i < NCHK / (NW * 64); i++) {
-        const int base = (i * NW + w) * 64;
-        const int p = base + lane;
-        const int r = p / T::KCH, cp = p % T::KCH;
-        const int c = cp ^ (r & (T::KCH - 1) & 7);
-        lds_dma16(gK + r * D + c * 16, stage + base * 16);
-    }
-    // V8 tile: D rows of 128 bytes (8 chunks)
-    uint8_t* sV = stage + T::K_TILE;
-#pragma unroll
-    for (int i = 0; i < NCHK / (NW * 64); i++) {
-        const int base = (i * NW + w) * 64;
-        const int p = base + lane;
-        const int r = p / 8, cp = p % 8;
-        const int c = cp ^ (r & 7);
-        lds_dma16(gV + r * BLK + c * 16, sV + base * 16);
-    }
-    // per-channel scale and mean of the block: D/4 chunks each, last wave
-    if (w == NW - 1) {
-        constexpr int NC = D / 4;  // 16-byte chunks in D floats
-        float* sS = reinterpret_cast<float*>(sV + T::V_TILE);
-        const size_t gi = ((size_t)bh * a.nb + kb) * D;
-        if (lane < 2 * NC) {
-            const float* src = lane < NC ? a.v_scale + gi + lane * 4 : a.v_mean + gi + (lane - NC) * 4;
-            lds_dma16(src, reinterpret_cast<uint8_t*>(sS));
-        }
-    }
+// Per-lane byte offsets of the 16-byte chunks a group-0 wave copies: the
+// same for every block.  Tile rows of 128 bytes (K8 at d = 128 and every V8
+// tile) or 64 bytes (K8 at d = 64); LDS chunk position cp of row r receives
+// global chunk cp ^ chunk_swizzle(r).  (Slices are 4 KiB = a whole number of
+// swizzle periods, so the row index within a slice gives the same swizzle.)
+__device__ __forceinline__ uint32_t dma_offset(int w, int lane, int row_bytes) {
+    const int cpr = row_bytes / 16;      // chunks per row
+    const int p = w * 64 + lane;         // chunk position within a 4 KiB slice
+    const int r = p / cpr, cp = p % cpr;
+    return (uint32_t)(r * row_bytes + ((cp ^ chunk_swizzle(r, cpr)) << 4));
 }
 
-template <int D, bool OUT_BF16, bool DUMP>
-__global__ __launch_bounds__(NW * 64, 2) void attn_fp8_kernel(AttnArgs a) {
+typedef int v4si __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor of `bytes` bytes at `base` (gfx9: raw 32-bit data, no
+// stride); reads past the end return zeros.  All fields are wave-uniform.
+__device__ __forceinline__ v4si make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    v4si r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+    r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32));
+    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+    r[3] = 0x00020000;
+    return r;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const lds_u8* p) {
+    return (uint32_t)reinterpret_cast<uintptr_t>(p);
+}
+
+// Direct global->LDS copies.  Written as inline assembly so that the
+// compiler neither waits on them nor counts them: every wait on these copies
+// is explicit (wait_vmcnt) and every LDS hand-over goes through a barrier.
+// They have no register outputs; M0 (the wave's LDS base) is set in the same
+// block, one wait state before the load.
+__device__ __forceinline__ void lds_dma16(const v4si& r, const lds_u8* lds_wave_base, uint32_t voff,
+                                          uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(__builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base))), "v"(voff), "s"(r),
+                    "s"(__builtin_amdgcn_readfirstlane(soff))
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ void lds_dma4(const v4si& r, const lds_u8* lds_wave_base, uint32_t voff,
+                                         uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                 :: "s"(__builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base))), "v"(voff), "s"(r),
+                    "s"(__builtin_amdgcn_readfirstlane(soff))
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ void lds_dma16_flat(const void* g, const lds_u8* lds_wave_base) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :: "s"(__builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base))),
+                    "v"(reinterpret_cast<uint64_t>(g))
+                 : "memory", "m0");
+}
+
+// Group-0 waves (w < 4, 256 threads) copy block kb into `stage`: their
+// share of the K8 and V8 tiles, plus (each wave, into its own slot) the
+// block's per-channel scales and means and the K scales from block kb on.
+// Every copy runs with all 64 lanes, so each loading wave issues exactly
+// NLD copies per block and the wait counts below are exact.  Buffer
+// descriptors cover one head: reads past it return zeros.
+template <int D>
+struct Fp8Loader {
     using T = Fp8Tile<D>;
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    const int nwg = a.BH * a.nqt;
-    const int pid = xcd_remap(blockIdx.x, nwg);
-    const int bh = pid / a.nqt, qtile = pid % a.nqt;
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, col = lane & 15, g = lane >> 4;
-    const int q0 = qtile * ATTN_BM + w * QW;
-    const int L = a.L, nb = a.nb;
-    const size_t Lp = (size_t)nb * BLK;
-    const bool dump = DUMP && bh == a.dump_bh && qtile == a.dump_qt;
-
-    // Q8 operands (B operand of S^T = K8 Q8^T): lane (col, g) holds bytes
-    // [32 g, 32 g + 32) of query q0 + 16 qt + col.
-    v8i qop[2];
-#pragma unroll
-    for (int qt = 0; qt < 2; qt++) {
-        const int row = q0 + 16 * qt + col;
-        uint4 x = make_uint4(0, 0, 0, 0), y = make_uint4(0, 0, 0, 0);
-        if (row < L && (D == 128 || g < 2)) {
-            const uint8_t* src = a.q8 + ((size_t)bh * Lp + row) * D + 32 * g;
-            x = *reinterpret_cast<const uint4*>(src);
-            y = *reinterpret_cast<const uint4*>(src + 16);
-        }
-        qop[qt][0] = x.x; qop[qt][1] = x.y; qop[qt][2] = x.z; qop[qt][3] = x.w;
-        qop[qt][4] = y.x; qop[qt][5] = y.y; qop[qt][6] = y.z; qop[qt][7] = y.w;
+    static constexpr int NLD = 2 * T::LPT + 2;
+    static constexpr int NC = D / 4;  // 16-byte chunks of D floats
+    v4si rk, rv, rks;
+    const float *vs, *vm;
+    uint32_t off_k, off_v, off_sv;
+    int w, lane;
+    __device__ __forceinline__ Fp8Loader(const AttnArgs& a, int bh, int w_, int lane_) : w(w_), lane(lane_) {
+        const size_t Lp = (size_t)a.nb * BLK;
+        rk = make_rsrc(a.k8 + (size_t)bh * Lp * D, (uint32_t)(Lp * D));
+        rv = make_rsrc(a.v8 + (size_t)bh * a.nb * D * BLK, (uint32_t)((size_t)a.nb * D * BLK));
+        rks = make_rsrc(a.k_scale + (size_t)bh * a.nb, (uint32_t)(a.nb * 4));
+        vs = a.v_scale + (size_t)bh * a.nb * D;
+        vm = a.v_mean + (size_t)bh * a.nb * D;
+        off_k = dma_offset(w, lane, D);
+        off_v = dma_offset(w, lane, BLK);
+        off_sv = (uint32_t)((lane % (2 * NC)) % NC) * 16;  // lanes past 2*NC repeat
     }
-    const int qblk = min(q0 / BLK, nb - 1);
-    const float sq = a.q_scale[(size_t)bh * nb + qblk];
-    const float* ksc = a.k_scale + (size_t)bh * nb;
-
-    v8i ones;
+    __device__ __forceinline__ void issue(lds_u8* stage, int kb) const {
 #pragma unroll
-    for (int i = 0; i < 8; i++) ones[i] = 0x38383838;  // E4M3 1.0
-    const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
-
-    constexpr int NCT = D / 16;
-    v4f O[2][NCT];
+        for (int i = 0; i < T::LPT; i++)
+            lds_dma16(rk, stage + (i * 4 + w) * 1024, off_k, kb * T::K_TILE + i * 4096);
 #pragma unroll
-    for (int qt = 0; qt < 2; qt++)
+        for (int i = 0; i < T::LPT; i++)
+            lds_dma16(rv, stage + T::K_TILE + (i * 4 + w) * 1024, off_v, kb * T::V_TILE + i * 4096);
+        const float* src = ((lane % (2 * NC)) < NC ? vs : vm) + (size_t)kb * D;
+        lds_dma16_flat(reinterpret_cast<const uint8_t*>(src) + off_sv, stage + T::SV_OFF + w * 1024);
+        lds_dma4(rks, stage + T::KS_OFF + w * 256, lane * 4, kb * 4);
+    }
+};
+
+// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int D, bool DUMP>
+struct Fp8Wave {
+    using T = Fp8Tile<D>;
+    const AttnArgs& a;
+    int bh, w, lane, col, g, grp, q0, L, nb;
+    size_t Lp;
+    bool dump;
+    float sq;
+    v8i qop[2];
+    v4f O[2][T::NCT];
+    float m[2], l[2];
+    // per-block values carried between slots
+    v4f S[2][8];
+    uint32_t P[2][8];
+    float alpha[2];
+
+    __device__ __forceinline__ Fp8Wave(const AttnArgs& args, int bh_, int qtile, int w_, int lane_)
+        : a(args), bh(bh_), w(w_), lane(lane_) {
+        col = lane & 15;
+        g = lane >> 4;
+        grp = w >> 2;
+        q0 = qtile * ATTN_BM + w * QW;
+        L = a.L;
+        nb = a.nb;
+        Lp = (size_t)nb * BLK;
+        dump = DUMP && bh == a.dump_bh && qtile == a.dump_qt;
+        // Q8 operands (B operand of S^T = K8 Q8^T): lane (col, g) holds bytes
+        // [32 g, 32 g + 32) of query q0 + 16 qt + col.
 #pragma unroll
-        for (int ct = 0; ct < NCT; ct++) O[qt][ct] = zero4;
-    float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+        for (int qt = 0; qt < 2; qt++) {
+            const int row = q0 + 16 * qt + col;
+            uint4 x = make_uint4(0, 0, 0, 0), y = make_uint4(0, 0, 0, 0);
+            if (row < L && (D == 128 || g < 2)) {
+                const uint8_t* src = a.q8 + ((size_t)bh * Lp + row) * D + 32 * g;
+                x = *reinterpret_cast<const uint4*>(src);
+                y = *reinterpret_cast<const uint4*>(src + 16);
+            }
+            qop[qt][0] = x.x; qop[qt][1] = x.y; qop[qt][2] = x.z; qop[qt][3] = x.w;
+            qop[qt][4] = y.x; qop[qt][5] = y.y; qop[qt][6] = y.z; qop[qt][7] = y.w;
+        }
+        const int qblk = min(q0 / BLK, nb - 1);
+        sq = a.q_scale[(size_t)bh * nb + qblk];
+        // the Q operands and scale are in registers before any block copy is
+        // issued, so no later wait on them can drain the copy pipeline
+        __builtin_amdgcn_s_waitcnt(0);
+        const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int qt = 0; qt < 2; qt++) {
+            m[qt] = -INFINITY;
+            l[qt] = 0.f;
+#pragma unroll
+            for (int ct = 0; ct < T::NCT; ct++) O[qt][ct] = zero4;
+        }
+    }
 
-    issue_block_load<D>(a, smem, bh, 0, w, lane);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-
-    for (int kb = 0; kb < nb; kb++) {
-        uint8_t* stage = smem + (kb & 1) * T::STAGE;
-        if (kb + 1 < nb) issue_block_load<D>(a, smem + ((kb + 1) & 1) * T::STAGE, bh, kb + 1, w, lane);
-        const uint8_t* sK = stage;
-        const uint8_t* sV = stage + T::K_TILE;
-        const float* sS = reinterpret_cast<const float*>(sV + T::V_TILE);
-
-        // ---- S^T = K8 Q8^T : 8 key tiles x 2 query tiles
-        v4f S[2][8];
+    // slot A: S^T = K8 Q8^T for 8 key tiles x 2 query tiles (matrix cores).
+    // Operand reads run two key tiles ahead of the products.
+    __device__ __forceinline__ void slot_qk(const lds_u8* st) {
+        const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kt = 0; kt < 8; kt++) {
             v8i kop;
             if (D == 128 || g < 2) {
-                kop = lds_operand(sK, 16 * kt + col, D, T::KCH, g);
+                kop = lds_operand(st, 16 * kt + col, D, T::KCH, g);
             } else {
 #pragma unroll
                 for (int i = 0; i < 8; i++) kop[i] = 0;
@@ -175,41 +272,46 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fp8_kernel(AttnArgs a) {
 #pragma unroll
             for (int qt = 0; qt < 2; qt++) S[qt][kt] = mfma_fp8(kop, qop[qt], zero4);
         }
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS read: tiles 0, 1
+#pragma unroll
+        for (int kt = 0; kt < 8; kt++) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA: tile kt
+            if (kt + 2 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read: tile kt+2
+        }
+    }
 
-        const float cb = __fmul_rn(__fmul_rn(sq, ksc[kb]), a.C0);
+    // slot B: running max and ExpCast-FP8 bytes (vector ALU).  The last,
+    // partial block (keys past L) has its own copy of the whole slot so that
+    // no masking work leaks into the full blocks.
+    template <bool MASKED>
+    __device__ __forceinline__ void softmax_rows(int kb, float cb, int lim) {
         const float c8 = 8.0f * cb;
-        const int nvalid = L - kb * BLK;  // keys of this block that exist (>= 1)
-        const bool partial = nvalid < BLK;
-
-        uint32_t P[2][8];
-        float alpha[2];
 #pragma unroll
         for (int qt = 0; qt < 2; qt++) {
             float mx = -INFINITY;
-            if (!partial) {
+            if (!MASKED) {
 #pragma unroll
                 for (int kt = 0; kt < 8; kt++)
-                    mx = fmaxf(mx, fmaxf(fmaxf(S[qt][kt][0], S[qt][kt][1]), fmaxf(S[qt][kt][2], S[qt][kt][3])));
+                    mx = fmaxf(fmaxf(mx, fmaxf(S[qt][kt][0], S[qt][kt][1])), fmaxf(S[qt][kt][2], S[qt][kt][3]));
             } else {
+                // key 16 kt + 4 g + i exists iff 16 kt + i < lim
 #pragma unroll
                 for (int kt = 0; kt < 8; kt++)
 #pragma unroll
-                    for (int i = 0; i < 4; i++)
-                        if (16 * kt + 4 * g + i < nvalid) mx = fmaxf(mx, S[qt][kt][i]);
+                    for (int i = 0; i < 4; i++) mx = fmaxf(mx, (16 * kt + i < lim) ? S[qt][kt][i] : -INFINITY);
             }
             mx = max_over_groups(mx);
             const float t = __fmul_rn(mx, cb);
             const float mn = fmaxf(m[qt], t);
             const float krow = __fsub_rn(a.KB, 8.0f * mn);
-            alpha[qt] = exp2f(m[qt] - mn);
+            alpha[qt] = __builtin_amdgcn_exp2f(m[qt] - mn);  // 2^(m - m'), 0 on the first block
             m[qt] = mn;
 #pragma unroll
             for (int kt = 0; kt < 8; kt++) {
                 uint32_t pk = 0;
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
-                    // keys past L keep byte 0
-                    if (!partial || 16 * kt + 4 * g + i < nvalid)
+                    if (!MASKED || 16 * kt + i < lim)  // keys past L keep byte 0
                         pk = expcast_byte_into(S[qt][kt][i], c8, krow, i, pk);
                 }
                 P[qt][kt] = pk;
@@ -228,84 +330,172 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fp8_kernel(AttnArgs a) {
                 }
             }
         }
+    }
 
-        // ---- row sums of the bytes: ones(16x128) * P^T, exact
-        float ell[2];
+    __device__ __forceinline__ void slot_softmax(int kb, const lds_u8* st) {
+        const float ks = *reinterpret_cast<const VC_LDS float*>(st + T::KS_OFF);
+        const float cb = __fmul_rn(__fmul_rn(sq, ks), a.C0);
+        const int nvalid = L - kb * BLK;  // keys of this block that exist (>= 1)
+        if (nvalid < BLK)
+            softmax_rows<true>(kb, cb, nvalid - 4 * g);
+        else
+            softmax_rows<false>(kb, cb, 0);
+    }
+
+    // slot C: row sums (ones(16x128) * P^T, exact), V8^T P^T on the matrix
+    // cores, and O += s_v (.) acc + l_b mean_b on the vector ALU, one channel
+    // tile behind the products.
+    __device__ __forceinline__ void slot_pv(const lds_u8* st) {
+        const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
+        v8i ones;  // E4M3 1.0, made here so it takes no register across slots
+        int one4;
+        asm volatile("v_mov_b32 %0, 0x38383838" : "=v"(one4));
+#pragma unroll
+        for (int i = 0; i < 8; i++) ones[i] = one4;
         v8i pv[2];
+        float ell[2];
 #pragma unroll
         for (int qt = 0; qt < 2; qt++) {
 #pragma unroll
             for (int kt = 0; kt < 8; kt++) pv[qt][kt] = (int)P[qt][kt];
-            v4f r = mfma_fp8(ones, pv[qt], zero4);
+            const v4f r = mfma_fp8(ones, pv[qt], zero4);
             ell[qt] = r[0];
         }
+        const lds_u8* sV = st + T::K_TILE;
+        const VC_LDS float* sS = reinterpret_cast<const VC_LDS float*>(st + T::SV_OFF);
+#pragma unroll
+        for (int ct = 0; ct < T::NCT; ct++) {
+            const v8i vop = lds_operand(sV, 16 * ct + col, BLK, 8, g);
+            const f32x4 sv = *reinterpret_cast<const VC_LDS f32x4*>(sS + 16 * ct + 4 * g);
+            const f32x4 mu = *reinterpret_cast<const VC_LDS f32x4*>(sS + D + 16 * ct + 4 * g);
+#pragma unroll
+            for (int qt = 0; qt < 2; qt++) {
+                const v4f acc = mfma_fp8(vop, pv[qt], zero4);
+#pragma unroll
+                for (int i = 0; i < 4; i++)
+                    O[qt][ct][i] = __builtin_fmaf(sv[i], acc[i], __builtin_fmaf(ell[qt], mu[i], O[qt][ct][i]));
+            }
+        }
+#pragma unroll
+        for (int qt = 0; qt < 2; qt++) l[qt] = __builtin_fmaf(alpha[qt], l[qt], ell[qt]);
+        // operand reads two channel tiles ahead, epilogue one tile behind
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // DS read: tiles 0, 1 (+ scale, mean)
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA: row sums
+#pragma unroll
+        for (int ct = 0; ct < T::NCT; ct++) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA: tile ct
+            if (ct + 2 < T::NCT) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+            if (ct > 0) __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);  // VALU: tile ct-1
+        }
+    }
 
-        // ---- rescale only when some row of the wave raised its max
+    // The three slots of block kb (stage `cur`).  The loading group (LOADER)
+    // starts the copy of block kb + 2 into stage `ahead` during its softmax
+    // slot -- unconditionally, past the end it re-copies the last block into a
+    // stage nobody reads again, so the copy count per block is fixed -- and at
+    // the end of its PV slot waits for its share of block kb + 1 (the barrier
+    // that follows publishes the whole block to both groups).
+    template <bool LOADER>
+    __device__ __forceinline__ void block(const Fp8Loader<D>& ld, int kb, const lds_u8* cur,
+                                          lds_u8* ahead) {
+        slot_qk(cur);
+        slot_barrier();
+        if (LOADER) ld.issue(ahead, min(kb + 2, nb - 1));
+        slot_softmax(kb, cur);
+        // rescale only when some row of the wave raised its max
         if (__any((alpha[0] != 1.0f) | (alpha[1] != 1.0f))) {
 #pragma unroll
             for (int qt = 0; qt < 2; qt++)
 #pragma unroll
-                for (int ct = 0; ct < NCT; ct++) O[qt][ct] *= alpha[qt];
+                for (int ct = 0; ct < T::NCT; ct++) O[qt][ct] *= alpha[qt];
         }
-#pragma unroll
-        for (int qt = 0; qt < 2; qt++) l[qt] = __builtin_fmaf(alpha[qt], l[qt], ell[qt]);
-
-        // ---- O^T += s_v (.) (V8^T P^T) + l_b mean_b
-#pragma unroll
-        for (int ct = 0; ct < NCT; ct++) {
-            const v8i vop = lds_operand(sV, 16 * ct + col, BLK, 8, g);
-            const float4 sv = *reinterpret_cast<const float4*>(sS + 16 * ct + 4 * g);
-            const float4 mu = *reinterpret_cast<const float4*>(sS + D + 16 * ct + 4 * g);
-#pragma unroll
-            for (int qt = 0; qt < 2; qt++) {
-                const v4f acc = mfma_fp8(vop, pv[qt], zero4);
-                O[qt][ct][0] = __builtin_fmaf(sv.x, acc[0], __builtin_fmaf(ell[qt], mu.x, O[qt][ct][0]));
-                O[qt][ct][1] = __builtin_fmaf(sv.y, acc[1], __builtin_fmaf(ell[qt], mu.y, O[qt][ct][1]));
-                O[qt][ct][2] = __builtin_fmaf(sv.z, acc[2], __builtin_fmaf(ell[qt], mu.z, O[qt][ct][2]));
-                O[qt][ct][3] = __builtin_fmaf(sv.w, acc[3], __builtin_fmaf(ell[qt], mu.w, O[qt][ct][3]));
-            }
+        slot_barrier();
+        slot_pv(cur);
+        if (LOADER) {
+            if (DUMP)
+                wait_vmcnt<0>();
+            else
+                wait_vmcnt<Fp8Loader<D>::NLD>();
         }
-
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        slot_barrier();
     }
 
-    // ---- O / l, original row order; lane (col, g) holds channels 16 ct + 4 g + i
+    template <bool LOADER>
+    __device__ __forceinline__ void run(const Fp8Loader<D>& ld, lds_u8* st0, lds_u8* st1, lds_u8* st2) {
+        for (int kb = 0; kb < nb; kb += 3) {
+            block<LOADER>(ld, kb, st0, st2);
+            if (kb + 1 < nb) block<LOADER>(ld, kb + 1, st1, st0);
+            if (kb + 2 < nb) block<LOADER>(ld, kb + 2, st2, st1);
+        }
+    }
+};
+
+template <int D, bool OUT_BF16, bool DUMP>
+__global__ __launch_bounds__(NW * 64, 2) void attn_fp8_kernel(AttnArgs a) {
+    using T = Fp8Tile<D>;
+    __shared__ __attribute__((aligned(16))) uint8_t st0_[T::STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t st1_[T::STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t st2_[T::STAGE];
+    lds_u8* st0 = (lds_u8*)st0_;
+    lds_u8* st1 = (lds_u8*)st1_;
+    lds_u8* st2 = (lds_u8*)st2_;
+    const int nwg = a.BH * a.nqt;
+    const int pid = xcd_remap(blockIdx.x, nwg);
+    const int bh = pid / a.nqt, qtile = pid % a.nqt;
+    // wave index as a scalar (uniform) value
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    Fp8Wave<D, DUMP> s(a, bh, qtile, w, lane);
+    const Fp8Loader<D> ld(a, bh, w, lane);
+    const int nb = a.nb;
+
+    // Blocks 0 and 1 are in flight before the first slot; block 0 is
+    // published by the first barrier.  Group 1 then waits one more slot so
+    // that its matrix slots overlap group 0's vector slots.
+    if (s.grp == 0) {
+        ld.issue(st0, 0);
+        ld.issue(st1, min(1, nb - 1));
+        wait_vmcnt<Fp8Loader<D>::NLD>();
+        slot_barrier();
+    } else {
+        slot_barrier();
+        slot_barrier();
+    }
+    if (s.grp == 0) {
+        s.template run<true>(ld, st0, st1, st2);
+        wait_vmcnt<0>();  // copies past the end
+        slot_barrier();
+    } else {
+        s.template run<false>(ld, st0, st1, st2);
+    }
+
+    // O / l, original row order; lane (col, g) holds channels 16 ct + 4 g + i
 #pragma unroll
     for (int qt = 0; qt < 2; qt++) {
-        const int row = q0 + 16 * qt + col;
-        if (row >= L) continue;
-        const float il = 1.0f / l[qt];
+        const int row = s.q0 + 16 * qt + s.col;
+        if (row >= s.L) continue;
+        const float il = 1.0f / s.l[qt];
         if (OUT_BF16) {
-            uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + ((size_t)bh * L + row) * D;
+            uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + ((size_t)bh * s.L + row) * D;
 #pragma unroll
-            for (int ct = 0; ct < NCT; ct++) {
-                uint32_t lo = pack_bf16x2(O[qt][ct][0] * il, O[qt][ct][1] * il);
-                uint32_t hi = pack_bf16x2(O[qt][ct][2] * il, O[qt][ct][3] * il);
-                *reinterpret_cast<uint2*>(o + 16 * ct + 4 * g) = make_uint2(lo, hi);
+            for (int ct = 0; ct < T::NCT; ct++) {
+                uint32_t lo = pack_bf16x2(s.O[qt][ct][0] * il, s.O[qt][ct][1] * il);
+                uint32_t hi = pack_bf16x2(s.O[qt][ct][2] * il, s.O[qt][ct][3] * il);
+                *reinterpret_cast<uint2*>(o + 16 * ct + 4 * s.g) = make_uint2(lo, hi);
             }
         } else {
-            float* o = reinterpret_cast<float*>(a.out) + ((size_t)bh * L + row) * D;
+            float* o = reinterpret_cast<float*>(a.out) + ((size_t)bh * s.L + row) * D;
 #pragma unroll
-            for (int ct = 0; ct < NCT; ct++)
-                *reinterpret_cast<float4*>(o + 16 * ct + 4 * g) =
-                    make_float4(O[qt][ct][0] * il, O[qt][ct][1] * il, O[qt][ct][2] * il, O[qt][ct][3] * il);
+            for (int ct = 0; ct < T::NCT; ct++)
+                *reinterpret_cast<float4*>(o + 16 * ct + 4 * s.g) =
+                    make_float4(s.O[qt][ct][0] * il, s.O[qt][ct][1] * il, s.O[qt][ct][2] * il,
+                                s.O[qt][ct][3] * il);
         }
     }
 }
 
 template <int D, bool OB, bool DUMP>
 hipError_t launch_t(const AttnArgs& a, hipStream_t st) {
-    const int smem = 2 * Fp8Tile<D>::STAGE;
-    auto kern = attn_fp8_kernel<D, OB, DUMP>;
-    static bool attr_set = false;  // benign race: idempotent attribute
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, smem);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
-    hipLaunchKernelGGL(kern, dim3(a.BH * a.nqt), dim3(NW * 64), smem, st, a);
+    hipLaunchKernelGGL((attn_fp8_kernel<D, OB, DUMP>), dim3(a.BH * a.nqt), dim3(NW * 64), 0, st, a);
     return hipGetLastError();
 }
 

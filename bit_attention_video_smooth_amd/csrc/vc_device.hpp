@@ -50,12 +50,13 @@ __device__ __forceinline__ uint32_t e4m3_rne(float x) {
     return s | code;
 }
 
-// ExpCast-FP8: y = fma(S, c8, krow) rounded to the nearest integer (ties to
-// even) and saturated to [0, 255]; callers keep y below 126.5.
+// ExpCast-FP8: y = fma(S, c8, krow), then v_cvt_pk_u8_f32, which rounds to
+// the nearest integer (ties to even) and saturates to [0, 255], into byte
+// `sel` of `acc`.  Callers keep y below 126.5.
 __device__ __forceinline__ uint32_t expcast_byte_into(float S, float c8, float krow, int sel,
                                                       uint32_t acc) {
-    float y = __builtin_fmaf(S, c8, krow);
-    return __builtin_amdgcn_cvt_pk_u8_f32(__builtin_rintf(y), sel, acc);
+    const float y = __builtin_fmaf(S, c8, krow);
+    return __builtin_amdgcn_cvt_pk_u8_f32(y, sel, acc);
 }
 
 // max over lanes {l, l^16, l^32, l^48} (one query's four lane groups)

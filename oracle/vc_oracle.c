@@ -423,7 +423,8 @@ float vco_c0(int d) { return (float)(1.4426950408889634074 / sqrt((double)d)); }
 /* produced by vco_prepare_head.  For mode 1 pass qf [L,d], kf [Lp,d]         */
 /* (keys already in permuted order), rf [nb,d,128], v_mean; scales ignored.  */
 /* out: [r1-r0, d] fp32.  bytes_out (may be NULL): [r1-r0, Lp] ExpCast bytes */
-/* of the final pass, for byte-level checks.  S_out likewise (may be NULL).  */
+/* of the final pass, for byte-level checks.  S_out and y_out (the fp32 FMA  */
+/* result before rounding) likewise (may be NULL).                           */
 /* ------------------------------------------------------------------------ */
 
 void vco_attention_rows(int mode, int L, int d, int z_off,
@@ -431,7 +432,8 @@ void vco_attention_rows(int mode, int L, int d, int z_off,
                         const float* q_scale, const float* k_scale,
                         const float* v_scale, const float* v_mean,
                         const double* qf, const double* kf, const double* rf,
-                        int r0, int r1, float* out, uint8_t* bytes_out, float* S_out)
+                        int r0, int r1, float* out, uint8_t* bytes_out, float* S_out,
+                        float* y_out)
 {
     int nb = (L + VCO_BLK - 1) / VCO_BLK;
     int64_t Lp = (int64_t)nb * VCO_BLK;
@@ -479,6 +481,9 @@ void vco_attention_rows(int mode, int L, int d, int z_off,
                     uint8_t by = (j < n) ? vco_expcast1(S[j], c8, krow) : 0;
                     if (bytes_out) bytes_out[(int64_t)(i - r0) * Lp + b * VCO_BLK + j] = by;
                     if (S_out) S_out[(int64_t)(i - r0) * Lp + b * VCO_BLK + j] = (j < n) ? S[j] : 0.0f;
+                    if (y_out)
+                        y_out[(int64_t)(i - r0) * Lp + b * VCO_BLK + j] =
+                            (j < n) ? fmaf(S[j], c8, krow) : -INFINITY;
                     p[j] = dec[by];
                     if (j < n) ell += p[j];
                 }

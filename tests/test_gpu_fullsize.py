@@ -1,0 +1,74 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times: the whole tensor is prepared and attended on the GPU; the
+oracle then checks sampled heads (codes, scales, means bit-exact), sampled
+query tiles (first and ragged last) of the output, and the k-means objective
+of one head."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_attention_video_smooth_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def api():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    from bit_attention_video_smooth_amd import api as a
+    a._lib.load()
+    return a
+
+
+def dev_bf16(u16):
+    return torch.from_numpy(np.ascontiguousarray(u16)).view(torch.bfloat16).cuda()
+
+
+@pytest.mark.parametrize("cfg_idx", [1, 2, 4])
+def test_full_size_sampled(api, cfg_idx):
+    cfg = synth.CONFIGS[cfg_idx]
+    B, H, L, d = cfg.B, cfg.H, cfg.L, cfg.d
+    q, k, v = synth.make_inputs(cfg, cfg_idx)
+    perm = synth.random_perms(B, H, L, 100 + cfg_idx)
+    P = api.prepare(dev_bf16(q), dev_bf16(k), dev_bf16(v), perm_in=torch.from_numpy(perm).cuda())
+    out = api.attention(P)
+    torch.cuda.synchronize()
+    nb = (L + 127) // 128
+    last_tile = ((L - 1) // 256) * 256
+    for bh in sorted({0, B * H - 1}):
+        b, h = divmod(bh, H)
+        o = oracle.prepare_head(q[b, h], k[b, h], v[b, h], perm[b, h])
+        assert np.array_equal(P.q8[b, h].cpu().numpy(), o["q8"])
+        assert np.array_equal(P.k8[b, h].cpu().numpy(), o["k8"])
+        assert np.array_equal(api.v_codes_natural(P.v8[b, h]).cpu().numpy(), o["v8"])
+        for n in ("q_scale", "k_scale", "v_scale", "v_mean"):
+            assert np.array_equal(getattr(P, n)[b, h].cpu().numpy(), o[n]), n
+        for r0 in (0, last_tile):
+            r1 = min(L, r0 + 256)
+            ref = oracle.attention_head(o, L, 8, rows=(r0, r1))
+            got = out[b, h, r0:r1].cpu().numpy()
+            rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+            ma = float(np.abs(got - ref).max() / np.abs(ref).max())
+            print("%s bh=%d rows %d-%d: rel-L2 %.3g max-abs/max %.3g" % (cfg.name, bh, r0, r1, rel, ma))
+            assert rel <= 1e-3 and ma <= 1e-2
+    assert nb == P.q_scale.shape[-1]
+
+
+@pytest.mark.parametrize("cfg_idx", [4, 1])
+def test_full_size_kmeans_objective(api, cfg_idx):
+    cfg = synth.CONFIGS[cfg_idx]
+    B, H, L, d = cfg.B, cfg.H, cfg.L, cfg.d
+    q, k, v = synth.make_inputs(cfg, cfg_idx)
+    P = api.prepare(dev_bf16(q), dev_bf16(k), dev_bf16(v), seed=cfg_idx)
+    obj = P.kmeans_obj.cpu().numpy()
+    perm = P.perm.cpu().numpy()
+    for bh in range(B * H):
+        b, h = divmod(bh, H)
+        assert np.array_equal(np.sort(perm[b, h]), np.arange(L))
+    nb = (L + 127) // 128
+    b, h = divmod(B * H - 1, H)
+    J = oracle.kmeans(v[b, h], nb, 8, oracle.head_seed(cfg_idx, b, h, H))[2]
+    print("%s k-means head %d: gpu J %.7g oracle J %.7g ratio %.6f" % (cfg.name, B * H - 1, obj[b, h], J, obj[b, h] / J))
+    assert abs(obj[b, h] / J - 1) <= 0.01

@@ -78,22 +78,34 @@ def test_expcast_bit_exact(api):
     assert bad.size == 0, (S[bad[:5]], c8[bad[:5]], krow[bad[:5]], got[bad[:5]], ref[bad[:5]])
 
 
-def test_fp8_matrix_core_sum_is_correctly_rounded(api):
-    """One 16x16x128 FP8 product with a zero accumulator: compare with the
-    exact sum rounded once to fp32 (the oracle's definition of S)."""
+# Measured on MI355X: the FP8 matrix-core 128-term dot product is exact when
+# all products share a narrow exponent range, but is not the correctly
+# rounded sum in general; it stays within 2^-12 of sum |a_k b_k| (the bound
+# used below with a factor-2 margin).
+FP8_DOT_REL = 2.0 ** -11
+
+
+def test_fp8_matrix_core_sum_error_bound(api):
     rng = np.random.default_rng(3)
-    n = 512
+    n = 256
     codes = np.concatenate([np.arange(0, 0x7F), np.arange(0x80, 0xFF)]).astype(np.uint8)
     a = rng.choice(codes, size=(n, 16, 128)).astype(np.uint8)
     b = rng.choice(codes, size=(n, 16, 128)).astype(np.uint8)
-    c = api.mfma_fp8(torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda()).cpu().numpy()
-    da, db = oracle.e4m3_decode(a), oracle.e4m3_decode(b)
-    exact = np.einsum("tik,tjk->tij", da, db)
-    ref = exact.astype(np.float32)
-    frac = float(np.mean(c == ref))
-    err = np.abs(c.astype(np.float64) - exact) / np.maximum(np.abs(exact), 1e-30)
-    print("fp8 mfma: bit-exact fraction %.6f, max rel err %.3g" % (frac, err.max()))
-    assert frac == 1.0
+    # narrow range: codes 0x30..0x47 (|x| in [0.5, 4)), every partial sum exact in fp32
+    an = rng.integers(0x30, 0x48, (n, 16, 128)).astype(np.uint8) | (rng.integers(0, 2, (n, 16, 128)).astype(np.uint8) << 7)
+    bn = rng.integers(0x30, 0x48, (n, 16, 128)).astype(np.uint8)
+    for (x, y, exact_expected) in ((a, b, False), (an, bn, True)):
+        c = api.mfma_fp8(torch.from_numpy(x).cuda(), torch.from_numpy(y).cuda()).cpu().numpy()
+        dx, dy = oracle.e4m3_decode(x), oracle.e4m3_decode(y)
+        exact = np.einsum("tik,tjk->tij", dx, dy)
+        mag = np.einsum("tik,tjk->tij", np.abs(dx), np.abs(dy))
+        frac = float(np.mean(c == exact.astype(np.float32)))
+        worst = float((np.abs(c - exact) / np.maximum(mag, 1e-300)).max())
+        print("fp8 mfma: correctly rounded fraction %.6f, max |err| / sum|terms| = 2^%.2f"
+              % (frac, np.log2(max(worst, 1e-300))))
+        assert worst <= FP8_DOT_REL
+        if exact_expected:
+            assert frac == 1.0
 
 
 # -------------------------------------------------------------- prepare ----
@@ -164,24 +176,47 @@ def test_attention_bf16_output(api):
 
 
 @pytest.mark.parametrize("shape", [SHAPES[0], SHAPES[1], SHAPES[4]])
-def test_attention_scores_and_bytes_bit_exact(api, shape):
+def test_attention_scores_and_bytes(api, shape):
+    """Dump of one query tile: the kernel's S is the matrix-core sum, within
+    FP8_DOT_REL * sum_c |q_c k_c| of the oracle's exactly rounded S; ExpCast
+    bytes agree except where that S difference (and the running max it moves)
+    can carry y across a rounding boundary, and then by one code."""
     B, H, L, d, grid = shape
     q, k, v = _inputs(B, H, L, d, 30 + L, grid)
     perm = synth.random_perms(B, H, L, 10)
     P = api.prepare(dev_bf16(q), dev_bf16(k), dev_bf16(v), perm_in=torch.from_numpy(perm).cuda())
     nqt = (L + 255) // 256
-    for bh, qt in {(0, 0), (B * H - 1, nqt - 1)}:
+    for bh, qt in sorted({(0, 0), (B * H - 1, nqt - 1)}):
         b, h = divmod(bh, H)
         out, S, Pb = api.attention_dump(P, bh, qt)
         S, Pb = S.cpu().numpy(), Pb.cpu().numpy()
         r0, r1 = qt * 256, min(L, qt * 256 + 256)
-        o = _oracle_prep(q, k, v, perm, b, h)
-        ro, rby, rS = oracle.attention_head(o, L, 8, rows=(r0, r1), want_bytes=True)
         n = r1 - r0
-        s_eq = np.mean(S[:n] == rS)
-        b_eq = np.mean(Pb[:n] == rby)
-        print("dump bh=%d qt=%d: S equal %.6f, bytes equal %.6f" % (bh, qt, s_eq, b_eq))
-        assert s_eq == 1.0 and b_eq == 1.0
+        o = _oracle_prep(q, k, v, perm, b, h)
+        ro, rby, rS, ry = oracle.attention_head(o, L, 8, rows=(r0, r1), want_bytes=True)
+        Lp = rS.shape[1]
+        qd = oracle.e4m3_decode(o["q8"][r0:r1])
+        kd = oracle.e4m3_decode(o["k8"])
+        mag = np.abs(qd) @ np.abs(kd).T                       # [n, Lp]
+        tolS = FP8_DOT_REL * mag
+        assert np.all(np.abs(S[:n].astype(np.float64) - rS) <= tolS + 1e-30)
+        # y moves by 8 c_b dS directly and by 8 dm through the running max
+        nb = Lp // 128
+        qb = np.minimum(np.arange(r0, r1) // 128, nb - 1)
+        cb = (np.float32(o["q_scale"][qb][:, None] * o["k_scale"][None, :]) * oracle.C0(d)).astype(np.float64)
+        cbk = np.repeat(cb, 128, axis=1)                       # [n, Lp]
+        blk_tol = (cbk * tolS).reshape(n, nb, 128).max(axis=2)
+        run_tol = np.maximum.accumulate(blk_tol, axis=1)      # bound on |dm| so far
+        ytol = 8 * cbk * tolS + 8 * np.repeat(run_tol, 128, axis=1) + 1e-4
+        diff = Pb[:n].astype(int) - rby.astype(int)
+        bad = diff != 0
+        frac = float(bad.mean())
+        dist = np.abs(ry.astype(np.float64) - (np.floor(ry.astype(np.float64)) + 0.5))
+        print("dump bh=%d qt=%d: S max |dS|/tol %.3f, byte mismatch %.2e (max |d| %d)"
+              % (bh, qt, float((np.abs(S[:n] - rS) / (tolS + 1e-30)).max()), frac, np.abs(diff).max()))
+        assert np.abs(diff).max() <= 1
+        assert frac <= 2e-3
+        assert np.all(dist[bad] <= ytol[bad])
 
 
 # ----------------------------------------------------------------- BF16 ----

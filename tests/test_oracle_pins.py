@@ -428,7 +428,7 @@ def test_oracle_bytes_are_expcast_of_scores(oracle_mod):
     cfg = synth.custom(1, 1, 256, 64)
     q, k, v = (a[0, 0] for a in synth.make_inputs(cfg, 5))
     P = oracle_mod.prepare_head(q, k, v, np.arange(256, dtype=np.int32))
-    out, by, S = oracle_mod.attention_head(P, 256, rows=(0, 16), want_bytes=True)
+    out, by, S, y = oracle_mod.attention_head(P, 256, rows=(0, 16), want_bytes=True)
     qd = oracle_mod.e4m3_decode(P["q8"][:16])
     kd = oracle_mod.e4m3_decode(P["k8"][:128])
     S0 = (qd @ kd.T).astype(np.float32)
@@ -439,6 +439,7 @@ def test_oracle_bytes_are_expcast_of_scores(oracle_mod):
     ref = oracle_mod.expcast(S0, np.float32(8) * cb, krow[:, None])
     assert np.array_equal(ref, by[:, :128])
     assert (by[:, :128].max(1) == 120).all()  # the row max lands on 2^8
+    assert np.array_equal(np.clip(np.rint(y[:, :128].astype(np.float64)), 0, 126).astype(np.uint8), by[:, :128])
 
 
 def test_synth_bf16_rounding_matches_library():

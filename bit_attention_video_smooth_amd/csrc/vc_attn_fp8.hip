@@ -65,13 +65,17 @@ __device__ __forceinline__ void slot_barrier() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// XOR swizzle of the 16-byte chunks of LDS tile rows.  LDS has 64 banks of
-// 4 bytes (256 bytes): two 128-byte rows (or four 64-byte rows) share one
-// bank line, so the chunk index is XORed with the row's line number, and the
-// 16 rows one matrix-core operand read touches land on 16 distinct chunk
-// positions of the bank space.
+// XOR swizzle of the 16-byte chunks of LDS tile rows.  A 16-byte-per-lane
+// LDS read moves 256 bytes per clock; it runs at that rate only when every
+// group of 8 consecutive lanes touches 8 distinct 16-byte positions modulo
+// 128 bytes and the 16 lanes of a quarter-wave touch 16 distinct positions
+// modulo 256 bytes (measured on gfx950).  A matrix-core operand read sends
+// rows r = 0..15 of a tile to lanes 0..15 with one chunk index, so the
+// swizzle must make the chunk position depend on r & 7 within each half and
+// flip between the halves: f(r) = (r & 7) ^ (r >> 3) for 128-byte rows, and
+// ((r >> 1) & 3) ^ (r >> 3) for 64-byte rows.
 __host__ __device__ constexpr int chunk_swizzle(int r, int nch) {
-    return nch == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3);
+    return nch == 8 ? ((r & 7) ^ ((r >> 3) & 1)) : (((r >> 1) & 3) ^ ((r >> 3) & 1));
 }
 
 // A/B operand of one 16-row tile: row `r` of a tile with `pitch`-byte rows of

@@ -24,11 +24,13 @@
 //    16-byte loads (XOR-swizzled 16-byte chunks) two blocks ahead; each
 //    stage is its own LDS object so the compiler's wait insertion can tell
 //    a stage being filled from the stage being read;
-//  * the two wave groups of a workgroup (one wave of each per SIMD) run the
-//    same four-slot program per block -- QK^T (matrix), softmax (vector),
-//    PV (matrix), epilogue (vector) -- offset by one slot, with a
-//    workgroup barrier between slots, so every matrix-core slot of one group
-//    overlaps a vector-ALU slot of the other on the same SIMD;
+//  * a wave issues a vector instruction at most every ~5 cycles (~10 when
+//    it depends on the one before), so the vector work is written as
+//    independent chains, and the two waves that share a SIMD run in phase
+//    so that both feed its vector ALU; one workgroup barrier per block
+//    keeps the LDS ring consistent, and the waves are free to drift apart
+//    within a block so that one's matrix products overlap the other's
+//    vector work;
 //  * workgroups are remapped so that the query tiles of one head run on
 //    one XCD and share its L2.
 #include "vc_device.hpp"
@@ -38,7 +40,7 @@ namespace vc {
 
 namespace {
 
-constexpr int NW = 8;    // waves per workgroup (two groups of four)
+constexpr int NW = 8;    // waves per workgroup (group 0 = waves 0-3 also copy)
 constexpr int QW = 32;   // queries per wave
 static_assert(NW * QW == ATTN_BM, "tile");
 
@@ -57,9 +59,9 @@ struct Fp8Tile {
     static constexpr int NCT = D / 16;          // 16-channel output tiles
 };
 
-// End of a slot: this wave's LDS reads are complete, then all waves meet.
-// The scheduling fences keep every instruction inside its slot.
-__device__ __forceinline__ void slot_barrier() {
+// End of a block: this wave's LDS reads are complete, then all waves meet.
+// The scheduling fences keep every instruction on its side of the barrier.
+__device__ __forceinline__ void block_barrier() {
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
@@ -98,6 +100,54 @@ __device__ __forceinline__ v8i lds_operand(const lds_u8* tile, int r, int pitch,
 
 __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// max(a, b, c) in one instruction; written out so that the compiler keeps
+// the chains it is given instead of re-associating them into a tree.
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
+// Row max of two query tiles over the four lane groups, the two reductions
+// interleaved.
+__device__ __forceinline__ void max_over_groups2(float& x, float& y) {
+    auto px = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    auto py = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+    x = fmaxf(__uint_as_float(px[0]), __uint_as_float(px[1]));
+    y = fmaxf(__uint_as_float(py[0]), __uint_as_float(py[1]));
+    auto qx = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    auto qy = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+    x = fmaxf(__uint_as_float(qx[0]), __uint_as_float(qx[1]));
+    y = fmaxf(__uint_as_float(qy[0]), __uint_as_float(qy[1]));
+}
+
+// ExpCast bytes of 16 values y[4 d + i] -> byte i of p_d: round to nearest
+// even, saturate to [0, 255] (y never exceeds 126 here).  The conversions of
+// the four dwords are interleaved so that each one's dependency on the
+// previous byte of the same dword is four instructions back.
+__device__ __forceinline__ void cvt_bytes16(const float (&y)[16], uint32_t& p0, uint32_t& p1,
+                                            uint32_t& p2, uint32_t& p3) {
+    asm("v_cvt_pk_u8_f32 %0, %4, 0, 0\n\t"
+        "v_cvt_pk_u8_f32 %1, %8, 0, 0\n\t"
+        "v_cvt_pk_u8_f32 %2, %12, 0, 0\n\t"
+        "v_cvt_pk_u8_f32 %3, %16, 0, 0\n\t"
+        "v_cvt_pk_u8_f32 %0, %5, 1, %0\n\t"
+        "v_cvt_pk_u8_f32 %1, %9, 1, %1\n\t"
+        "v_cvt_pk_u8_f32 %2, %13, 1, %2\n\t"
+        "v_cvt_pk_u8_f32 %3, %17, 1, %3\n\t"
+        "v_cvt_pk_u8_f32 %0, %6, 2, %0\n\t"
+        "v_cvt_pk_u8_f32 %1, %10, 2, %1\n\t"
+        "v_cvt_pk_u8_f32 %2, %14, 2, %2\n\t"
+        "v_cvt_pk_u8_f32 %3, %18, 2, %3\n\t"
+        "v_cvt_pk_u8_f32 %0, %7, 3, %0\n\t"
+        "v_cvt_pk_u8_f32 %1, %11, 3, %1\n\t"
+        "v_cvt_pk_u8_f32 %2, %15, 3, %2\n\t"
+        "v_cvt_pk_u8_f32 %3, %19, 3, %3"
+        : "=&v"(p0), "=&v"(p1), "=&v"(p2), "=&v"(p3)
+        : "v"(y[0]), "v"(y[1]), "v"(y[2]), "v"(y[3]), "v"(y[4]), "v"(y[5]), "v"(y[6]), "v"(y[7]),
+          "v"(y[8]), "v"(y[9]), "v"(y[10]), "v"(y[11]), "v"(y[12]), "v"(y[13]), "v"(y[14]), "v"(y[15]));
 }
 
 // Per-lane byte offsets of the 16-byte chunks a group-0 wave copies: the
@@ -216,7 +266,7 @@ struct Fp8Wave {
     v8i qop[2];
     v4f O[2][T::NCT];
     float m[2], l[2];
-    // per-block values carried between slots
+    // per-block values carried between the stages of a block
     v4f S[2][8];
     uint32_t P[2][8];
     float alpha[2];
@@ -260,7 +310,7 @@ struct Fp8Wave {
         }
     }
 
-    // slot A: S^T = K8 Q8^T for 8 key tiles x 2 query tiles (matrix cores).
+    // S^T = K8 Q8^T for 8 key tiles x 2 query tiles (matrix cores).
     // Operand reads run two key tiles ahead of the products.
     __device__ __forceinline__ void slot_qk(const lds_u8* st) {
         const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
@@ -284,41 +334,83 @@ struct Fp8Wave {
         }
     }
 
-    // slot B: running max and ExpCast-FP8 bytes (vector ALU).  The last,
-    // partial block (keys past L) has its own copy of the whole slot so that
-    // no masking work leaks into the full blocks.
+    // Running max and ExpCast-FP8 bytes (vector ALU).  A wave issues a
+    // dependent vector instruction only every ~10 cycles but independent ones
+    // every ~5, so the work is laid out as independent chains: four max3
+    // chains (two per query tile), the two cross-lane reductions side by
+    // side, and the byte conversions four dwords at a time.  The last, partial
+    // block (keys past L) has its own copy so that no masking work leaks into
+    // the full blocks.
     template <bool MASKED>
     __device__ __forceinline__ void softmax_rows(int kb, float cb, int lim) {
         const float c8 = 8.0f * cb;
+        float mx[2];
+        if (!MASKED) {
+            float ch[2][2];
 #pragma unroll
-        for (int qt = 0; qt < 2; qt++) {
-            float mx = -INFINITY;
-            if (!MASKED) {
+            for (int qt = 0; qt < 2; qt++)
 #pragma unroll
-                for (int kt = 0; kt < 8; kt++)
-                    mx = fmaxf(fmaxf(mx, fmaxf(S[qt][kt][0], S[qt][kt][1])), fmaxf(S[qt][kt][2], S[qt][kt][3]));
-            } else {
+                for (int h = 0; h < 2; h++) ch[qt][h] = vmax3(S[qt][4 * h][0], S[qt][4 * h][1], S[qt][4 * h][2]);
+            // the other 13 scores of each chain: S[4h][3], then kt = 4h+1 .. 4h+3
+#pragma unroll
+            for (int j = 0; j < 13; j += 2) {
+#pragma unroll
+                for (int qt = 0; qt < 2; qt++)
+#pragma unroll
+                    for (int h = 0; h < 2; h++) {
+                        const int e0 = 3 + j, e1 = 4 + j;  // element index within the chain's 16
+                        const float a0 = S[qt][4 * h + e0 / 4][e0 % 4];
+                        if (e1 < 16)
+                            ch[qt][h] = vmax3(ch[qt][h], a0, S[qt][4 * h + e1 / 4][e1 % 4]);
+                        else
+                            ch[qt][h] = fmaxf(ch[qt][h], a0);
+                    }
+            }
+#pragma unroll
+            for (int qt = 0; qt < 2; qt++) mx[qt] = fmaxf(ch[qt][0], ch[qt][1]);
+        } else {
+#pragma unroll
+            for (int qt = 0; qt < 2; qt++) {
+                mx[qt] = -INFINITY;
                 // key 16 kt + 4 g + i exists iff 16 kt + i < lim
 #pragma unroll
                 for (int kt = 0; kt < 8; kt++)
 #pragma unroll
-                    for (int i = 0; i < 4; i++) mx = fmaxf(mx, (16 * kt + i < lim) ? S[qt][kt][i] : -INFINITY);
+                    for (int i = 0; i < 4; i++) mx[qt] = fmaxf(mx[qt], (16 * kt + i < lim) ? S[qt][kt][i] : -INFINITY);
             }
-            mx = max_over_groups(mx);
-            const float t = __fmul_rn(mx, cb);
+        }
+        max_over_groups2(mx[0], mx[1]);
+        float krow[2];
+#pragma unroll
+        for (int qt = 0; qt < 2; qt++) {
+            const float t = __fmul_rn(mx[qt], cb);
             const float mn = fmaxf(m[qt], t);
-            const float krow = __fsub_rn(a.KB, 8.0f * mn);
+            krow[qt] = __fsub_rn(a.KB, 8.0f * mn);
             alpha[qt] = __builtin_amdgcn_exp2f(m[qt] - mn);  // 2^(m - m'), 0 on the first block
             m[qt] = mn;
+        }
 #pragma unroll
-            for (int kt = 0; kt < 8; kt++) {
-                uint32_t pk = 0;
+        for (int qt = 0; qt < 2; qt++) {
+            if (!MASKED) {
 #pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    if (!MASKED || 16 * kt + i < lim)  // keys past L keep byte 0
-                        pk = expcast_byte_into(S[qt][kt][i], c8, krow, i, pk);
+                for (int k4 = 0; k4 < 8; k4 += 4) {
+                    float y[16];
+#pragma unroll
+                    for (int d = 0; d < 4; d++)
+#pragma unroll
+                        for (int i = 0; i < 4; i++) y[4 * d + i] = __builtin_fmaf(S[qt][k4 + d][i], c8, krow[qt]);
+                    cvt_bytes16(y, P[qt][k4], P[qt][k4 + 1], P[qt][k4 + 2], P[qt][k4 + 3]);
                 }
-                P[qt][kt] = pk;
+            } else {
+#pragma unroll
+                for (int kt = 0; kt < 8; kt++) {
+                    uint32_t pk = 0;
+#pragma unroll
+                    for (int i = 0; i < 4; i++)
+                        if (16 * kt + i < lim)  // keys past L keep byte 0
+                            pk = expcast_byte_into(S[qt][kt][i], c8, krow[qt], i, pk);
+                    P[qt][kt] = pk;
+                }
             }
             if (DUMP && dump) {
                 const int rl = w * QW + 16 * qt + col;
@@ -346,12 +438,12 @@ struct Fp8Wave {
             softmax_rows<false>(kb, cb, 0);
     }
 
-    // slot C: row sums (ones(16x128) * P^T, exact), V8^T P^T on the matrix
+    // Row sums (ones(16x128) * P^T, exact), V8^T P^T on the matrix
     // cores, and O += s_v (.) acc + l_b mean_b on the vector ALU, one channel
     // tile behind the products.
     __device__ __forceinline__ void slot_pv(const lds_u8* st) {
         const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
-        v8i ones;  // E4M3 1.0, made here so it takes no register across slots
+        v8i ones;  // E4M3 1.0, made here so it takes no register across the block
         int one4;
         asm volatile("v_mov_b32 %0, 0x38383838" : "=v"(one4));
 #pragma unroll
@@ -393,27 +485,27 @@ struct Fp8Wave {
         }
     }
 
-    // The three slots of block kb (stage `cur`).  The loading group (LOADER)
-    // starts the copy of block kb + 2 into stage `ahead` during its softmax
-    // slot -- unconditionally, past the end it re-copies the last block into a
-    // stage nobody reads again, so the copy count per block is fixed -- and at
-    // the end of its PV slot waits for its share of block kb + 1 (the barrier
-    // that follows publishes the whole block to both groups).
+    // Block kb (stage `cur`): S^T on the matrix cores, softmax bytes on the
+    // vector ALU, then P V and the epilogue.  The loading group (LOADER)
+    // starts the copy of block kb + 2 into stage `ahead` (the stage of block
+    // kb - 1, which every wave left before the previous barrier) --
+    // unconditionally: past the end it re-copies the last block into a stage
+    // nobody reads again, so the copy count per block is fixed -- and at the
+    // end waits for its share of block kb + 1; the one barrier per block then
+    // publishes block kb + 1 to all waves and frees stage `cur`.
     template <bool LOADER>
     __device__ __forceinline__ void block(const Fp8Loader<D>& ld, int kb, const lds_u8* cur,
                                           lds_u8* ahead) {
         slot_qk(cur);
-        slot_barrier();
         if (LOADER) ld.issue(ahead, min(kb + 2, nb - 1));
         slot_softmax(kb, cur);
-        // rescale only when some row of the wave raised its max
-        if (__any((alpha[0] != 1.0f) | (alpha[1] != 1.0f))) {
+        // rescale a query tile only when one of its rows raised its max
 #pragma unroll
-            for (int qt = 0; qt < 2; qt++)
+        for (int qt = 0; qt < 2; qt++)
+            if (__any(alpha[qt] != 1.0f)) {
 #pragma unroll
                 for (int ct = 0; ct < T::NCT; ct++) O[qt][ct] *= alpha[qt];
-        }
-        slot_barrier();
+            }
         slot_pv(cur);
         if (LOADER) {
             if (DUMP)
@@ -421,7 +513,7 @@ struct Fp8Wave {
             else
                 wait_vmcnt<Fp8Loader<D>::NLD>();
         }
-        slot_barrier();
+        block_barrier();
     }
 
     template <bool LOADER>
@@ -452,22 +544,18 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fp8_kernel(AttnArgs a) {
     const Fp8Loader<D> ld(a, bh, w, lane);
     const int nb = a.nb;
 
-    // Blocks 0 and 1 are in flight before the first slot; block 0 is
-    // published by the first barrier.  Group 1 then waits one more slot so
-    // that its matrix slots overlap group 0's vector slots.
+    // Blocks 0 and 1 are in flight before the loop; block 0 is published by
+    // the first barrier, and every wave then passes one barrier per block.
+    // The loading waves drain their copies past the end before they exit.
     if (s.grp == 0) {
         ld.issue(st0, 0);
         ld.issue(st1, min(1, nb - 1));
         wait_vmcnt<Fp8Loader<D>::NLD>();
-        slot_barrier();
-    } else {
-        slot_barrier();
-        slot_barrier();
     }
+    block_barrier();
     if (s.grp == 0) {
         s.template run<true>(ld, st0, st1, st2);
-        wait_vmcnt<0>();  // copies past the end
-        slot_barrier();
+        wait_vmcnt<0>();
     } else {
         s.template run<false>(ld, st0, st1, st2);
     }

@@ -37,15 +37,73 @@ def parse():
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--no-bf16", action="store_true")
     p.add_argument("--v-scale-mode", type=int, default=0)
+    p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                   help="only run a plain device copy of MIB MiB (negation, fp32) three times: the "
+                        "reference kernel of known size that calibrates the HBM byte counters")
     return p.parse_args()
+
+
+# Sources the attention kernel is built from; the committed HBM-traffic
+# summary records their hash and is ignored once any of them changes.
+KERNEL_SOURCES = ["bit_attention_video_smooth_amd/csrc/vc_attn_fp8.hip",
+                  "bit_attention_video_smooth_amd/csrc/vc_device.hpp",
+                  "bit_attention_video_smooth_amd/csrc/vc_internal.hpp",
+                  "bit_attention_video_smooth_amd/build.py"]
+TRAFFIC_SUMMARY = "profiles/attn_fp8_wan720p_hbm_traffic.txt"
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the attention kernel from the committed
+    FETCH_SIZE / WRITE_SIZE summary (already scaled by the copy-kernel
+    factors), or None if the summary is absent, is for another workload, or
+    was taken on different kernel sources."""
+    path = os.path.join(ROOT, TRAFFIC_SUMMARY)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.lstrip().startswith("#"):
+                key, val = line.split("=", 1)
+                kv[key.strip()] = val.strip()
+    if kv.get("workload") != workload or kv.get("source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_probe(mib):
+    import torch
+    n = (mib << 20) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4, "launches": 3}))
 
 
 def main():
     args = parse()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(the workload shards by (batch, head) with no exchange; see DESIGN.md)", file=sys.stderr)
+              "(the workload shards by (batch, head) with no exchange between GPUs)", file=sys.stderr)
         sys.exit(2)
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     import numpy as np
     import torch
 
@@ -144,7 +202,7 @@ def main():
                     "quant_gbs": quant_bytes / quant_ms / 1e6},
         "bf16_attention": bf16,
         "roofline": {"bound": "mfma", "achieved": attn_tflops, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": attn_tflops / FP8_PEAK_TFLOPS, "traffic": None},
+                     "frac": attn_tflops / FP8_PEAK_TFLOPS, "traffic": measured_traffic(cfg.name)},
         "cpu_baseline": None,
     }
     if not args.no_cpu:

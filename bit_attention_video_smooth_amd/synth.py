@@ -12,9 +12,9 @@ the structure the pages describe stand in for them:
 * V is a smooth spatio-temporal field (a sum of 8 random low-frequency
   sinusoids over (t/T, h/Hg, w/W), amplitudes ~ N(0, 1/8)) plus
   0.3 * N(0, 1) noise, with a few outlier tokens scaled up in a few
-  channels that change from head to head -- the value outliers "sit in a
-  few tokens, and their channels shift across heads" (MarkTechPost
-  abstract on VC-Attention);
+  channels that change from head to head, the outlier structure the
+  MarkTechPost abstract on VC-Attention describes (a handful of tokens,
+  with no channel pattern that holds across heads);
 * the classifier-free-guidance pair (B = 2) shares the V field, noise and
   outliers, plus an independent N(0, 0.1^2) perturbation per batch entry;
 * everything is rounded to bf16 (round to nearest even) last.

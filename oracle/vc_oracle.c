@@ -20,7 +20,7 @@
  *         Softmax".
  *
  * What is computed (all free choices are fixed here; each is a reading of the
- * pages and is listed in the design doc):
+ * pages where they leave a step open):
  *  - E4M3 is the OCP E4M3FN format (bias 7, max 448, no infinities): [MTP]
  *    states that an E4M3 byte read as an integer is about 8*log2(v)+56, which
  *    holds only with exponent bias 7.
@@ -164,8 +164,9 @@ static inline float vco_bf16(uint16_t u)
 
 /* ------------------------------------------------------------------------ */
 /* Step a1 (QK smoothing, K half): per-channel mean of K over all L tokens.  */
-/* The pages evaluate "after QK smoothing"; subtracting one vector from every */
-/* key adds a per-query constant to each score row, which softmax ignores.   */
+/* The pages measure with QK smoothing applied; subtracting one vector from  */
+/* every key adds a per-query constant to each score row, which softmax     */
+/* ignores.                                                                  */
 /* ------------------------------------------------------------------------ */
 
 void vco_k_mean(const uint16_t* k, int L, int d, float* kbar)

@@ -36,7 +36,8 @@ def flags():
 
 # NaN inputs are outside the library's contract; without NaN semantics the
 # compiler drops the quieting moves it otherwise puts around every max.
-EXTRA = {"vc_attn_fp8.hip": ["-fno-honor-nans"], "vc_attn_bf16.hip": ["-fno-honor-nans"]}
+EXTRA = {"vc_attn_fp8.hip": ["-fno-honor-nans"], "vc_attn_bf16.hip": ["-fno-honor-nans"],
+         "vc_kmeans.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src: str) -> str:

@@ -5,15 +5,19 @@
 // same block; MarkTechPost abstract: 128-token blocks after sorting).
 //
 // Per Lloyd round:
-//   assign  -- distances ||c||^2 - 2 x.c on BF16 matrix cores (centroids as a
-//              bf16 high part plus a bf16 low part, so x.c carries ~16
-//              mantissa bits), argmin fused in registers, ties to the lowest
-//              centroid index;
+//   assign  -- squared distances ||c||^2 - 2 x.c on BF16 matrix cores, the
+//              centroid split into a bf16 high part and a bf16 low part so
+//              that x.c (x is bf16 already) carries ~16 mantissa bits;
+//              argmin fused in registers, ties to the lowest centroid index;
+//              one workgroup takes 512 tokens so that each centroid tile it
+//              stages in LDS serves many tokens;
 //   sort    -- stable counting sort by cluster: per-chunk histograms, one
 //              scan per head in (cluster, chunk) order, in-chunk ranks;
 //   update  -- one workgroup per cluster sums its members (gathered through
-//              the sorted order) in fp64 and divides once; empty clusters
-//              keep their centroid.
+//              the sorted order, 16 bytes per lane) in fp64 and divides once;
+//              empty clusters keep their centroid.
+// With the split, the assignment follows the exact-arithmetic one except at
+// near-exact ties.
 // Initial centroids: token range cut into k strata, one SplitMix64-drawn
 // token per stratum (Steele, Lea & Flood 2014; counter-based, so every
 // centroid draws independently).
@@ -24,8 +28,11 @@ namespace vc {
 
 namespace {
 
-constexpr int KT = 64;      // centroids per LDS tile of the assign kernel
-constexpr int CHUNK = 256;  // tokens per chunk of the counting sort
+constexpr int KT = 64;       // centroids per LDS tile of the assign kernel
+constexpr int CHUNK = 1024;  // tokens per chunk of the counting sort
+constexpr int ATOK = 512;    // tokens per assign workgroup (8 waves x 64)
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint64_t splitmix64(uint64_t seed, uint64_t i) {
     uint64_t z = seed + (i + 1) * 0x9E3779B97F4A7C15ULL;
@@ -45,7 +52,8 @@ __global__ void km_init(const uint16_t* __restrict__ v, float* __restrict__ cent
         cent[((size_t)bh * kpad + c) * d + e] = bf16_to_f32(v[((size_t)bh * L + j) * d + e]);
 }
 
-// fp32 centroids -> bf16 high/low parts and squared norms (padding: +inf norm)
+// fp32 centroids -> bf16 high and low parts (round to nearest even) and the
+// squared norm (padding rows: zeros and +inf norm, never chosen)
 __global__ void km_split(const float* __restrict__ cent, uint16_t* __restrict__ hi,
                          uint16_t* __restrict__ lo, float* __restrict__ cnorm, int d, int k, int kpad) {
     const int c = blockIdx.x, bh = blockIdx.y;
@@ -55,7 +63,7 @@ __global__ void km_split(const float* __restrict__ cent, uint16_t* __restrict__ 
         const size_t i = ((size_t)bh * kpad + c) * d + e;
         const float x = c < k ? cent[i] : 0.f;
         const uint32_t u = __float_as_uint(x);
-        const uint32_t hb = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;  // round to nearest even
+        const uint32_t hb = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
         const float rem = x - __uint_as_float(hb << 16);
         const uint32_t ur = __float_as_uint(rem);
         const uint32_t lb = (ur + 0x7FFFu + ((ur >> 16) & 1u)) >> 16;
@@ -84,33 +92,45 @@ __device__ __forceinline__ v8bf as_bf(uint4 x) {
     return r;
 }
 
-// Better (value, index) of two candidates: lower distance, then lower index.
-__device__ __forceinline__ void take_better(float& bv, int& bi, float v, int i) {
-    if (v < bv || (v == bv && i < bi)) {
-        bv = v;
-        bi = i;
-    }
+// Position of logical 16-byte chunk lc of centroid row r in LDS.  A 16-byte
+// LDS read is conflict-free when every 8 consecutive lanes hit distinct
+// 16-byte positions modulo 128 bytes and every 16 lanes distinct positions
+// modulo 256 bytes; an operand read sends rows r = 0..15 of a tile to lanes
+// 0..15 with one lc, which these XORs spread.
+template <int D>
+__device__ __forceinline__ int cent_chunk(int r, int lc) {
+    if (D == 128) return lc ^ (r & 15);                     // 256-byte rows, 16 chunks
+    return lc ^ ((r & 7) ^ ((r >> 3) & 1));                 // 128-byte rows, 8 chunks
 }
 
-// Grid (ceil(L/128), B*H), 256 threads: 4 waves x 32 tokens.  Output tile of
-// the matrix core is (16 centroids) x (16 tokens), so each lane scans 4
-// centroids of one token per tile; four lanes per token merge at the end.
+// Grid (ceil(L/512), B*H), 512 threads: 8 waves x 64 tokens.  The output
+// tile of the matrix core is (16 centroids) x (16 tokens): a lane scans 4
+// centroids of one token per tile and the four lanes of a token merge at the
+// end.  Centroid tiles of 64 rows are double-buffered in LDS.  The product
+// accumulates onto -||c||^2 / 2, so the nearest centroid is the largest
+// score x.c - ||c||^2 / 2; a lane meets its candidates in increasing index
+// order, so a strict comparison keeps the lowest index among equal scores.
 template <int D>
-__global__ __launch_bounds__(256) void km_assign(const uint16_t* __restrict__ v,
+__global__ __launch_bounds__(512) void km_assign(const uint16_t* __restrict__ v,
                                                  const uint16_t* __restrict__ chi,
                                                  const uint16_t* __restrict__ clo,
                                                  const float* __restrict__ cnorm,
                                                  int32_t* __restrict__ assign, int L, int k, int kpad) {
-    constexpr int NU = D / 32;
-    constexpr int RB = D * 2;  // bytes per centroid row
-    __shared__ __attribute__((aligned(16))) uint8_t sh[2][KT * RB];
-    __shared__ float sn[KT];
+    constexpr int NU = D / 32;          // 32-element steps of the bf16 product
+    constexpr int RB = D * 2;           // bytes per centroid row
+    constexpr int NTT = 4;              // 16-token tiles per wave
+    constexpr int NCH = KT * RB / 16;   // 16-byte chunks per centroid tile
+    constexpr int CPT = NCH / 512;      // chunks staged per thread
+    constexpr int CPR = RB / 16;        // chunks per row
+    __shared__ __attribute__((aligned(16))) uint8_t sh[2][KT * RB];  // high parts
+    __shared__ __attribute__((aligned(16))) uint8_t sl[2][KT * RB];  // low parts
+    __shared__ __attribute__((aligned(16))) float sn[2][KT];  // -||c||^2 / 2
     const int bh = blockIdx.y;
     const int t = threadIdx.x, w = t >> 6, lane = t & 63, col = lane & 15, g = lane >> 4;
-    const int tok0 = blockIdx.x * 128 + w * 32;
-    v8bf xop[2][NU];
+    const int tok0 = blockIdx.x * ATOK + w * 64;
+    v8bf xop[NTT][NU];
 #pragma unroll
-    for (int tt = 0; tt < 2; tt++) {
+    for (int tt = 0; tt < NTT; tt++) {
         const int j = tok0 + 16 * tt + col;
 #pragma unroll
         for (int u = 0; u < NU; u++) {
@@ -119,39 +139,67 @@ __global__ __launch_bounds__(256) void km_assign(const uint16_t* __restrict__ v,
             xop[tt][u] = as_bf(x);
         }
     }
-    float bv[2] = {INFINITY, INFINITY};
-    int bi[2] = {0x7FFFFFFF, 0x7FFFFFFF};
-    const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
+    float bv[NTT];
+    int bi[NTT];
+#pragma unroll
+    for (int tt = 0; tt < NTT; tt++) {
+        bv[tt] = -INFINITY;
+        bi[tt] = 0x7FFFFFFF;
+    }
     const uint8_t* hib = reinterpret_cast<const uint8_t*>(chi + (size_t)bh * kpad * D);
     const uint8_t* lob = reinterpret_cast<const uint8_t*>(clo + (size_t)bh * kpad * D);
-    for (int c0 = 0; c0 < kpad; c0 += KT) {
-        // stage KT centroid rows (hi, lo) into LDS, 16-byte chunks, XOR swizzle
-        constexpr int NCH = KT * RB / 16;
-        for (int p = t; p < NCH; p += 256) {
-            const int r = p / (RB / 16), cp = p % (RB / 16);
-            const int cs = cp ^ (r & (RB / 16 - 1) & 7);
-            *reinterpret_cast<uint4*>(&sh[0][p * 16]) =
-                *reinterpret_cast<const uint4*>(hib + (size_t)(c0 + r) * RB + cs * 16);
-            *reinterpret_cast<uint4*>(&sh[1][p * 16]) =
-                *reinterpret_cast<const uint4*>(lob + (size_t)(c0 + r) * RB + cs * 16);
+    const float* nb = cnorm + (size_t)bh * kpad;
+    // staging: thread t copies LDS chunks p = t + 512 i, i < CPT; chunk p of
+    // LDS row r holds logical chunk cent_chunk(r, p % CPR) of centroid row r
+    size_t goff[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT; i++) {
+        const int p = t + 512 * i, r = p / CPR, cp = p % CPR;
+        goff[i] = (size_t)r * RB + cent_chunk<D>(r, cp) * 16;
+    }
+    // (ext-vector registers, so that the staged copies stay in VGPRs)
+    u32x4 stg[CPT], stl[CPT];
+    float stn = 0.f;
+#pragma unroll
+    for (int i = 0; i < CPT; i++) {
+        stg[i] = *reinterpret_cast<const u32x4*>(hib + goff[i]);
+        stl[i] = *reinterpret_cast<const u32x4*>(lob + goff[i]);
+    }
+    if (t < KT) stn = nb[t];
+#pragma unroll
+    for (int i = 0; i < CPT; i++) {
+        *reinterpret_cast<u32x4*>(&sh[0][(t + 512 * i) * 16]) = stg[i];
+        *reinterpret_cast<u32x4*>(&sl[0][(t + 512 * i) * 16]) = stl[i];
+    }
+    if (t < KT) sn[0][t] = -0.5f * stn;
+    __syncthreads();
+    const int ntile = kpad / KT;
+    for (int tile = 0; tile < ntile; tile++) {
+        const int c0 = tile * KT, buf = tile & 1;
+        if (tile + 1 < ntile) {
+            const size_t cb = (size_t)(c0 + KT) * RB;
+#pragma unroll
+            for (int i = 0; i < CPT; i++) {
+                stg[i] = *reinterpret_cast<const u32x4*>(hib + cb + goff[i]);
+                stl[i] = *reinterpret_cast<const u32x4*>(lob + cb + goff[i]);
+            }
+            if (t < KT) stn = nb[c0 + KT + t];
         }
-        if (t < KT) sn[t] = cnorm[(size_t)bh * kpad + c0 + t];
-        __syncthreads();
 #pragma unroll
         for (int ct = 0; ct < KT / 16; ct++) {
+            if (c0 + 16 * ct >= k) break;  // padding tiles (uniform)
             const int r = 16 * ct + col;
             v8bf ah[NU], al[NU];
 #pragma unroll
             for (int u = 0; u < NU; u++) {
-                // logical chunk 4u+g of row r lives at (4u+g) ^ swizzle
-                const int lc = 4 * u + g;
-                const int pc = lc ^ (r & (RB / 16 - 1) & 7);
-                ah[u] = as_bf(*reinterpret_cast<const uint4*>(&sh[0][r * RB + pc * 16]));
-                al[u] = as_bf(*reinterpret_cast<const uint4*>(&sh[1][r * RB + pc * 16]));
+                const int pos = r * RB + cent_chunk<D>(r, 4 * u + g) * 16;
+                ah[u] = as_bf(*reinterpret_cast<const uint4*>(&sh[buf][pos]));
+                al[u] = as_bf(*reinterpret_cast<const uint4*>(&sl[buf][pos]));
             }
+            const v4f init = *reinterpret_cast<const v4f*>(&sn[buf][16 * ct + 4 * g]);
 #pragma unroll
-            for (int tt = 0; tt < 2; tt++) {
-                v4f acc = zero4;
+            for (int tt = 0; tt < NTT; tt++) {
+                v4f acc = init;
 #pragma unroll
                 for (int u = 0; u < NU; u++) {
                     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[u], xop[tt][u], acc, 0, 0, 0);
@@ -159,22 +207,33 @@ __global__ __launch_bounds__(256) void km_assign(const uint16_t* __restrict__ v,
                 }
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
-                    const int ci = 16 * ct + 4 * g + i;
-                    const float dist = __builtin_fmaf(-2.0f, acc[i], sn[ci]);
-                    take_better(bv[tt], bi[tt], dist, c0 + ci);
+                    const bool better = acc[i] > bv[tt];
+                    bv[tt] = fmaxf(bv[tt], acc[i]);
+                    bi[tt] = better ? c0 + 16 * ct + 4 * g + i : bi[tt];
                 }
             }
+        }
+        if (tile + 1 < ntile) {
+#pragma unroll
+            for (int i = 0; i < CPT; i++) {
+                *reinterpret_cast<u32x4*>(&sh[buf ^ 1][(t + 512 * i) * 16]) = stg[i];
+                *reinterpret_cast<u32x4*>(&sl[buf ^ 1][(t + 512 * i) * 16]) = stl[i];
+            }
+            if (t < KT) sn[buf ^ 1][t] = -0.5f * stn;
         }
         __syncthreads();
     }
 #pragma unroll
-    for (int tt = 0; tt < 2; tt++) {
+    for (int tt = 0; tt < NTT; tt++) {
         // merge the four lane groups (lanes col, col+16, col+32, col+48)
 #pragma unroll
         for (int o = 16; o <= 32; o <<= 1) {
             const float ov = __shfl_xor(bv[tt], o);
             const int oi = __shfl_xor(bi[tt], o);
-            take_better(bv[tt], bi[tt], ov, oi);
+            if (ov > bv[tt] || (ov == bv[tt] && oi < bi[tt])) {
+                bv[tt] = ov;
+                bi[tt] = oi;
+            }
         }
         const int j = tok0 + 16 * tt + col;
         if (g == 0 && j < L) assign[(size_t)bh * L + j] = bi[tt] < k ? bi[tt] : k - 1;
@@ -233,69 +292,124 @@ __global__ __launch_bounds__(1024) void km_scan(int32_t* __restrict__ cnt, int32
     }
 }
 
-// stable scatter: slot = start[chunk][a_j] + #(earlier tokens of the chunk in a_j)
+// Stable scatter of one chunk: the waves take their 64 tokens in order; a
+// token's slot is its cluster's running position in LDS plus the number of
+// earlier lanes of its wave in the same cluster; the last such lane advances
+// the running position before the next wave reads it.
 __global__ __launch_bounds__(CHUNK) void km_scatter(const int32_t* __restrict__ assign,
                                                     const int32_t* __restrict__ cnt,
                                                     int32_t* __restrict__ perm, int L, int k,
                                                     int nchunk) {
-    __shared__ int sa[CHUNK];
+    extern __shared__ int run[];
     const int ch = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
+    const int w = t >> 6, lane = t & 63;
+    for (int c = t; c < k; c += CHUNK) run[c] = cnt[((size_t)bh * nchunk + ch) * k + c];
     const int j = ch * CHUNK + t;
     const int a = j < L ? assign[(size_t)bh * L + j] : -1;
-    sa[t] = a;
-    __syncthreads();
-    if (j >= L) return;
     int rank = 0;
-    for (int i = 0; i < t; i++) rank += (sa[i] == a);
-    perm[(size_t)bh * L + cnt[((size_t)bh * nchunk + ch) * k + a] + rank] = j;
+    bool last = true;
+    for (int i = 0; i < 64; i++) {
+        const int ai = __shfl(a, i);
+        rank += (i < lane && ai == a) ? 1 : 0;
+        if (i > lane && ai == a) last = false;
+    }
+    __syncthreads();
+    for (int s = 0; s < CHUNK / 64; s++) {
+        if (w == s && a >= 0) {
+            const int slot = run[a] + rank;
+            perm[(size_t)bh * L + slot] = j;
+            if (last) run[a] = slot + 1;
+        }
+        __syncthreads();
+    }
 }
 
-// one workgroup per (cluster, head): centroid = fp64 mean of members
+// One workgroup per (cluster, head): centroid = fp64 mean of its members.
+// Lanes take 16 bytes (8 channels) of a member row; 256 / (D / 8) rows are
+// in flight per pass, two passes unrolled.
 template <int D>
 __global__ __launch_bounds__(256) void km_update(const uint16_t* __restrict__ v,
                                                  const int32_t* __restrict__ perm,
                                                  const int32_t* __restrict__ counts,
                                                  const int32_t* __restrict__ starts,
                                                  float* __restrict__ cent, int L, int k, int kpad) {
-    constexpr int RPI = 256 / D;  // member rows per iteration
-    __shared__ double red[RPI][D];
+    constexpr int LPR = D / 8;      // lanes per row
+    constexpr int RPP = 256 / LPR;  // rows per pass
+    __shared__ double red[RPP][D];
     const int c = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
-    const int e = t % D, rs = t / D;
+    const int q = t % LPR, rs = t / LPR;
     const int n = counts[(size_t)bh * k + c];
     if (n == 0) return;  // empty cluster keeps its centroid (uniform branch)
     const int s0 = starts[(size_t)bh * k + c];
-    double s = 0.0;
-    for (int i = rs; i < n; i += RPI) {
-        const int j = perm[(size_t)bh * L + s0 + i];
-        s += (double)bf16_to_f32(v[((size_t)bh * L + j) * D + e]);
+    const int32_t* pm = perm + (size_t)bh * L + s0;
+    const uint16_t* vb = v + (size_t)bh * L * D + 8 * q;
+    double acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) acc[e] = 0.0;
+    int i = rs;
+    for (; i + RPP < n; i += 2 * RPP) {
+        const int j0 = pm[i], j1 = pm[i + RPP];
+        const uint4 x0 = *reinterpret_cast<const uint4*>(vb + (size_t)j0 * D);
+        const uint4 x1 = *reinterpret_cast<const uint4*>(vb + (size_t)j1 * D);
+        const uint32_t w0[4] = {x0.x, x0.y, x0.z, x0.w}, w1[4] = {x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            acc[2 * e] += (double)__uint_as_float(w0[e] << 16);
+            acc[2 * e + 1] += (double)__uint_as_float(w0[e] & 0xFFFF0000u);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            acc[2 * e] += (double)__uint_as_float(w1[e] << 16);
+            acc[2 * e + 1] += (double)__uint_as_float(w1[e] & 0xFFFF0000u);
+        }
     }
-    red[rs][e] = s;
+    if (i < n) {
+        const uint4 x0 = *reinterpret_cast<const uint4*>(vb + (size_t)pm[i] * D);
+        const uint32_t w0[4] = {x0.x, x0.y, x0.z, x0.w};
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            acc[2 * e] += (double)__uint_as_float(w0[e] << 16);
+            acc[2 * e + 1] += (double)__uint_as_float(w0[e] & 0xFFFF0000u);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; e++) red[rs][8 * q + e] = acc[e];
     __syncthreads();
-    if (rs == 0) {
+    if (t < D) {
         double tot = 0.0;
-        for (int i = 0; i < RPI; i++) tot += red[i][e];
-        cent[((size_t)bh * kpad + c) * D + e] = (float)(tot / (double)n);
+        for (int r = 0; r < RPP; r++) tot += red[r][t];
+        cent[((size_t)bh * kpad + c) * D + t] = (float)(tot / (double)n);
     }
 }
 
-// objective: sum_j ||x_j - C_{a_j}||^2 in fp64, per 256-token chunk
+// objective: sum_j ||x_j - C_{a_j}||^2 in fp64, per chunk of CHUNK tokens;
+// D / 8 lanes per token, 16 bytes of the row each
 template <int D>
 __global__ __launch_bounds__(256) void km_objective(const uint16_t* __restrict__ v,
                                                     const int32_t* __restrict__ assign,
                                                     const float* __restrict__ cent,
                                                     double* __restrict__ part, int L, int kpad,
                                                     int nchunk) {
+    constexpr int LPR = D / 8, TPP = 256 / LPR;
     __shared__ double red[4];
     const int ch = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
-    const int j = ch * CHUNK + t;
+    const int q = t % LPR, r = t / LPR;
     double s = 0.0;
-    if (j < L) {
+    for (int jj = r; jj < CHUNK; jj += TPP) {
+        const int j = ch * CHUNK + jj;
+        if (j >= L) break;
         const int a = assign[(size_t)bh * L + j];
-        const uint16_t* x = v + ((size_t)bh * L + j) * D;
-        const float* cc = cent + ((size_t)bh * kpad + a) * D;
-        for (int e = 0; e < D; e++) {
-            const double dd = (double)bf16_to_f32(x[e]) - (double)cc[e];
-            s += dd * dd;
+        const uint4 x = *reinterpret_cast<const uint4*>(v + ((size_t)bh * L + j) * D + 8 * q);
+        const float4* cc = reinterpret_cast<const float4*>(cent + ((size_t)bh * kpad + a) * D + 8 * q);
+        const float4 c0 = cc[0], c1 = cc[1];
+        const uint32_t wv[4] = {x.x, x.y, x.z, x.w};
+        const float cf[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const double d0 = (double)__uint_as_float(wv[e] << 16) - (double)cf[2 * e];
+            const double d1 = (double)__uint_as_float(wv[e] & 0xFFFF0000u) - (double)cf[2 * e + 1];
+            s += d0 * d0;
+            s += d1 * d1;
         }
     }
     s = wave_sum_f64(s);
@@ -317,21 +431,21 @@ template <int D>
 hipError_t launch_kmeans_t(const KmeansArgs& a, hipStream_t st) {
     const int BH = a.B * a.H;
     const uint16_t* v = static_cast<const uint16_t*>(a.v);
-    const int ntile = (a.L + 127) / 128;
+    const int ntile = (a.L + ATOK - 1) / ATOK;
     hipLaunchKernelGGL(km_init, dim3(a.k, BH), dim3(64), 0, st, v, a.cent, a.L, D, a.k, a.kpad, a.H,
                        a.seed);
     const int rounds = a.iters > 0 ? a.iters : 1;
     for (int it = 0; it < rounds; it++) {
         hipLaunchKernelGGL(km_split, dim3(a.kpad, BH), dim3(64), 0, st, a.cent, a.cent_hi, a.cent_lo,
                            a.cnorm, D, a.k, a.kpad);
-        hipLaunchKernelGGL((km_assign<D>), dim3(ntile, BH), dim3(256), 0, st, v, a.cent_hi, a.cent_lo,
+        hipLaunchKernelGGL((km_assign<D>), dim3(ntile, BH), dim3(512), 0, st, v, a.cent_hi, a.cent_lo,
                            a.cnorm, a.assign, a.L, a.k, a.kpad);
         hipLaunchKernelGGL(km_chunk_count, dim3(a.nchunk, BH), dim3(CHUNK), a.k * sizeof(int), st,
                            a.assign, a.chunk_cnt, a.L, a.k, a.nchunk);
         hipLaunchKernelGGL(km_scan, dim3(BH), dim3(1024), 0, st, a.chunk_cnt, a.counts, a.offsets, a.k,
                            a.nchunk);
-        hipLaunchKernelGGL(km_scatter, dim3(a.nchunk, BH), dim3(CHUNK), 0, st, a.assign, a.chunk_cnt,
-                           a.perm, a.L, a.k, a.nchunk);
+        hipLaunchKernelGGL(km_scatter, dim3(a.nchunk, BH), dim3(CHUNK), a.k * sizeof(int), st, a.assign,
+                           a.chunk_cnt, a.perm, a.L, a.k, a.nchunk);
         if (a.iters > 0)
             hipLaunchKernelGGL((km_update<D>), dim3(a.k, BH), dim3(256), 0, st, v, a.perm, a.counts,
                                a.offsets, a.cent, a.L, a.k, a.kpad);
@@ -354,7 +468,7 @@ size_t kmeans_workspace_bytes(int B, int H, int L, int d, int k) {
     const size_t nchunk = ((size_t)L + CHUNK - 1) / CHUNK;
     size_t s = 0;
     s += align256(BH * kpad * d * 4);       // cent
-    s += 2 * align256(BH * kpad * d * 2);   // hi, lo
+    s += 2 * align256(BH * kpad * d * 2);   // bf16 high and low parts
     s += align256(BH * kpad * 4);           // cnorm
     s += align256(BH * L * 4);              // assign
     s += 2 * align256(BH * k * 4);          // counts, offsets

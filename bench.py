@@ -149,6 +149,8 @@ def main():
     prep_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     attn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     print("step %.3f ms (prepare %.3f, attention %.3f)" % (ms_step, prep_ms, attn_ms), file=sys.stderr, flush=True)
+    if args.v_scale_mode not in (0, 1):
+        sys.exit("--v-scale-mode must be 0 or 1")
 
     # prepare without k-means (permutation reused, as across adjacent steps)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
@@ -161,6 +163,18 @@ def main():
     E = B * H * L * d
     nb = api.nblocks(L)
     quant_bytes = 3 * E * 2 + 3 * E * 1 + B * H * nb * d * 8 + B * H * L * 4
+    # the same step's attention on V prepared with the other V-scale mode
+    P1 = api.alloc_prepared(B, H, L, d)
+    api.prepare(q, k, v, perm_in=P.perm, out=P1, ws=ws, v_scale_mode=1 - args.v_scale_mode)
+    api.attention(P1, out=out)
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for _ in range(args.steps):
+        api.attention(P1, out=out)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    other_ms = ev[0].elapsed_time(ev[1]) / args.steps
+    del P1
     bf16 = None
     if not args.no_bf16:
         ob = torch.empty((B, H, L, d), dtype=torch.float32, device="cuda")
@@ -197,6 +211,9 @@ def main():
                    "v_scale_mode": args.v_scale_mode},
         "frac_fp8_peak_step": flop / ms_step / 1e9 / FP8_PEAK_TFLOPS,
         "attention": {"ms": attn_ms, "tflops": attn_tflops, "frac_fp8_peak": attn_tflops / FP8_PEAK_TFLOPS},
+        "attention_other_v_scale_mode": {"v_scale_mode": 1 - args.v_scale_mode, "ms": other_ms,
+                                         "tflops": flop / other_ms / 1e9,
+                                         "frac_fp8_peak": flop / other_ms / 1e9 / FP8_PEAK_TFLOPS},
         "prepare": {"ms_with_kmeans": prep_ms, "ms_without_kmeans": quant_ms,
                     "quant_algorithmic_bytes": quant_bytes,
                     "quant_gbs": quant_bytes / quant_ms / 1e6},

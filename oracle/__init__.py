@@ -71,7 +71,7 @@ def lib():
             L.vco_c0.restype = f32
             L.vco_c0.argtypes = [i32]
             L.vco_attention_rows.argtypes = [i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P,
-                                             i32, i32, P, P, P, P]
+                                             i32, i32, P, P, P, P, P]
             L.vco_num_threads.restype = i32
             L.vco_prepare.argtypes = [i32, i32, i32, i32, i32, i32, u64, i32, i32, P, P, P, P,
                                       P, P, P, P, P, P, P, P, P]
@@ -239,11 +239,13 @@ def expcast_z(z, z_off: int = 8) -> np.ndarray:
 # Blockwise attention (steps a9-a14).
 # --------------------------------------------------------------------------
 
-def attention_head(prep: dict, L: int, z_off: int = 8, rows=None, want_bytes=False):
+def attention_head(prep: dict, L: int, z_off: int = 8, rows=None, want_bytes=False, scores=None):
     """Quantised VC-Attention for one head from prepare_head() output.
     rows: (r0, r1) or None for all.  Returns O [r1-r0, d] fp32 (and, with
     want_bytes, the ExpCast bytes, S values and pre-rounding y values
-    [r1-r0, Lp] of every block)."""
+    [r1-r0, Lp] of every block).  scores: optional fp32 [r1-r0, Lp] used in
+    place of the exactly rounded Q8 K8^T sums (every later step is unique
+    given the scores)."""
     q8 = _c(prep["q8"], np.uint8)
     k8 = _c(prep["k8"], np.uint8)
     v8 = _c(prep["v8"], np.uint8)
@@ -256,8 +258,12 @@ def attention_head(prep: dict, L: int, z_off: int = 8, rows=None, want_bytes=Fal
     by = np.empty((r1 - r0, Lp), np.uint8) if want_bytes else None
     S = np.empty((r1 - r0, Lp), np.float32) if want_bytes else None
     y = np.empty((r1 - r0, Lp), np.float32) if want_bytes else None
+    sin = None
+    if scores is not None:
+        sin = _c(scores, np.float32)
+        assert sin.shape == (r1 - r0, Lp)
     lib().vco_attention_rows(0, L, d, z_off, _p(q8), _p(k8), _p(v8), _p(qs), _p(ks), _p(vs),
-                             _p(vm), None, None, None, r0, r1, _p(out), _p(by), _p(S), _p(y))
+                             _p(vm), None, None, None, r0, r1, _p(out), _p(by), _p(S), _p(y), _p(sin))
     return (out, by, S, y) if want_bytes else out
 
 
@@ -281,7 +287,7 @@ def attention_exact_blockwise(qf, kf_perm, v_perm, v_mean):
         rf[b, :, :n] = (vp[b * BLK:b * BLK + n] - vm[b].astype(np.float64)).T
     out = np.empty((L, d), np.float32)
     lib().vco_attention_rows(1, L, d, 8, None, None, None, None, None, None, _p(vm),
-                             _p(qf), _p(kf), _p(rf), 0, L, _p(out), None, None, None)
+                             _p(qf), _p(kf), _p(rf), 0, L, _p(out), None, None, None, None)
     return out
 
 

@@ -426,6 +426,10 @@ float vco_c0(int d) { return (float)(1.4426950408889634074 / sqrt((double)d)); }
 /* out: [r1-r0, d] fp32.  bytes_out (may be NULL): [r1-r0, Lp] ExpCast bytes */
 /* of the final pass, for byte-level checks.  S_out and y_out (the fp32 FMA  */
 /* result before rounding) likewise (may be NULL).                           */
+/* S_in (mode 0, may be NULL): fp32 scores [r1-r0, Lp] to use in place of    */
+/* the exactly rounded sums -- the pages fix the score only as the product  */
+/* of the quantised Q and K, so any fp32 value a matrix core returns for it */
+/* is a valid score, and every later step is then unique given S.           */
 /* ------------------------------------------------------------------------ */
 
 void vco_attention_rows(int mode, int L, int d, int z_off,
@@ -434,7 +438,7 @@ void vco_attention_rows(int mode, int L, int d, int z_off,
                         const float* v_scale, const float* v_mean,
                         const double* qf, const double* kf, const double* rf,
                         int r0, int r1, float* out, uint8_t* bytes_out, float* S_out,
-                        float* y_out)
+                        float* y_out, const float* S_in)
 {
     int nb = (L + VCO_BLK - 1) / VCO_BLK;
     int64_t Lp = (int64_t)nb * VCO_BLK;
@@ -459,6 +463,11 @@ void vco_attention_rows(int mode, int L, int d, int z_off,
             double m_new, ell = 0.0;
             /* scores */
             for (int j = 0; j < n; j++) {
+                if (mode == 0 && S_in) {
+                    S[j] = S_in[(int64_t)(i - r0) * Lp + b * VCO_BLK + j];
+                    Sd[j] = S[j];
+                    continue;
+                }
                 int64_t kr = (int64_t)(b * VCO_BLK + j) * d;
                 double acc = 0.0;
                 for (int c = 0; c < d; c++)

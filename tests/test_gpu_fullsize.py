@@ -56,6 +56,32 @@ def test_full_size_sampled(api, cfg_idx):
     assert nb == P.q_scale.shape[-1]
 
 
+def test_full_size_pow2_scales(api):
+    """Wan 720p with power-of-two V scales (mode 1), in the benchmark's
+    launch configuration: sampled heads and query tiles against the oracle."""
+    cfg_idx = 2
+    cfg = synth.CONFIGS[cfg_idx]
+    B, H, L, d = cfg.B, cfg.H, cfg.L, cfg.d
+    q, k, v = synth.make_inputs(cfg, cfg_idx)
+    perm = synth.random_perms(B, H, L, 300)
+    P = api.prepare(dev_bf16(q), dev_bf16(k), dev_bf16(v), perm_in=torch.from_numpy(perm).cuda(), v_scale_mode=1)
+    out = api.attention(P)
+    torch.cuda.synchronize()
+    last_tile = ((L - 1) // 256) * 256
+    for bh in (0, B * H - 1):
+        b, h = divmod(bh, H)
+        o = oracle.prepare_head(q[b, h], k[b, h], v[b, h], perm[b, h], 1, 1)
+        assert np.array_equal(P.v_scale[b, h].cpu().numpy(), o["v_scale"])
+        for r0 in (0, last_tile):
+            r1 = min(L, r0 + 256)
+            ref = oracle.attention_head(o, L, 8, rows=(r0, r1))
+            got = out[b, h, r0:r1].cpu().numpy()
+            rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+            ma = float(np.abs(got - ref).max() / np.abs(ref).max())
+            print("pow2 bh=%d rows %d-%d: rel-L2 %.3g max-abs/max %.3g" % (bh, r0, r1, rel, ma))
+            assert rel <= 1e-3 and ma <= 1e-2
+
+
 @pytest.mark.parametrize("cfg_idx", [4, 1])
 def test_full_size_kmeans_objective(api, cfg_idx):
     cfg = synth.CONFIGS[cfg_idx]

@@ -447,3 +447,21 @@ def test_synth_bf16_rounding_matches_library():
     x[:4] = [0.0, -0.0, 1.00390625, 1.01171875]  # exact bf16 ties
     ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(synth.f32_to_bf16_bits(x), ref)
+
+
+def test_given_scores_path_reproduces_exact_path(oracle_mod):
+    """Feeding the oracle its own exactly rounded scores through the `scores`
+    input reproduces its output and bytes bit for bit (the input only replaces
+    the dot product; every later step is shared)."""
+    cfg = synth.custom(1, 1, 700, 64)
+    q, k, v = synth.make_inputs(cfg, 3)
+    perm = synth.random_perms(1, 1, 700, 3)[0, 0]
+    o = oracle_mod.prepare_head(q[0, 0], k[0, 0], v[0, 0], perm)
+    out, by, S, _ = oracle_mod.attention_head(o, 700, 8, want_bytes=True)
+    out2, by2, S2, _ = oracle_mod.attention_head(o, 700, 8, want_bytes=True, scores=S[:700].copy())
+    assert np.array_equal(out, out2) and np.array_equal(by, by2) and np.array_equal(S, S2)
+    # and a perturbed score (made the row's new maximum) changes only its row
+    S3 = S.copy()
+    S3[5, 10] = 4.0 * np.abs(S[5]).max() + 1.0
+    _, by3, _, _ = oracle_mod.attention_head(o, 700, 8, want_bytes=True, scores=S3)
+    assert not np.array_equal(by3[5], by[5]) and np.array_equal(by3[6:], by[6:])

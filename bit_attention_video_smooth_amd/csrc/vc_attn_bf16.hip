@@ -7,11 +7,16 @@
 // Same geometry as the FP8 kernel: 8 waves x 32 queries per workgroup, the
 // score tile computed transposed (S^T = K Q^T, v_mfma_f32_16x16x32_bf16) so
 // that each lane holds 32 scores of one query, and the bf16 probabilities a
-// lane produces are its B operand of O^T = V^T P^T.  K tiles stream to LDS
-// with direct 16-byte loads; V tiles are transposed through registers into a
-// [channel][key-slot] LDS layout (4 consecutive keys per 8-byte write).
+// lane produces are its B operand of O^T = V^T P^T; the row sums are a
+// product of a ones tile with those same bf16 probabilities.  K tiles and V
+// rows arrive by direct global->LDS copies one block ahead (K into a
+// double-buffered, XOR-swizzled stage; V rows into one staging buffer); after
+// the copies land, the V rows are transposed LDS->LDS into the next stage's
+// [channel][key-slot] layout between two workgroup barriers, so no copy
+// sits in registers across a block.
 #include "vc_device.hpp"
 #include "vc_internal.hpp"
+#include "vc_lds.hpp"
 
 namespace vc {
 
@@ -25,103 +30,183 @@ struct Bf16Tile {
     static constexpr int K_TILE = BLK * D * 2;  // [128 keys][D] bf16
     static constexpr int V_TILE = D * BLK * 2;  // [D][128 slots] bf16
     static constexpr int STAGE = K_TILE + V_TILE;
-    static constexpr int KCH = D / 8;           // 16-byte chunks per K row
+    static constexpr int LDS = 2 * STAGE + K_TILE;  // two stages + V-row staging
+    static constexpr int KCH = D / 8;           // 16-byte chunks per K (or V) row
     static constexpr int NU = D / 32;           // 32-wide slices of the head dim
-    static constexpr int VUNITS = (BLK / 4) * (D / 8);  // (4 keys x 8 channels) units
+    static constexpr int PIECES = K_TILE / 1024;  // 1 KiB pieces of a K tile (or of the V rows)
+    static constexpr int PPW = PIECES / NW;       // pieces of each per wave
+    static constexpr int VUNITS = (BLK / 4) * (D / 8);  // (4 keys x 8 channels) transpose units
 };
 
 __device__ __forceinline__ v4f mfma_bf16(const v8bf& a, const v8bf& b, const v4f& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ v8bf as_bf(uint4 x) {
+__device__ __forceinline__ v8bf as_bf(u32x4 x) {
     v8bf r;
     __builtin_memcpy(&r, &x, 16);
     return r;
 }
 
+// Swizzle of the 16-byte chunks of a K row: conflict-free 16-byte operand
+// reads need distinct positions modulo 128 bytes per 8 lanes and modulo 256
+// bytes per 16 lanes (rows r = 0..15 of a tile go to lanes 0..15).
+template <int D>
+__device__ __forceinline__ int kswz(int r) {
+    return D == 128 ? (r & 15) : ((r & 7) ^ ((r >> 3) & 1));
+}
+
+// V^T row (channel c, 256 bytes = 16 chunks of 8 key slots) swizzle.
 __device__ __forceinline__ int vswz(int c) { return (c ^ (c >> 3)) & 15; }
 
+// Copies of block kb: K rows into `sk` (LDS chunk p of row r holds chunk
+// p ^ kswz(r) of the key row) and V rows, unswizzled, into `stg`.  Wave w
+// takes 1 KiB pieces w, w + NW, ... of each.  Rows past L read as zeros.
 template <int D>
-__device__ __forceinline__ void issue_k_load(const AttnBf16Args& a, uint8_t* stage, int bh, int kb,
-                                             int w, int lane) {
+struct Bf16Loader {
     using T = Bf16Tile<D>;
-    const uint8_t* gK = reinterpret_cast<const uint8_t*>(a.k + ((size_t)bh * a.L) * D);
-    constexpr int NCHK = T::K_TILE / 16;
+    v4si rk, rv;
+    uint32_t koff[T::PPW], voff[T::PPW];
+    int w;
+    __device__ __forceinline__ Bf16Loader(const AttnBf16Args& a, int bh, int w_, int lane) : w(w_) {
+        const uint32_t head = (uint32_t)((size_t)a.L * D * 2);
+        rk = make_rsrc(a.k + (size_t)bh * a.L * D, head);
+        rv = make_rsrc(a.v + (size_t)bh * a.L * D, head);
 #pragma unroll
-    for (int i = 0; i < NCHK / (NW * 64); i++) {
-        const int base = (i * NW + w) * 64;
-        const int p = base + lane;
-        const int r = p / T::KCH, cp = p % T::KCH;
-        const int c = cp ^ (r & (T::KCH - 1));
-        int key = kb * BLK + r;
-        key = key < a.L ? key : a.L - 1;  // rows past L are masked in the softmax
-        __builtin_amdgcn_global_load_lds(gK + (size_t)key * D * 2 + c * 16,
-                                         (VC_LDS void*)(stage + base * 16), 16, 0, 0);
-    }
-}
-
-template <int D>
-__device__ __forceinline__ void load_v_regs(const AttnBf16Args& a, int bh, int kb, int t, uint4 (&r)[4]) {
-    using T = Bf16Tile<D>;
-    if (t < T::VUNITS) {
-        const int kg = t / (D / 8), cc = t % (D / 8);
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            int key = kb * BLK + 4 * kg + j;
-            key = key < a.L ? key : a.L - 1;
-            r[j] = *reinterpret_cast<const uint4*>(a.v + ((size_t)bh * a.L + key) * D + cc * 8);
+        for (int i = 0; i < T::PPW; i++) {
+            const int p = (i * NW + w) * 64 + lane;  // 16-byte chunk of the tile
+            const int r = p / T::KCH, cp = p % T::KCH;
+            koff[i] = (uint32_t)(r * D * 2 + ((cp ^ kswz<D>(r)) << 4));
+            voff[i] = (uint32_t)(p * 16);
         }
     }
+    __device__ __forceinline__ void issue(lds_u8* sk, lds_u8* stg, int kb) const {
+        const uint32_t base = (uint32_t)kb * T::K_TILE;
+#pragma unroll
+        for (int i = 0; i < T::PPW; i++) lds_dma16(rk, sk + (i * NW + w) * 1024, koff[i], base);
+#pragma unroll
+        for (int i = 0; i < T::PPW; i++) lds_dma16(rv, stg + (i * NW + w) * 1024, voff[i], base);
+    }
+};
+
+// V rows of one block (staging, [128 keys][D]) -> V^T tile [D][128 slots]:
+// thread t moves 4 keys x 8 channels; channel c's key slot for key k is the
+// B-operand order of the products (32-key slice u, 16-key half h, 4-key group).
+template <int D>
+__device__ __forceinline__ void transpose_v(const lds_u8* stg, lds_u8* sV, int t) {
+    using T = Bf16Tile<D>;
+    if (t >= T::VUNITS) return;
+    const int kg = t / (D / 8), cc = t % (D / 8);
+    u32x4 r[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) r[j] = *reinterpret_cast<const VC_LDS u32x4*>(stg + (4 * kg + j) * (D * 2) + cc * 16);
+    const int k0 = 4 * kg;
+    const int u = k0 / 32, h = (k0 % 32) / 16, gq = (k0 % 16) / 4;
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+        const int c = cc * 8 + e;
+        const int sh = (e & 1) * 16;
+        const uint32_t k0v = (r[0][e >> 1] >> sh) & 0xFFFFu, k1v = (r[1][e >> 1] >> sh) & 0xFFFFu;
+        const uint32_t k2v = (r[2][e >> 1] >> sh) & 0xFFFFu, k3v = (r[3][e >> 1] >> sh) & 0xFFFFu;
+        const int chunk = (4 * u + gq) ^ vswz(c);
+        const u32x2 val = {k0v | (k1v << 16), k2v | (k3v << 16)};
+        *reinterpret_cast<VC_LDS u32x2*>(sV + c * (BLK * 2) + chunk * 16 + h * 8) = val;
+    }
 }
 
-template <int D>
-__device__ __forceinline__ void store_v_lds(uint8_t* stage, int t, const uint4 (&r)[4]) {
-    using T = Bf16Tile<D>;
-    if (t < T::VUNITS) {
-        uint8_t* sV = stage + T::K_TILE;
-        const int kg = t / (D / 8), cc = t % (D / 8);
-        const int k0 = 4 * kg;
-        const int u = k0 / 32, h = (k0 % 32) / 16, gq = (k0 % 16) / 4;
-        const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&r[0]);
-        const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&r[1]);
-        const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&r[2]);
-        const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&r[3]);
+// Running max and bf16 probabilities p = 2^(S c - m') of one block for both
+// query tiles (exp2 on the transcendental unit directly: results below the
+// fp32 normal range flush to zero, which a probability next to the row
+// maximum never is).  MASKED: keys 16 kt + 4 g + i with 16 kt + i >= lim
+// do not exist.  The max is four independent max3 chains.
+template <bool MASKED>
+__device__ __forceinline__ void softmax(v4f (&S)[2][8], uint32_t (&P)[2][16], float (&alpha)[2],
+                                        float (&m)[2], int lim, float c) {
+    float mx[2];
+    if (MASKED) {
 #pragma unroll
-        for (int e = 0; e < 8; e++) {
-            const int c = cc * 8 + e;
-            const int sh = (e & 1) * 16;
-            const uint32_t k0v = (w0[e >> 1] >> sh) & 0xFFFFu, k1v = (w1[e >> 1] >> sh) & 0xFFFFu;
-            const uint32_t k2v = (w2[e >> 1] >> sh) & 0xFFFFu, k3v = (w3[e >> 1] >> sh) & 0xFFFFu;
-            const int chunk = (4 * u + gq) ^ vswz(c);
-            *reinterpret_cast<uint2*>(sV + c * (BLK * 2) + chunk * 16 + h * 8) =
-                make_uint2(k0v | (k1v << 16), k2v | (k3v << 16));
+        for (int qt = 0; qt < 2; qt++)
+#pragma unroll
+            for (int kt = 0; kt < 8; kt++)
+#pragma unroll
+                for (int i = 0; i < 4; i++)
+                    if (16 * kt + i >= lim) S[qt][kt][i] = -INFINITY;
+    }
+    float ch[2][2];
+#pragma unroll
+    for (int qt = 0; qt < 2; qt++)
+#pragma unroll
+        for (int h = 0; h < 2; h++) ch[qt][h] = vmax3(S[qt][4 * h][0], S[qt][4 * h][1], S[qt][4 * h][2]);
+#pragma unroll
+    for (int j = 0; j < 13; j += 2)
+#pragma unroll
+        for (int qt = 0; qt < 2; qt++)
+#pragma unroll
+            for (int h = 0; h < 2; h++) {
+                const int e0 = 3 + j, e1 = 4 + j;
+                const float a0 = S[qt][4 * h + e0 / 4][e0 % 4];
+                if (e1 < 16)
+                    ch[qt][h] = vmax3(ch[qt][h], a0, S[qt][4 * h + e1 / 4][e1 % 4]);
+                else
+                    ch[qt][h] = fmaxf(ch[qt][h], a0);
+            }
+#pragma unroll
+    for (int qt = 0; qt < 2; qt++) mx[qt] = fmaxf(ch[qt][0], ch[qt][1]);
+    {
+        auto px = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx[0]), __float_as_uint(mx[0]), false, false);
+        auto py = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx[1]), __float_as_uint(mx[1]), false, false);
+        mx[0] = fmaxf(__uint_as_float(px[0]), __uint_as_float(px[1]));
+        mx[1] = fmaxf(__uint_as_float(py[0]), __uint_as_float(py[1]));
+        auto qx = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx[0]), __float_as_uint(mx[0]), false, false);
+        auto qy = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx[1]), __float_as_uint(mx[1]), false, false);
+        mx[0] = fmaxf(__uint_as_float(qx[0]), __uint_as_float(qx[1]));
+        mx[1] = fmaxf(__uint_as_float(qy[0]), __uint_as_float(qy[1]));
+    }
+#pragma unroll
+    for (int qt = 0; qt < 2; qt++) {
+        const float mn = fmaxf(m[qt], mx[qt] * c);
+        alpha[qt] = __builtin_amdgcn_exp2f(m[qt] - mn);  // 0 on the first block
+        m[qt] = mn;
+#pragma unroll
+        for (int kt = 0; kt < 8; kt++) {
+            float p[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[qt][kt][i], c, -mn));
+            P[qt][2 * kt] = pack_bf16x2(p[0], p[1]);
+            P[qt][2 * kt + 1] = pack_bf16x2(p[2], p[3]);
         }
     }
 }
 
 template <int D, bool OUT_BF16>
-__global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnBf16Args a) {
+__global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnBf16Args a) {
     using T = Bf16Tile<D>;
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_[T::LDS];
+    lds_u8* lds = (lds_u8*)lds_;
+    lds_u8* stg = lds + 2 * T::STAGE;
     const int nwg = a.BH * a.nqt;
     const int pid = xcd_remap(blockIdx.x, nwg);
     const int bh = pid / a.nqt, qtile = pid % a.nqt;
-    const int t = threadIdx.x, w = t >> 6, lane = t & 63, col = lane & 15, g = lane >> 4;
+    const int t = threadIdx.x, lane = t & 63, col = lane & 15, g = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);
     const int q0 = qtile * ATTN_BM + w * QW;
     const int L = a.L, nkb = a.nkb;
 
+    // Q operands (B operand of S^T = K Q^T): lane (col, g) holds elements
+    // [32 u + 8 g, 32 u + 8 g + 8) of query q0 + 16 qt + col
     v8bf qop[2][T::NU];
 #pragma unroll
     for (int qt = 0; qt < 2; qt++) {
         const int row = q0 + 16 * qt + col;
 #pragma unroll
         for (int u = 0; u < T::NU; u++) {
-            uint4 x = make_uint4(0, 0, 0, 0);
-            if (row < L) x = *reinterpret_cast<const uint4*>(a.q + ((size_t)bh * L + row) * D + 32 * u + 8 * g);
+            u32x4 x = {0, 0, 0, 0};
+            if (row < L) x = *reinterpret_cast<const u32x4*>(a.q + ((size_t)bh * L + row) * D + 32 * u + 8 * g);
             qop[qt][u] = as_bf(x);
         }
     }
+    __builtin_amdgcn_s_waitcnt(0);
     const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
     constexpr int NCT = D / 16;
     v4f O[2][NCT];
@@ -131,34 +216,30 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnBf16Args a) {
         for (int ct = 0; ct < NCT; ct++) O[qt][ct] = zero4;
     float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
     const float c = a.C0;
+    const Bf16Loader<D> ld(a, bh, w, lane);
 
-    uint4 vr[4];
-    issue_k_load<D>(a, smem, bh, 0, w, lane);
-    load_v_regs<D>(a, bh, 0, t, vr);
-    store_v_lds<D>(smem, t, vr);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    ld.issue(lds, stg, 0);
+    wait_vmcnt<0>();
+    block_barrier();
+    transpose_v<D>(stg, lds + T::K_TILE, t);
+    block_barrier();
 
     for (int kb = 0; kb < nkb; kb++) {
-        uint8_t* stage = smem + (kb & 1) * T::STAGE;
-        uint8_t* next = smem + ((kb + 1) & 1) * T::STAGE;
+        const lds_u8* sK = lds + (kb & 1) * T::STAGE;
+        const lds_u8* sV = sK + T::K_TILE;
+        lds_u8* nxt = lds + ((kb + 1) & 1) * T::STAGE;
         const bool more = kb + 1 < nkb;
-        if (more) {
-            issue_k_load<D>(a, next, bh, kb + 1, w, lane);
-            load_v_regs<D>(a, bh, kb + 1, t, vr);
-        }
-        const uint8_t* sK = stage;
-        const uint8_t* sV = stage + T::K_TILE;
+        if (more) ld.issue(nxt, stg, kb + 1);  // both freed before the last barrier
 
         v4f S[2][8];
 #pragma unroll
         for (int kt = 0; kt < 8; kt++) {
             const int r = 16 * kt + col;
-            const uint8_t* row = sK + r * (D * 2);
+            const lds_u8* row = sK + r * (D * 2);
             v8bf kop[T::NU];
 #pragma unroll
             for (int u = 0; u < T::NU; u++)
-                kop[u] = as_bf(*reinterpret_cast<const uint4*>(row + (((4 * u + g) ^ (r & (T::KCH - 1))) << 4)));
+                kop[u] = as_bf(*reinterpret_cast<const VC_LDS u32x4*>(row + (((4 * u + g) ^ kswz<D>(r)) << 4)));
 #pragma unroll
             for (int qt = 0; qt < 2; qt++) {
                 v4f acc = zero4;
@@ -167,76 +248,78 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnBf16Args a) {
                 S[qt][kt] = acc;
             }
         }
+        // K operand reads one key tile ahead of the products
+        __builtin_amdgcn_sched_group_barrier(0x100, T::NU, 0);
+#pragma unroll
+        for (int kt = 0; kt < 8; kt++) {
+            if (kt + 1 < 8) __builtin_amdgcn_sched_group_barrier(0x100, T::NU, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2 * T::NU, 0);
+        }
 
         const int nvalid = L - kb * BLK;
-        const bool partial = nvalid < BLK;
         float alpha[2];
         uint32_t P[2][16];
+        if (nvalid < BLK)
+            softmax<true>(S, P, alpha, m, nvalid - 4 * g, c);
+        else
+            softmax<false>(S, P, alpha, m, 0, c);
+        // rescale a query tile only when one of its rows raised its max
 #pragma unroll
-        for (int qt = 0; qt < 2; qt++) {
-            if (partial) {
-#pragma unroll
-                for (int kt = 0; kt < 8; kt++)
-#pragma unroll
-                    for (int i = 0; i < 4; i++)
-                        if (16 * kt + 4 * g + i >= nvalid) S[qt][kt][i] = -INFINITY;
-            }
-            float mx = -INFINITY;
-#pragma unroll
-            for (int kt = 0; kt < 8; kt++)
-                mx = fmaxf(mx, fmaxf(fmaxf(S[qt][kt][0], S[qt][kt][1]), fmaxf(S[qt][kt][2], S[qt][kt][3])));
-            mx = max_over_groups(mx);
-            const float mn = fmaxf(m[qt], mx * c);
-            alpha[qt] = exp2f(m[qt] - mn);
-            m[qt] = mn;
-            float rs = 0.f;
-#pragma unroll
-            for (int kt = 0; kt < 8; kt++) {
-                float p[4];
-#pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    p[i] = exp2f(__builtin_fmaf(S[qt][kt][i], c, -mn));
-                    rs += p[i];
-                }
-                P[qt][2 * kt] = pack_bf16x2(p[0], p[1]);
-                P[qt][2 * kt + 1] = pack_bf16x2(p[2], p[3]);
-            }
-            // sum over the four lane groups of this query
-            auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(rs), __float_as_uint(rs), false, false);
-            rs = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
-            auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(rs), __float_as_uint(rs), false, false);
-            rs = __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
-            l[qt] = __builtin_fmaf(alpha[qt], l[qt], rs);
-        }
-        if (__any((alpha[0] != 1.0f) | (alpha[1] != 1.0f))) {
-#pragma unroll
-            for (int qt = 0; qt < 2; qt++)
+        for (int qt = 0; qt < 2; qt++)
+            if (__any(alpha[qt] != 1.0f)) {
 #pragma unroll
                 for (int ct = 0; ct < NCT; ct++) O[qt][ct] *= alpha[qt];
-        }
+            }
         // P^T operand of slice u: keys 32u + 16 (j/4) + 4 g + j%4
         v8bf pop[2][4];
 #pragma unroll
         for (int qt = 0; qt < 2; qt++)
 #pragma unroll
             for (int u = 0; u < 4; u++) {
-                uint4 x = make_uint4(P[qt][4 * u], P[qt][4 * u + 1], P[qt][4 * u + 2], P[qt][4 * u + 3]);
+                const u32x4 x = {P[qt][4 * u], P[qt][4 * u + 1], P[qt][4 * u + 2], P[qt][4 * u + 3]};
                 pop[qt][u] = as_bf(x);
             }
+        // row sums of the bf16 probabilities the products use: ones(16x32) P^T
+        // per 32-key slice, on the matrix cores
+        {
+            v8bf ones;
+#pragma unroll
+            for (int i = 0; i < 8; i++) ones[i] = (__bf16)1.0f;
+#pragma unroll
+            for (int qt = 0; qt < 2; qt++) {
+                v4f rs = zero4;
+#pragma unroll
+                for (int u = 0; u < 4; u++) rs = mfma_bf16(ones, pop[qt][u], rs);
+                l[qt] = __builtin_fmaf(alpha[qt], l[qt], rs[0]);
+            }
+        }
 #pragma unroll
         for (int ct = 0; ct < NCT; ct++) {
             const int cr = 16 * ct + col;
-            const uint8_t* row = sV + cr * (BLK * 2);
+            const lds_u8* row = sV + cr * (BLK * 2);
 #pragma unroll
             for (int u = 0; u < 4; u++) {
-                const v8bf vop = as_bf(*reinterpret_cast<const uint4*>(row + (((4 * u + g) ^ vswz(cr)) << 4)));
+                const v8bf vop = as_bf(*reinterpret_cast<const VC_LDS u32x4*>(row + (((4 * u + g) ^ vswz(cr)) << 4)));
 #pragma unroll
                 for (int qt = 0; qt < 2; qt++) O[qt][ct] = mfma_bf16(vop, pop[qt][u], O[qt][ct]);
             }
         }
-        if (more) store_v_lds<D>(next, t, vr);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        // V operand reads one channel tile ahead of the products
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);  // row sums
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ct++) {
+            if (ct + 1 < NCT) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        }
+        if (more) {
+            // block kb + 1 has landed (K in its stage, V rows in the staging
+            // buffer); transpose the V rows into its stage
+            wait_vmcnt<0>();
+            block_barrier();
+            transpose_v<D>(stg, nxt + T::K_TILE, t);
+            block_barrier();
+        }
     }
 
 #pragma unroll
@@ -264,16 +347,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(AttnBf16Args a) {
 
 template <int D, bool OB>
 hipError_t launch_t(const AttnBf16Args& a, hipStream_t st) {
-    const int smem = 2 * Bf16Tile<D>::STAGE;
-    auto kern = attn_bf16_kernel<D, OB>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, smem);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
-    hipLaunchKernelGGL(kern, dim3(a.BH * a.nqt), dim3(NW * 64), smem, st, a);
+    hipLaunchKernelGGL((attn_bf16_kernel<D, OB>), dim3(a.BH * a.nqt), dim3(NW * 64), 0, st, a);
     return hipGetLastError();
 }
 

@@ -35,6 +35,7 @@
 //    one XCD and share its L2.
 #include "vc_device.hpp"
 #include "vc_internal.hpp"
+#include "vc_lds.hpp"
 
 namespace vc {
 
@@ -59,14 +60,6 @@ struct Fp8Tile {
     static constexpr int NCT = D / 16;          // 16-channel output tiles
 };
 
-// End of a block: this wave's LDS reads are complete, then all waves meet.
-// The scheduling fences keep every instruction on its side of the barrier.
-__device__ __forceinline__ void block_barrier() {
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-}
-
 // XOR swizzle of the 16-byte chunks of LDS tile rows.  A 16-byte-per-lane
 // LDS read moves 256 bytes per clock; it runs at that rate only when every
 // group of 8 consecutive lanes touches 8 distinct 16-byte positions modulo
@@ -83,9 +76,6 @@ __host__ __device__ constexpr int chunk_swizzle(int r, int nch) {
 // A/B operand of one 16-row tile: row `r` of a tile with `pitch`-byte rows of
 // `nch` 16-byte chunks (swizzled as above); lane group g takes bytes
 // [32 g, 32 g + 32) of the logical row.
-typedef VC_LDS uint8_t lds_u8;
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ v8i lds_operand(const lds_u8* tile, int r, int pitch, int nch, int g) {
     const int sw = chunk_swizzle(r, nch);
@@ -100,14 +90,6 @@ __device__ __forceinline__ v8i lds_operand(const lds_u8* tile, int r, int pitch,
 
 __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
-}
-
-// max(a, b, c) in one instruction; written out so that the compiler keeps
-// the chains it is given instead of re-associating them into a tree.
-__device__ __forceinline__ float vmax3(float a, float b, float c) {
-    float r;
-    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-    return r;
 }
 
 // Row max of two query tiles over the four lane groups, the two reductions
@@ -162,52 +144,6 @@ __device__ __forceinline__ uint32_t dma_offset(int w, int lane, int row_bytes) {
     return (uint32_t)(r * row_bytes + ((cp ^ chunk_swizzle(r, cpr)) << 4));
 }
 
-typedef int v4si __attribute__((ext_vector_type(4)));
-
-// Buffer descriptor of `bytes` bytes at `base` (gfx9: raw 32-bit data, no
-// stride); reads past the end return zeros.  All fields are wave-uniform.
-__device__ __forceinline__ v4si make_rsrc(const void* base, uint32_t bytes) {
-    const uint64_t p = reinterpret_cast<uint64_t>(base);
-    v4si r;
-    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)p);
-    r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32));
-    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
-    r[3] = 0x00020000;
-    return r;
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const lds_u8* p) {
-    return (uint32_t)reinterpret_cast<uintptr_t>(p);
-}
-
-// Direct global->LDS copies.  Written as inline assembly so that the
-// compiler neither waits on them nor counts them: every wait on these copies
-// is explicit (wait_vmcnt) and every LDS hand-over goes through a barrier.
-// They have no register outputs; M0 (the wave's LDS base) is set in the same
-// block, one wait state before the load.
-__device__ __forceinline__ void lds_dma16(const v4si& r, const lds_u8* lds_wave_base, uint32_t voff,
-                                          uint32_t soff) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 :: "s"(__builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base))), "v"(voff), "s"(r),
-                    "s"(__builtin_amdgcn_readfirstlane(soff))
-                 : "memory", "m0");
-}
-
-__device__ __forceinline__ void lds_dma4(const v4si& r, const lds_u8* lds_wave_base, uint32_t voff,
-                                         uint32_t soff) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
-                 :: "s"(__builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base))), "v"(voff), "s"(r),
-                    "s"(__builtin_amdgcn_readfirstlane(soff))
-                 : "memory", "m0");
-}
-
-__device__ __forceinline__ void lds_dma16_flat(const void* g, const lds_u8* lds_wave_base) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-                 :: "s"(__builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base))),
-                    "v"(reinterpret_cast<uint64_t>(g))
-                 : "memory", "m0");
-}
-
 // Group-0 waves (w < 4, 256 threads) copy block kb into `stage`: their
 // share of the K8 and V8 tiles, plus (each wave, into its own slot) the
 // block's per-channel scales and means and the K scales from block kb on.
@@ -246,14 +182,6 @@ struct Fp8Loader {
         lds_dma4(rks, stage + T::KS_OFF + w * 256, lane * 4, kb * 4);
     }
 };
-
-// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
-// 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 template <int D, bool DUMP>
 struct Fp8Wave {

@@ -20,17 +20,18 @@
 //    B operand (written so by the preprocessing kernel);
 //  * the row sum of the ExpCast bytes is one more FP8 product (a row of
 //    ones times P^T), exact, off the vector ALU;
-//  * K8/V8 tiles stream into a three-stage LDS ring with direct-to-LDS
+//  * K8/V8 tiles stream into a four-stage LDS ring with direct-to-LDS
 //    16-byte loads (XOR-swizzled 16-byte chunks) two blocks ahead; each
 //    stage is its own LDS object so the compiler's wait insertion can tell
 //    a stage being filled from the stage being read;
 //  * a wave issues a vector instruction at most every ~5 cycles (~10 when
 //    it depends on the one before), so the vector work is written as
-//    independent chains, and the two waves that share a SIMD run in phase
-//    so that both feed its vector ALU; one workgroup barrier per block
-//    keeps the LDS ring consistent, and the waves are free to drift apart
-//    within a block so that one's matrix products overlap the other's
-//    vector work;
+//    independent chains; while one wave streams matrix products, the other
+//    wave on its SIMD still issues about four vector instructions per
+//    product, so the two wave groups run offset by most of a block (one
+//    workgroup barrier per block, passed at different points of the block
+//    by the two groups) and one group's S^T products meet the other's
+//    softmax;
 //  * workgroups are remapped so that the query tiles of one head run on
 //    one XCD and share its L2.
 #include "vc_device.hpp"
@@ -198,6 +199,7 @@ struct Fp8Wave {
     v4f S[2][8];
     uint32_t P[2][8];
     float alpha[2];
+    float krow[2], cb;
 
     __device__ __forceinline__ Fp8Wave(const AttnArgs& args, int bh_, int qtile, int w_, int lane_)
         : a(args), bh(bh_), w(w_), lane(lane_) {
@@ -270,8 +272,7 @@ struct Fp8Wave {
     // block (keys past L) has its own copy so that no masking work leaks into
     // the full blocks.
     template <bool MASKED>
-    __device__ __forceinline__ void softmax_rows(int kb, float cb, int lim) {
-        const float c8 = 8.0f * cb;
+    __device__ __forceinline__ void softmax_max(float cb, int lim) {
         float mx[2];
         if (!MASKED) {
             float ch[2][2];
@@ -308,7 +309,6 @@ struct Fp8Wave {
             }
         }
         max_over_groups2(mx[0], mx[1]);
-        float krow[2];
 #pragma unroll
         for (int qt = 0; qt < 2; qt++) {
             const float t = __fmul_rn(mx[qt], cb);
@@ -317,6 +317,10 @@ struct Fp8Wave {
             alpha[qt] = __builtin_amdgcn_exp2f(m[qt] - mn);  // 2^(m - m'), 0 on the first block
             m[qt] = mn;
         }
+    }
+
+    template <bool MASKED>
+    __device__ __forceinline__ void softmax_bytes(int kb, float c8, int lim) {
 #pragma unroll
         for (int qt = 0; qt < 2; qt++) {
             if (!MASKED) {
@@ -358,12 +362,15 @@ struct Fp8Wave {
 
     __device__ __forceinline__ void slot_softmax(int kb, const lds_u8* st) {
         const float ks = *reinterpret_cast<const VC_LDS float*>(st + T::KS_OFF);
-        const float cb = __fmul_rn(__fmul_rn(sq, ks), a.C0);
+        cb = __fmul_rn(__fmul_rn(sq, ks), a.C0);
         const int nvalid = L - kb * BLK;  // keys of this block that exist (>= 1)
-        if (nvalid < BLK)
-            softmax_rows<true>(kb, cb, nvalid - 4 * g);
-        else
-            softmax_rows<false>(kb, cb, 0);
+        if (nvalid < BLK) {
+            softmax_max<true>(cb, nvalid - 4 * g);
+            softmax_bytes<true>(kb, 8.0f * cb, nvalid - 4 * g);
+        } else {
+            softmax_max<false>(cb, 0);
+            softmax_bytes<false>(kb, 8.0f * cb, 0);
+        }
     }
 
     // Row sums (ones(16x128) * P^T, exact), V8^T P^T on the matrix
@@ -414,17 +421,26 @@ struct Fp8Wave {
     }
 
     // Block kb (stage `cur`): S^T on the matrix cores, softmax bytes on the
-    // vector ALU, then P V and the epilogue.  The loading group (LOADER)
+    // vector ALU, then P V and the epilogue.  The loading group (waves 0-3)
     // starts the copy of block kb + 2 into stage `ahead` (the stage of block
-    // kb - 1, which every wave left before the previous barrier) --
-    // unconditionally: past the end it re-copies the last block into a stage
-    // nobody reads again, so the copy count per block is fixed -- and at the
-    // end waits for its share of block kb + 1; the one barrier per block then
-    // publishes block kb + 1 to all waves and frees stage `cur`.
-    template <bool LOADER>
+    // kb - 2) -- unconditionally: past the end it re-copies the last block
+    // into a stage nobody reads again, so the copy count per block is fixed --
+    // and at the end waits for its share of block kb + 1.
+    //
+    // Every wave passes one workgroup barrier per block; barrier n publishes
+    // block n.  The loading group passes it at the end of its block, the
+    // other group (LAG) right after its products S^T: that group thus runs
+    // most of a block behind, its softmax (vector ALU) meets the loading
+    // group's S^T products (matrix cores) on the shared SIMDs, and the two
+    // groups never sit in the same phase.  The lagging group still reads
+    // block kb (softmax, P V) until it reaches barrier kb + 2, so the ring
+    // has four stages: block kb + 2 is copied, after barrier kb, into the
+    // stage of block kb - 2, which both groups left before that barrier.
+    template <bool LOADER, bool LAG>
     __device__ __forceinline__ void block(const Fp8Loader<D>& ld, int kb, const lds_u8* cur,
                                           lds_u8* ahead) {
         slot_qk(cur);
+        if (LAG) block_barrier();
         if (LOADER) ld.issue(ahead, min(kb + 2, nb - 1));
         slot_softmax(kb, cur);
         // rescale a query tile only when one of its rows raised its max
@@ -441,15 +457,16 @@ struct Fp8Wave {
             else
                 wait_vmcnt<Fp8Loader<D>::NLD>();
         }
-        block_barrier();
+        if (!LAG) block_barrier();
     }
 
-    template <bool LOADER>
-    __device__ __forceinline__ void run(const Fp8Loader<D>& ld, lds_u8* st0, lds_u8* st1, lds_u8* st2) {
-        for (int kb = 0; kb < nb; kb += 3) {
-            block<LOADER>(ld, kb, st0, st2);
-            if (kb + 1 < nb) block<LOADER>(ld, kb + 1, st1, st0);
-            if (kb + 2 < nb) block<LOADER>(ld, kb + 2, st2, st1);
+    template <bool LOADER, bool LAG>
+    __device__ __forceinline__ void run(const Fp8Loader<D>& ld, lds_u8* const (&st)[4]) {
+        for (int kb = 0; kb < nb; kb += 4) {
+            block<LOADER, LAG>(ld, kb, st[0], st[2]);
+            if (kb + 1 < nb) block<LOADER, LAG>(ld, kb + 1, st[1], st[3]);
+            if (kb + 2 < nb) block<LOADER, LAG>(ld, kb + 2, st[2], st[0]);
+            if (kb + 3 < nb) block<LOADER, LAG>(ld, kb + 3, st[3], st[1]);
         }
     }
 };
@@ -460,9 +477,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fp8_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t st0_[T::STAGE];
     __shared__ __attribute__((aligned(16))) uint8_t st1_[T::STAGE];
     __shared__ __attribute__((aligned(16))) uint8_t st2_[T::STAGE];
-    lds_u8* st0 = (lds_u8*)st0_;
-    lds_u8* st1 = (lds_u8*)st1_;
-    lds_u8* st2 = (lds_u8*)st2_;
+    __shared__ __attribute__((aligned(16))) uint8_t st3_[T::STAGE];
+    lds_u8* const st[4] = {(lds_u8*)st0_, (lds_u8*)st1_, (lds_u8*)st2_, (lds_u8*)st3_};
     const int nwg = a.BH * a.nqt;
     const int pid = xcd_remap(blockIdx.x, nwg);
     const int bh = pid / a.nqt, qtile = pid % a.nqt;
@@ -473,19 +489,19 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fp8_kernel(AttnArgs a) {
     const int nb = a.nb;
 
     // Blocks 0 and 1 are in flight before the loop; block 0 is published by
-    // the first barrier, and every wave then passes one barrier per block.
-    // The loading waves drain their copies past the end before they exit.
+    // the first barrier.  The loading waves drain their copies past the end
+    // before they exit.
     if (s.grp == 0) {
-        ld.issue(st0, 0);
-        ld.issue(st1, min(1, nb - 1));
+        ld.issue(st[0], 0);
+        ld.issue(st[1], min(1, nb - 1));
         wait_vmcnt<Fp8Loader<D>::NLD>();
     }
     block_barrier();
     if (s.grp == 0) {
-        s.template run<true>(ld, st0, st1, st2);
+        s.template run<true, false>(ld, st);
         wait_vmcnt<0>();
     } else {
-        s.template run<false>(ld, st0, st1, st2);
+        s.template run<false, true>(ld, st);
     }
 
     // O / l, original row order; lane (col, g) holds channels 16 ct + 4 g + i

@@ -47,6 +47,7 @@ def parse():
 # summary records their hash and is ignored once any of them changes.
 KERNEL_SOURCES = ["bit_attention_video_smooth_amd/csrc/vc_attn_fp8.hip",
                   "bit_attention_video_smooth_amd/csrc/vc_device.hpp",
+                  "bit_attention_video_smooth_amd/csrc/vc_lds.hpp",
                   "bit_attention_video_smooth_amd/csrc/vc_internal.hpp",
                   "bit_attention_video_smooth_amd/build.py"]
 TRAFFIC_SUMMARY = "profiles/attn_fp8_wan720p_hbm_traffic.txt"

@@ -71,7 +71,7 @@ def lib():
             L.vco_c0.restype = f32
             L.vco_c0.argtypes = [i32]
             L.vco_attention_rows.argtypes = [i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P,
-                                             i32, i32, P, P, P, P, P]
+                                             i32, i32, P, P, P, P, P, f32]
             L.vco_num_threads.restype = i32
             L.vco_prepare.argtypes = [i32, i32, i32, i32, i32, i32, u64, i32, i32, P, P, P, P,
                                       P, P, P, P, P, P, P, P, P]
@@ -239,13 +239,24 @@ def expcast_z(z, z_off: int = 8) -> np.ndarray:
 # Blockwise attention (steps a9-a14).
 # --------------------------------------------------------------------------
 
-def attention_head(prep: dict, L: int, z_off: int = 8, rows=None, want_bytes=False, scores=None):
+def skip_threshold(skip_lambda: float) -> np.float32:
+    """fp32(log2(lambda)) in double rounded once; -inf (reject nothing) for
+    lambda = 0.  The pages' rule exp(m~ - m) < lambda ([TRT] "Sparse
+    Attention with Skip Softmax") is then fp32(t - m) < this, in log2 units."""
+    lam = float(skip_lambda)
+    if not (0.0 <= lam <= 1.0):
+        raise ValueError("skip_lambda must lie in [0, 1]")
+    return np.float32(-np.inf) if lam == 0.0 else np.float32(np.log2(np.float64(lam)))
+
+
+def attention_head(prep: dict, L: int, z_off: int = 8, rows=None, want_bytes=False, scores=None,
+                   skip_lambda: float = 0.0):
     """Quantised VC-Attention for one head from prepare_head() output.
     rows: (r0, r1) or None for all.  Returns O [r1-r0, d] fp32 (and, with
     want_bytes, the ExpCast bytes, S values and pre-rounding y values
     [r1-r0, Lp] of every block).  scores: optional fp32 [r1-r0, Lp] used in
     place of the exactly rounded Q8 K8^T sums (every later step is unique
-    given the scores)."""
+    given the scores).  skip_lambda: the Skip Softmax threshold (0: off)."""
     q8 = _c(prep["q8"], np.uint8)
     k8 = _c(prep["k8"], np.uint8)
     v8 = _c(prep["v8"], np.uint8)
@@ -263,15 +274,17 @@ def attention_head(prep: dict, L: int, z_off: int = 8, rows=None, want_bytes=Fal
         sin = _c(scores, np.float32)
         assert sin.shape == (r1 - r0, Lp)
     lib().vco_attention_rows(0, L, d, z_off, _p(q8), _p(k8), _p(v8), _p(qs), _p(ks), _p(vs),
-                             _p(vm), None, None, None, r0, r1, _p(out), _p(by), _p(S), _p(y), _p(sin))
+                             _p(vm), None, None, None, r0, r1, _p(out), _p(by), _p(S), _p(y), _p(sin),
+                             skip_threshold(skip_lambda))
     return (out, by, S, y) if want_bytes else out
 
 
-def attention_exact_blockwise(qf, kf_perm, v_perm, v_mean):
+def attention_exact_blockwise(qf, kf_perm, v_perm, v_mean, skip_lambda: float = 0.0):
     """Mode 1 of the blockwise loop: no quantisation, exact exp2, in double.
     qf [L,d], kf_perm [L,d] keys in permuted order, v_perm [L,d] values in
     permuted order, v_mean [nb,d] any per-block vector (the algebra must hold
-    for any mean).  Returns O [L,d] (fp32)."""
+    for any mean).  skip_lambda as in attention_head.  Returns O [L,d]
+    (fp32)."""
     qf = _c(qf, np.float64)
     L, d = qf.shape
     nb = nblocks(L)
@@ -287,7 +300,8 @@ def attention_exact_blockwise(qf, kf_perm, v_perm, v_mean):
         rf[b, :, :n] = (vp[b * BLK:b * BLK + n] - vm[b].astype(np.float64)).T
     out = np.empty((L, d), np.float32)
     lib().vco_attention_rows(1, L, d, 8, None, None, None, None, None, None, _p(vm),
-                             _p(qf), _p(kf), _p(rf), 0, L, _p(out), None, None, None, None)
+                             _p(qf), _p(kf), _p(rf), 0, L, _p(out), None, None, None, None,
+                             skip_threshold(skip_lambda))
     return out
 
 

@@ -430,6 +430,14 @@ float vco_c0(int d) { return (float)(1.4426950408889634074 / sqrt((double)d)); }
 /* the exactly rounded sums -- the pages fix the score only as the product  */
 /* of the quantised Q and K, so any fp32 value a matrix core returns for it */
 /* is a valid score, and every later step is then unique given S.           */
+/*                                                                          */
+/* Skip Softmax ([TRT] "Sparse Attention with Skip Softmax"): row i rejects */
+/* block b when exp(mtilde - m) < lambda, mtilde the block's maximum score  */
+/* and m the running maximum, both in natural-log units.  In the log2 units */
+/* used here that is 2^(t - m) < lambda, tested as fp32(t - m) < skip_thr   */
+/* with skip_thr = fp32(log2(lambda)) (-infinity: nothing is rejected).     */
+/* A rejected block leaves m, l and O as they are and its bytes are 0; it   */
+/* never moves the running maximum, since t < m there.                      */
 /* ------------------------------------------------------------------------ */
 
 void vco_attention_rows(int mode, int L, int d, int z_off,
@@ -438,7 +446,7 @@ void vco_attention_rows(int mode, int L, int d, int z_off,
                         const float* v_scale, const float* v_mean,
                         const double* qf, const double* kf, const double* rf,
                         int r0, int r1, float* out, uint8_t* bytes_out, float* S_out,
-                        float* y_out, const float* S_in)
+                        float* y_out, const float* S_in, float skip_thr)
 {
     int nb = (L + VCO_BLK - 1) / VCO_BLK;
     int64_t Lp = (int64_t)nb * VCO_BLK;
@@ -481,6 +489,16 @@ void vco_attention_rows(int mode, int L, int d, int z_off,
                 float mx = -INFINITY;
                 for (int j = 0; j < n; j++) if (S[j] > mx) mx = S[j];
                 volatile float t = mx * cb;
+                volatile float gap = t - (float)m; /* +inf on the first block */
+                if (gap < skip_thr) {
+                    for (int j = 0; j < VCO_BLK; j++) {
+                        int64_t o = (int64_t)(i - r0) * Lp + b * VCO_BLK + j;
+                        if (bytes_out) bytes_out[o] = 0;
+                        if (S_out) S_out[o] = (j < n) ? S[j] : 0.0f;
+                        if (y_out) y_out[o] = -INFINITY;
+                    }
+                    continue;
+                }
                 float mnf = ((float)m > t) ? (float)m : t;
                 if (m == -INFINITY) mnf = t;
                 m_new = mnf;
@@ -500,6 +518,7 @@ void vco_attention_rows(int mode, int L, int d, int z_off,
             } else {
                 double mx = -INFINITY;
                 for (int j = 0; j < n; j++) if (Sd[j] * C0d > mx) mx = Sd[j] * C0d;
+                if (mx - m < (double)skip_thr) continue;
                 m_new = (m > mx) ? m : mx;
                 for (int j = 0; j < n; j++) { p[j] = exp2(Sd[j] * C0d - m_new); ell += p[j]; }
             }

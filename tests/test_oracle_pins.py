@@ -465,3 +465,94 @@ def test_given_scores_path_reproduces_exact_path(oracle_mod):
     S3[5, 10] = 4.0 * np.abs(S[5]).max() + 1.0
     _, by3, _, _ = oracle_mod.attention_head(o, 700, 8, want_bytes=True, scores=S3)
     assert not np.array_equal(by3[5], by[5]) and np.array_equal(by3[6:], by[6:])
+
+
+# ---------------------------------------------------- Skip Softmax (BLASST) --
+# [TRT] "Sparse Attention with Skip Softmax": for query row i and KV block j
+# the block is negligible when exp(m~ - m) < lambda (m~ the block's maximum
+# score, m the running maximum); rejected blocks skip the exponentials and
+# their PV accumulation.
+
+def _skip_brute(qf, kf_perm, v_perm, lam):
+    """fp64 softmax attention over the kept blocks only, with the rejection
+    rule evaluated as printed, in natural-log units, blocks in ascending
+    order.  Returns (O, kept [L, nb])."""
+    L, d = qf.shape
+    nb = (L + 127) // 128
+    s = qf @ kf_perm.T / math.sqrt(d)
+    kept = np.zeros((L, nb), bool)
+    out = np.empty((L, d))
+    for i in range(L):
+        m = -np.inf
+        for b in range(nb):
+            mt = s[i, 128 * b:128 * b + 128].max()
+            if m > -np.inf and math.exp(mt - m) < lam:
+                continue
+            kept[i, b] = True
+            m = max(m, mt)
+        cols = np.concatenate([np.arange(128 * b, min(L, 128 * b + 128)) for b in np.nonzero(kept[i])[0]])
+        w = np.exp(s[i, cols] - s[i, cols].max())
+        out[i] = w @ v_perm[cols] / w.sum()
+    return out, kept
+
+
+@pytest.mark.parametrize("lam", [0.05, 0.3])
+def test_skip_softmax_exact_blockwise_matches_brute_force(oracle_mod, lam):
+    """Quantisation off: the blockwise loop with Skip Softmax equals softmax
+    attention restricted to the blocks the printed rule keeps."""
+    rng = np.random.default_rng(17)
+    L, d = 900, 64
+    qf = rng.normal(size=(L, d))
+    # keys whose blocks differ in score scale, so that some are rejected
+    kf = rng.normal(size=(L, d)) * np.repeat(rng.uniform(0.2, 1.6, (L + 127) // 128), 128)[:L, None]
+    vf = rng.normal(size=(L, d)) * 2
+    nb = (L + 127) // 128
+    means = rng.normal(0, 1, (nb, d)).astype(np.float32)
+    lam_eff = 2.0 ** float(oracle_mod.skip_threshold(lam))  # the fp32 threshold the loop uses
+    ref, kept = _skip_brute(qf, kf, vf, lam_eff)
+    frac = 1 - kept.mean()
+    assert 0.05 < frac < 0.95, frac
+    got = oracle_mod.attention_exact_blockwise(qf, kf, vf, means, skip_lambda=lam)
+    assert np.abs(got - ref).max() <= 4e-7 * np.abs(ref).max()
+    # and lambda = 0 keeps every block
+    full = oracle_mod.attention_exact_blockwise(qf, kf, vf, means)
+    assert np.abs(full - oracle_mod.attention_f64(qf, kf, vf)).max() <= 4e-7 * np.abs(full).max()
+
+
+def test_skip_softmax_quantised_rejects_by_the_printed_rule(oracle_mod):
+    """Quantised path: the rejected (row, block) pairs are those where
+    exp(m~ - m) < lambda with m~ and m from the same scores in natural-log
+    units; a rejected block gets bytes 0, and every kept block keeps exactly
+    the bytes of the run without rejection (a rejected block never moves the
+    running maximum).  lambda = 0 changes nothing."""
+    cfg = synth.custom(1, 1, 1000, 64)
+    q, k, v = synth.make_inputs(cfg, 21)
+    q, k, v = q[0, 0], k[0, 0], v[0, 0]
+    # stretch the keys of some blocks so that their scores fall behind
+    kf = oracle_mod.bf16_to_f32(k) * np.repeat(np.random.default_rng(2).uniform(0.2, 1.5, 8), 128)[:1000, None]
+    k = synth.f32_to_bf16_bits(kf.astype(np.float32))
+    perm = np.arange(1000, dtype=np.int32)
+    o = oracle_mod.prepare_head(q, k, v, perm)
+    L, lam = 1000, 0.3
+    out0, by0, S0, _ = oracle_mod.attention_head(o, L, want_bytes=True)
+    outz, byz, _, _ = oracle_mod.attention_head(o, L, want_bytes=True, skip_lambda=0.0)
+    assert np.array_equal(out0, outz) and np.array_equal(by0, byz)
+    out1, by1, S1, _ = oracle_mod.attention_head(o, L, want_bytes=True, skip_lambda=lam)
+    assert np.array_equal(S0, S1)
+    nb = 8
+    cb = (np.float32(o["q_scale"][np.arange(L) // 128][:, None] * o["k_scale"][None, :])
+          * oracle_mod.C0(64)).astype(np.float32)                          # [L, nb]
+    Sv = S0[:, :L].astype(np.float64)
+    bmax = np.stack([Sv[:, 128 * b:min(L, 128 * b + 128)].max(1) for b in range(nb)], 1)
+    t = (bmax * cb).astype(np.float32).astype(np.float64)                 # log2 units
+    m_before = np.concatenate([np.full((L, 1), -np.inf), np.maximum.accumulate(t, 1)[:, :-1]], 1)
+    with np.errstate(invalid="ignore"):
+        rule = np.exp((t - m_before) * math.log(2.0)) < lam               # natural-log units
+    near = np.abs((t - m_before) - math.log2(lam)) < 1e-5
+    live = by0.reshape(L, nb, 128).any(2)          # blocks with a nonzero byte when nothing is rejected
+    rej = ~by1.reshape(L, nb, 128).any(2) & live
+    assert np.all((rej == rule) | near | ~live)
+    assert 0.02 < rule.mean() < 0.9, rule.mean()
+    kept = np.repeat(~rule, 128, axis=1)
+    assert np.array_equal(by1[kept], by0[kept])
+    assert not by1[~kept].any()

@@ -53,7 +53,7 @@ class vc_prepared(ctypes.Structure):
 
 
 class vc_attn_params(ctypes.Structure):
-    _fields_ = [("z_off", ctypes.c_int32), ("out_dtype", ctypes.c_int32)]
+    _fields_ = [("z_off", ctypes.c_int32), ("out_dtype", ctypes.c_int32), ("skip_lambda", ctypes.c_float)]
 
 
 _lock = threading.Lock()

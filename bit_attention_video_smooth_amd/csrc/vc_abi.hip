@@ -106,6 +106,8 @@ int attention_common(const vc_shape* shape, const vc_attn_params* params, const 
     if (params->z_off < 0 || params->z_off > 8) return fail(VC_ERR_INVALID, "z_off=%d out of [0, 8]", params->z_off);
     if (params->out_dtype != 0 && params->out_dtype != 1)
         return fail(VC_ERR_INVALID, "out_dtype must be 0 (fp32) or 1 (bf16)");
+    if (!(params->skip_lambda >= 0.0f && params->skip_lambda <= 1.0f))
+        return fail(VC_ERR_INVALID, "skip_lambda must lie in [0, 1]");
     if ((r = check_prepared(in, false))) return r;
     if ((r = check_ptr(out, "out"))) return r;
     vc::AttnArgs a{};
@@ -118,6 +120,7 @@ int attention_common(const vc_shape* shape, const vc_attn_params* params, const 
     a.nqt = (shape->L + vc::ATTN_BM - 1) / vc::ATTN_BM;
     a.C0 = (float)(1.4426950408889634074 / sqrt((double)shape->d));
     a.KB = (float)(56.0 - 0.35 + 8.0 * (double)params->z_off);
+    a.skip_thr = params->skip_lambda > 0.0f ? (float)log2((double)params->skip_lambda) : -INFINITY;
     a.dump_bh = -1;
     a.dump_qt = -1;
     if (dump) {

@@ -184,7 +184,7 @@ struct Fp8Loader {
     }
 };
 
-template <int D, bool DUMP>
+template <int D, bool DUMP, bool SKIP>
 struct Fp8Wave {
     using T = Fp8Tile<D>;
     const AttnArgs& a;
@@ -200,6 +200,7 @@ struct Fp8Wave {
     uint32_t P[2][8];
     float alpha[2];
     float krow[2], cb;
+    bool reject[2];  // Skip Softmax: this lane's row rejects the block
 
     __device__ __forceinline__ Fp8Wave(const AttnArgs& args, int bh_, int qtile, int w_, int lane_)
         : a(args), bh(bh_), w(w_), lane(lane_) {
@@ -314,6 +315,13 @@ struct Fp8Wave {
             const float t = __fmul_rn(mx[qt], cb);
             const float mn = fmaxf(m[qt], t);
             krow[qt] = __fsub_rn(a.KB, 8.0f * mn);
+            if (SKIP) {
+                // exp(m~ - m) < lambda, in log2 units; +inf on the first
+                // block.  A rejected row has t < m, so m' = m and alpha = 1,
+                // and an infinite offset turns all its bytes into 0.
+                reject[qt] = __fsub_rn(t, m[qt]) < a.skip_thr;
+                if (reject[qt]) krow[qt] = -INFINITY;
+            }
             alpha[qt] = __builtin_amdgcn_exp2f(m[qt] - mn);  // 2^(m - m'), 0 on the first block
             m[qt] = mn;
         }
@@ -360,17 +368,22 @@ struct Fp8Wave {
         }
     }
 
-    __device__ __forceinline__ void slot_softmax(int kb, const lds_u8* st) {
+    // Returns true when every row of the wave rejects the block (Skip
+    // Softmax): then the bytes are not written and P V is skipped.
+    __device__ __forceinline__ bool slot_softmax(int kb, const lds_u8* st) {
         const float ks = *reinterpret_cast<const VC_LDS float*>(st + T::KS_OFF);
         cb = __fmul_rn(__fmul_rn(sq, ks), a.C0);
         const int nvalid = L - kb * BLK;  // keys of this block that exist (>= 1)
         if (nvalid < BLK) {
             softmax_max<true>(cb, nvalid - 4 * g);
+            if (SKIP && !DUMP && __builtin_expect(__all(reject[0] && reject[1]), 0)) return true;
             softmax_bytes<true>(kb, 8.0f * cb, nvalid - 4 * g);
         } else {
             softmax_max<false>(cb, 0);
+            if (SKIP && !DUMP && __builtin_expect(__all(reject[0] && reject[1]), 0)) return true;
             softmax_bytes<false>(kb, 8.0f * cb, 0);
         }
+        return false;
     }
 
     // Row sums (ones(16x128) * P^T, exact), V8^T P^T on the matrix
@@ -442,7 +455,7 @@ struct Fp8Wave {
         slot_qk(cur);
         if (LAG) block_barrier();
         if (LOADER) ld.issue(ahead, min(kb + 2, nb - 1));
-        slot_softmax(kb, cur);
+        const bool rejected = slot_softmax(kb, cur);
         // rescale a query tile only when one of its rows raised its max
 #pragma unroll
         for (int qt = 0; qt < 2; qt++)
@@ -450,7 +463,7 @@ struct Fp8Wave {
 #pragma unroll
                 for (int ct = 0; ct < T::NCT; ct++) O[qt][ct] *= alpha[qt];
             }
-        slot_pv(cur);
+        if (__builtin_expect(!rejected, 1)) slot_pv(cur);
         if (LOADER) {
             if (DUMP)
                 wait_vmcnt<0>();
@@ -471,7 +484,7 @@ struct Fp8Wave {
     }
 };
 
-template <int D, bool OUT_BF16, bool DUMP>
+template <int D, bool OUT_BF16, bool DUMP, bool SKIP>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fp8_kernel(AttnArgs a) {
     using T = Fp8Tile<D>;
     __shared__ __attribute__((aligned(16))) uint8_t st0_[T::STAGE];
@@ -484,7 +497,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fp8_kernel(AttnArgs a) {
     const int bh = pid / a.nqt, qtile = pid % a.nqt;
     // wave index as a scalar (uniform) value
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    Fp8Wave<D, DUMP> s(a, bh, qtile, w, lane);
+    Fp8Wave<D, DUMP, SKIP> s(a, bh, qtile, w, lane);
     const Fp8Loader<D> ld(a, bh, w, lane);
     const int nb = a.nb;
 
@@ -529,21 +542,26 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fp8_kernel(AttnArgs a) {
     }
 }
 
-template <int D, bool OB, bool DUMP>
+template <int D, bool OB, bool DUMP, bool SKIP>
 hipError_t launch_t(const AttnArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL((attn_fp8_kernel<D, OB, DUMP>), dim3(a.BH * a.nqt), dim3(NW * 64), 0, st, a);
+    hipLaunchKernelGGL((attn_fp8_kernel<D, OB, DUMP, SKIP>), dim3(a.BH * a.nqt), dim3(NW * 64), 0, st, a);
     return hipGetLastError();
+}
+
+template <int D, bool OB, bool DUMP>
+hipError_t launch_s(const AttnArgs& a, hipStream_t st) {
+    return a.skip_thr > -INFINITY ? launch_t<D, OB, DUMP, true>(a, st) : launch_t<D, OB, DUMP, false>(a, st);
 }
 
 }  // namespace
 
 hipError_t launch_attn_fp8(const AttnArgs& a, int d, int out_bf16, bool dump, hipStream_t st) {
     if (d == 128) {
-        if (dump) return out_bf16 ? launch_t<128, true, true>(a, st) : launch_t<128, false, true>(a, st);
-        return out_bf16 ? launch_t<128, true, false>(a, st) : launch_t<128, false, false>(a, st);
+        if (dump) return out_bf16 ? launch_s<128, true, true>(a, st) : launch_s<128, false, true>(a, st);
+        return out_bf16 ? launch_s<128, true, false>(a, st) : launch_s<128, false, false>(a, st);
     }
-    if (dump) return out_bf16 ? launch_t<64, true, true>(a, st) : launch_t<64, false, true>(a, st);
-    return out_bf16 ? launch_t<64, true, false>(a, st) : launch_t<64, false, false>(a, st);
+    if (dump) return out_bf16 ? launch_s<64, true, true>(a, st) : launch_s<64, false, true>(a, st);
+    return out_bf16 ? launch_s<64, true, false>(a, st) : launch_s<64, false, false>(a, st);
 }
 
 }  // namespace vc

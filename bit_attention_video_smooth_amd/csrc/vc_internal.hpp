@@ -44,6 +44,7 @@ struct AttnArgs {
     void* out;
     int L, nb, BH, nqt;
     float C0, KB;
+    float skip_thr;  // fp32(log2(lambda)) of Skip Softmax; -infinity: off
     int dump_bh, dump_qt;
     float* s_dump;
     uint8_t* p_dump;

@@ -126,6 +126,9 @@ typedef struct vc_attn_params {
     int32_t z_off;     /* ExpCast offset in 0..8: the running row maximum is
                           written as the code of 2^z_off (8 by default) */
     int32_t out_dtype; /* 0: fp32 output, 1: bf16 output */
+    float skip_lambda; /* Skip Softmax threshold lambda in [0, 1]; 0 rejects
+                          nothing (TensorRT-LLM blog, "Sparse Attention with
+                          Skip Softmax") */
 } vc_attn_params;
 
 /* Fused VC-Attention forward (agihunt ExpCast-FP8 bullet; MarkTechPost
@@ -138,7 +141,14 @@ typedef struct vc_attn_params {
  *   with KB = fp32(56 - 0.35 + 8 z_off);
  *   l_b = row sum of P;  acc = P V8_b on FP8 matrix cores;
  *   O = 2^(m - m') O + s_v,b * acc + l_b * mean_b;  l = 2^(m - m') l + l_b.
- * Output O / l, [B,H,L,d] in the original token order. */
+ * Output O / l, [B,H,L,d] in the original token order.
+ * Skip Softmax (TensorRT-LLM blog, "Sparse Attention with Skip Softmax"):
+ * with skip_lambda > 0, row i rejects block b when exp(m~ - m) < lambda for
+ * the block's maximum score m~ and the running maximum m; in the log2 units
+ * above that is fp32(t - m) < fp32(log2(lambda)), t = fp32(max S * c_b).  A
+ * rejected block leaves m, l and O unchanged (its bytes are 0); when every
+ * row of a wave's 32 queries rejects a block, the wave skips the block's
+ * ExpCast and P V work.  skip_lambda outside [0, 1] or NaN: -1. */
 int vc_attention_fwd(const vc_shape* shape, const vc_attn_params* params,
                      const vc_prepared* in, void* out, hipStream_t stream);
 

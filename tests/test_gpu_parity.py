@@ -138,7 +138,7 @@ def test_prepare_bit_exact(api, shape, v_mode, smooth_k):
 
 # ------------------------------------------------------------ attention ----
 
-def _oracle_out(q, k, v, perm, z_off=8, v_mode=0, rows=None, scores=None):
+def _oracle_out(q, k, v, perm, z_off=8, v_mode=0, rows=None, scores=None, skip_lambda=0.0):
     """Oracle output; with `scores` [B,H,L,Lp] the oracle runs on those fp32
     scores instead of its exactly rounded ones."""
     B, H, L, d = q.shape
@@ -148,7 +148,7 @@ def _oracle_out(q, k, v, perm, z_off=8, v_mode=0, rows=None, scores=None):
         for h in range(H):
             o = _oracle_prep(q, k, v, perm, b, h, 1, v_mode)
             sc = None if scores is None else scores[b, h, r0:r1]
-            out[b, h] = oracle.attention_head(o, L, z_off, rows=rows, scores=sc)
+            out[b, h] = oracle.attention_head(o, L, z_off, rows=rows, scores=sc, skip_lambda=skip_lambda)
     return out
 
 
@@ -295,6 +295,70 @@ def test_attention_scores_and_bytes(api, shape):
         _, gby, _, _ = oracle.attention_head(o, L, 8, rows=(r0, r1), want_bytes=True,
                                              scores=np.ascontiguousarray(S[:n]))
         assert np.array_equal(Pb[:n], gby)
+
+
+# ------------------------------------------------------------ Skip Softmax --
+
+def _skip_inputs(B, H, L, d, seed, grid):
+    """Synthetic inputs whose key blocks differ in score scale (a per-block
+    factor on K in sequence order), so that blocks fall behind the running
+    maximum by varying amounts and the rejection rule has work to do."""
+    q, k, v = _inputs(B, H, L, d, seed, grid)
+    nb = (L + 127) // 128
+    f = np.random.default_rng(seed).uniform(0.2, 1.5, (B, H, nb))
+    kf = oracle.bf16_to_f32(k) * np.repeat(f, 128, axis=2)[:, :, :L, None]
+    return q, synth.f32_to_bf16_bits(kf.astype(np.float32)), v
+
+
+@pytest.mark.parametrize("shape", [SHAPES[0], SHAPES[1], SHAPES[4]])
+@pytest.mark.parametrize("lam", [0.05, 0.3])
+def test_attention_skip_softmax_matches_oracle(api, shape, lam):
+    """Skip Softmax (rejection threshold lambda): given the kernel's scores,
+    output within the given-S bar and ExpCast bytes of a dumped tile
+    bit-exact (rejected blocks all zero); end to end within the output bar.
+    Some block must actually be rejected (the output differs from lambda = 0)."""
+    B, H, L, d, grid = shape
+    q, k, v = _skip_inputs(B, H, L, d, 60 + L, grid)
+    perm = np.tile(np.arange(L, dtype=np.int32), (B, H, 1))
+    P = api.prepare(dev_bf16(q), dev_bf16(k), dev_bf16(v), perm_in=torch.from_numpy(perm).cuda())
+    out = api.attention(P, skip_lambda=lam).cpu().numpy()
+    full = api.attention(P).cpu().numpy()
+    ref = _oracle_out(q, k, v, perm, skip_lambda=lam)
+    refS = _oracle_out(q, k, v, perm, scores=_kernel_scores(api, P), skip_lambda=lam)
+    r, ma = rel_l2(out, ref), float(np.abs(out - ref).max() / np.abs(ref).max())
+    rs, mas = rel_l2(out, refS), float(np.abs(out - refS).max() / np.abs(refS).max())
+    # bytes of the last (ragged) query tile of the last head, given the kernel's S
+    bh = B * H - 1
+    b, h = divmod(bh, H)
+    qt = (L - 1) // 256
+    r0, r1 = qt * 256, L
+    _, S, Pb = api.attention_dump(P, bh, qt, skip_lambda=lam)
+    _, _, Pf = api.attention_dump(P, bh, qt)
+    S, Pb, Pf = S.cpu().numpy()[:r1 - r0], Pb.cpu().numpy()[:r1 - r0], Pf.cpu().numpy()[:r1 - r0]
+    o = _oracle_prep(q, k, v, perm, b, h)
+    _, gby, _, _ = oracle.attention_head(o, L, 8, rows=(r0, r1), want_bytes=True, scores=np.ascontiguousarray(S),
+                                         skip_lambda=lam)
+    nb = Pb.shape[1] // 128
+    rejected = ~Pb.reshape(-1, nb, 128).any(2) & Pf.reshape(-1, nb, 128).any(2)
+    print("skip lambda=%g %s: rejected %.3f of the dumped tile's (row, block) pairs; end-to-end rel-L2 %.3g "
+          "max-abs/max %.3g | given kernel S rel-L2 %.3g max-abs/max %.3g | vs no rejection rel-L2 %.3g"
+          % (lam, (B, H, L, d), rejected.mean(), r, ma, rs, mas, rel_l2(out, full)))
+    assert np.array_equal(Pb, gby)
+    assert rel_l2(out, full) > 1e-6  # some block was rejected somewhere
+    assert rs <= GIVEN_S_REL and mas <= GIVEN_S_MAXABS
+    br, bm = _end_to_end_bar(d)
+    assert r <= br and ma <= bm
+
+
+def test_attention_skip_softmax_tiny_lambda_changes_nothing(api):
+    """A threshold no block reaches (lambda = 1e-30) runs the rejecting kernel
+    variant but keeps every block: output bit-identical to lambda = 0."""
+    B, H, L, d, grid = SHAPES[4]
+    q, k, v = _skip_inputs(B, H, L, d, 77, grid)
+    P = api.prepare(dev_bf16(q), dev_bf16(k), dev_bf16(v), seed=3)
+    a = api.attention(P).cpu().numpy()
+    b = api.attention(P, skip_lambda=1e-30).cpu().numpy()
+    assert np.array_equal(a, b)
 
 
 # ----------------------------------------------------------------- BF16 ----

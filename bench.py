@@ -37,6 +37,8 @@ def parse():
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--no-bf16", action="store_true")
     p.add_argument("--v-scale-mode", type=int, default=0)
+    p.add_argument("--skip-lambda", type=float, default=0.5,
+                   help="Skip Softmax threshold of the extra, reported (not timed-step) attention run; 0: none")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB (negation, fp32) three times: the "
                         "reference kernel of known size that calibrates the HBM byte counters")
@@ -176,6 +178,29 @@ def main():
     torch.cuda.synchronize()
     other_ms = ev[0].elapsed_time(ev[1]) / args.steps
     del P1
+    # Skip Softmax on the same prepared inputs: time, and the fraction of
+    # (row, block) pairs rejected in one sampled query tile (blocks whose
+    # bytes are all zero with rejection but not without)
+    skip = None
+    if args.skip_lambda > 0:
+        api.attention(P, out=out, skip_lambda=args.skip_lambda)
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for _ in range(args.steps):
+            api.attention(P, out=out, skip_lambda=args.skip_lambda)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        skip_ms = ev[0].elapsed_time(ev[1]) / args.steps
+        bh, qt = (B * H) // 2, api.nblocks(L) // 4
+        _, _, pb = api.attention_dump(P, bh, qt, skip_lambda=args.skip_lambda)
+        _, _, pf = api.attention_dump(P, bh, qt)
+        live = pf.view(256, nb, 128).any(2)
+        rej = (~pb.view(256, nb, 128).any(2)) & live
+        skip = {"lambda": args.skip_lambda, "ms": skip_ms, "speedup_vs_no_rejection": attn_ms / skip_ms,
+                "dense_equivalent_tflops": flop / skip_ms / 1e9,
+                "rejected_fraction_sample": float(rej.float().sum() / live.float().sum()),
+                "sample": "query tile %d of head %d (256 rows x %d blocks)" % (qt, bh, nb)}
+        print("skip softmax lambda %g: %.3f ms" % (args.skip_lambda, skip_ms), file=sys.stderr, flush=True)
     bf16 = None
     if not args.no_bf16:
         ob = torch.empty((B, H, L, d), dtype=torch.float32, device="cuda")
@@ -219,6 +244,7 @@ def main():
                     "quant_algorithmic_bytes": quant_bytes,
                     "quant_gbs": quant_bytes / quant_ms / 1e6},
         "bf16_attention": bf16,
+        "skip_softmax": skip,
         "roofline": {"bound": "mfma", "achieved": attn_tflops, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": attn_tflops / FP8_PEAK_TFLOPS, "traffic": measured_traffic(cfg.name)},
         "cpu_baseline": None,

@@ -263,6 +263,9 @@ struct Fp8Wave {
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA: tile kt
             if (kt + 2 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read: tile kt+2
         }
+        // keep the softmax out of this region: mixed into the products, its
+        // vector work would wait behind their operand reads (in-order issue)
+        __builtin_amdgcn_sched_barrier(0);
     }
 
     // Running max and ExpCast-FP8 bytes (vector ALU).  A wave issues a
@@ -369,21 +372,20 @@ struct Fp8Wave {
     }
 
     // Returns true when every row of the wave rejects the block (Skip
-    // Softmax): then the bytes are not written and P V is skipped.
+    // Softmax; its bytes are then all 0): the caller skips P V.  (Branching
+    // around the byte conversion as well costs more than it saves.)
     __device__ __forceinline__ bool slot_softmax(int kb, const lds_u8* st) {
         const float ks = *reinterpret_cast<const VC_LDS float*>(st + T::KS_OFF);
         cb = __fmul_rn(__fmul_rn(sq, ks), a.C0);
         const int nvalid = L - kb * BLK;  // keys of this block that exist (>= 1)
         if (nvalid < BLK) {
             softmax_max<true>(cb, nvalid - 4 * g);
-            if (SKIP && !DUMP && __builtin_expect(__all(reject[0] && reject[1]), 0)) return true;
             softmax_bytes<true>(kb, 8.0f * cb, nvalid - 4 * g);
         } else {
             softmax_max<false>(cb, 0);
-            if (SKIP && !DUMP && __builtin_expect(__all(reject[0] && reject[1]), 0)) return true;
             softmax_bytes<false>(kb, 8.0f * cb, 0);
         }
-        return false;
+        return SKIP && !DUMP && __all(reject[0] && reject[1]);
     }
 
     // Row sums (ones(16x128) * P^T, exact), V8^T P^T on the matrix

@@ -245,6 +245,7 @@ def main():
                     "quant_gbs": quant_bytes / quant_ms / 1e6},
         "bf16_attention": bf16,
         "skip_softmax": skip,
+        "grouping_schedule": grouping_schedule(prep_ms, quant_ms, attn_ms),
         "roofline": {"bound": "mfma", "achieved": attn_tflops, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": attn_tflops / FP8_PEAK_TFLOPS, "traffic": measured_traffic(cfg.name)},
         "cpu_baseline": None,
@@ -252,6 +253,20 @@ def main():
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(cfg, qn, kn, vn, args.cpu_rows)
     print(json.dumps(res))
+
+
+def grouping_schedule(prep_ms, quant_ms, attn_ms, num_steps=40):
+    """Amortised prepare cost over a denoising schedule where grouping
+    (k-means) runs only in the first 25% of the steps and a permutation is
+    reused across 4 adjacent steps, from the two prepare times measured
+    above (with k-means, and with the permutation passed back in)."""
+    from bit_attention_video_smooth_amd.schedule import GroupingSchedule
+    s = GroupingSchedule(num_steps)
+    n = len(s.grouping_steps())
+    amort = s.amortised(prep_ms, quant_ms)
+    return {"num_steps": num_steps, "group_frac": s.group_frac, "reuse": s.reuse, "grouping_steps": n,
+            "prepare_ms_amortised": amort, "step_ms_amortised": amort + attn_ms,
+            "grouping_share_of_attention": n * (prep_ms - quant_ms) / (num_steps * attn_ms)}
 
 
 def cpu_baseline(cfg, qn, kn, vn, rows):

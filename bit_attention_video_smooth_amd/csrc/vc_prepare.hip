@@ -239,7 +239,9 @@ __global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict
     }
 }
 
-__global__ void copy_perm_kernel(const int32_t* __restrict__ src, int32_t* __restrict__ dst, size_t n,
+// src may equal dst (a permutation kept from an earlier call): each element
+// is read and written by the same thread.
+__global__ void copy_perm_kernel(const int32_t* src, int32_t* dst, size_t n,
                                  double* __restrict__ obj, size_t nobj) {
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) dst[i] = src[i];

@@ -115,7 +115,9 @@ int vsmooth_workspace_bytes(const vc_shape* shape, const vsmooth_params* params,
  *   4. per permuted block: exact mean of V, residual r = V - mean, per
  *      channel scale (v_scale_mode), E4M3 codes of r (round to nearest even).
  * q, k, v: bf16 [B,H,L,d].  perm_in: NULL or int32 [B,H,L] (each row a
- * permutation of 0..L-1; copied to out->perm).  ws: ws_bytes >=
+ * permutation of 0..L-1; copied to out->perm; it may be out->perm itself,
+ * to keep the permutation of an earlier call across denoising steps, as the
+ * MarkTechPost abstract describes).  ws: ws_bytes >=
  * vsmooth_workspace_bytes().  Padded slots (>= L) get code 0. */
 int vsmooth_prepare(const vc_shape* shape, const vsmooth_params* params, const void* q,
                     const void* k, const void* v, const int32_t* perm_in,

@@ -218,6 +218,21 @@ def main():
                 "fp8_speedup_over_bf16": bf16_ms / attn_ms}
         print("bf16 attention %.3f ms" % bf16_ms, file=sys.stderr, flush=True)
 
+    # V-Smooth token-ordering ablation on this workload (prepare outputs of
+    # the library; statistics averaged over heads)
+    from bit_attention_video_smooth_amd.ablation import cube_permutation, value_stats
+    ablation = {}
+    orders = {"sequence": torch.arange(L, dtype=torch.int32, device="cuda").expand(B, H, L).contiguous(),
+              "static_cube_2x8x8": torch.from_numpy(cube_permutation(cfg.grid)).cuda().expand(B, H, L).contiguous(),
+              "kmeans": P.perm.clone()}
+    Pa = api.alloc_prepared(B, H, L, d)
+    for name, perm in orders.items():
+        api.prepare(q, k, v, perm_in=perm, out=Pa, ws=ws, v_scale_mode=args.v_scale_mode)
+        st = value_stats(Pa, v)
+        ablation[name] = {"energy_removed": float(st["energy_removed"].mean()),
+                          "v_rel_err": float(st["v_rel_err"].mean())}
+    del Pa
+
     attn_tflops = flop / attn_ms / 1e9
     res = {
         "metric": "FP8 attention TFLOP/s (4*B*H*L^2*d) & % FP8 MFMA peak, Wan2.2-shaped L=75,600",
@@ -246,6 +261,7 @@ def main():
         "bf16_attention": bf16,
         "skip_softmax": skip,
         "grouping_schedule": grouping_schedule(prep_ms, quant_ms, attn_ms),
+        "v_smooth_ablation": ablation,
         "roofline": {"bound": "mfma", "achieved": attn_tflops, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": attn_tflops / FP8_PEAK_TFLOPS, "traffic": measured_traffic(cfg.name)},
         "cpu_baseline": None,

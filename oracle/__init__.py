@@ -250,13 +250,17 @@ def skip_threshold(skip_lambda: float) -> np.float32:
 
 
 def attention_head(prep: dict, L: int, z_off: int = 8, rows=None, want_bytes=False, scores=None,
-                   skip_lambda: float = 0.0):
+                   skip_lambda: float = 0.0, prob_cast: int = 0):
     """Quantised VC-Attention for one head from prepare_head() output.
     rows: (r0, r1) or None for all.  Returns O [r1-r0, d] fp32 (and, with
     want_bytes, the ExpCast bytes, S values and pre-rounding y values
     [r1-r0, Lp] of every block).  scores: optional fp32 [r1-r0, Lp] used in
     place of the exactly rounded Q8 K8^T sums (every later step is unique
-    given the scores).  skip_lambda: the Skip Softmax threshold (0: off)."""
+    given the scores).  skip_lambda: the Skip Softmax threshold (0: off).
+    prob_cast: 0 ExpCast-FP8 bytes (the method), 1 exp-then-cast (the fp32
+    exponential 2^z, correctly rounded, cast to E4M3; y then holds z)."""
+    if prob_cast not in (0, 1):
+        raise ValueError("prob_cast must be 0 or 1")
     q8 = _c(prep["q8"], np.uint8)
     k8 = _c(prep["k8"], np.uint8)
     v8 = _c(prep["v8"], np.uint8)
@@ -273,7 +277,7 @@ def attention_head(prep: dict, L: int, z_off: int = 8, rows=None, want_bytes=Fal
     if scores is not None:
         sin = _c(scores, np.float32)
         assert sin.shape == (r1 - r0, Lp)
-    lib().vco_attention_rows(0, L, d, z_off, _p(q8), _p(k8), _p(v8), _p(qs), _p(ks), _p(vs),
+    lib().vco_attention_rows(2 if prob_cast else 0, L, d, z_off, _p(q8), _p(k8), _p(v8), _p(qs), _p(ks), _p(vs),
                              _p(vm), None, None, None, r0, r1, _p(out), _p(by), _p(S), _p(y), _p(sin),
                              skip_threshold(skip_lambda))
     return (out, by, S, y) if want_bytes else out

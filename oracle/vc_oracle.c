@@ -415,6 +415,11 @@ float vco_c0(int d) { return (float)(1.4426950408889634074 / sqrt((double)d)); }
 /*   acc_c = fp32(exact sum_j p_j rhat_jc)                                   */
 /*   alpha = 2^(m - m')   (0 on the first block)                             */
 /*   O     = alpha O + s_v,b (.) acc + l_b mu_b;  l = alpha l + l_b          */
+/* mode 2 (exp-then-cast, the FP8 path ExpCast replaces): as mode 0 but    */
+/*   byte_j = E4M3(fp32(2^z_j)), z_j = fmaf(S_j, c_b, fp32(z_off - m')),      */
+/*   2^z correctly rounded to fp32, E4M3 round to nearest even ([MTP]       */
+/*   abstract: ExpCast is compared with computing the FP32 exponential and  */
+/*   casting it to FP8).                                                    */
 /* mode 1 (exact algebra, for checking the blockwise bookkeeping):          */
 /*   qhat, khat, rhat are the real values (scales 1), S is a double sum,      */
 /*   p_j = 2^(S_j C0 - m') in double; the rest as in mode 0.  With mode 1 the */
@@ -464,14 +469,14 @@ void vco_attention_rows(int mode, int L, int d, int z_off,
         float* S = (float*)malloc(sizeof(float) * VCO_BLK);
         double* p = (double*)malloc(sizeof(double) * VCO_BLK);
         for (int c = 0; c < d; c++)
-            qrow[c] = (mode == 0) ? dec[q8[(int64_t)i * d + c]] : qf[(int64_t)i * d + c];
+            qrow[c] = (mode != 1) ? dec[q8[(int64_t)i * d + c]] : qf[(int64_t)i * d + c];
         double m = -INFINITY, l = 0.0;
         for (int b = 0; b < nb; b++) {
             int n = (L - b * VCO_BLK < VCO_BLK) ? L - b * VCO_BLK : VCO_BLK;
             double m_new, ell = 0.0;
             /* scores */
             for (int j = 0; j < n; j++) {
-                if (mode == 0 && S_in) {
+                if (mode != 1 && S_in) {
                     S[j] = S_in[(int64_t)(i - r0) * Lp + b * VCO_BLK + j];
                     Sd[j] = S[j];
                     continue;
@@ -479,11 +484,11 @@ void vco_attention_rows(int mode, int L, int d, int z_off,
                 int64_t kr = (int64_t)(b * VCO_BLK + j) * d;
                 double acc = 0.0;
                 for (int c = 0; c < d; c++)
-                    acc += qrow[c] * ((mode == 0) ? dec[k8[kr + c]] : kf[kr + c]);
+                    acc += qrow[c] * ((mode != 1) ? dec[k8[kr + c]] : kf[kr + c]);
                 Sd[j] = acc;
                 S[j] = (float)acc;
             }
-            if (mode == 0) {
+            if (mode == 0 || mode == 2) {
                 volatile float sqk = q_scale[i / VCO_BLK] * k_scale[b];
                 volatile float cb = sqk * C0;
                 float mx = -INFINITY;
@@ -505,13 +510,17 @@ void vco_attention_rows(int mode, int L, int d, int z_off,
                 volatile float e8 = 8.0f * mnf;
                 volatile float krow = KB - e8;
                 volatile float c8 = 8.0f * cb;
+                volatile float zrow = (float)z_off - mnf;
                 for (int j = 0; j < VCO_BLK; j++) {
-                    uint8_t by = (j < n) ? vco_expcast1(S[j], c8, krow) : 0;
+                    uint8_t by = 0;
+                    if (j < n)
+                        by = (mode == 0) ? vco_expcast1(S[j], c8, krow)
+                                         : vco_e4m3_encode((float)exp2((double)fmaf(S[j], cb, zrow)));
                     if (bytes_out) bytes_out[(int64_t)(i - r0) * Lp + b * VCO_BLK + j] = by;
                     if (S_out) S_out[(int64_t)(i - r0) * Lp + b * VCO_BLK + j] = (j < n) ? S[j] : 0.0f;
                     if (y_out)
                         y_out[(int64_t)(i - r0) * Lp + b * VCO_BLK + j] =
-                            (j < n) ? fmaf(S[j], c8, krow) : -INFINITY;
+                            (j >= n) ? -INFINITY : (mode == 0) ? fmaf(S[j], c8, krow) : fmaf(S[j], cb, zrow);
                     p[j] = dec[by];
                     if (j < n) ell += p[j];
                 }
@@ -527,9 +536,9 @@ void vco_attention_rows(int mode, int L, int d, int z_off,
                 int64_t vr = ((int64_t)b * d + c) * VCO_BLK;
                 double acc = 0.0;
                 for (int j = 0; j < n; j++)
-                    acc += p[j] * ((mode == 0) ? dec[v8[vr + j]] : rf[vr + j]);
-                double sv = (mode == 0) ? (double)v_scale[(int64_t)b * d + c] : 1.0;
-                double accr = (mode == 0) ? (double)(float)acc : acc;
+                    acc += p[j] * ((mode != 1) ? dec[v8[vr + j]] : rf[vr + j]);
+                double sv = (mode != 1) ? (double)v_scale[(int64_t)b * d + c] : 1.0;
+                double accr = (mode != 1) ? (double)(float)acc : acc;
                 O[c] = alpha * O[c] + sv * accr + ell * (double)v_mean[(int64_t)b * d + c];
             }
             l = alpha * l + ell;

@@ -556,3 +556,31 @@ def test_skip_softmax_quantised_rejects_by_the_printed_rule(oracle_mod):
     kept = np.repeat(~rule, 128, axis=1)
     assert np.array_equal(by1[kept], by0[kept])
     assert not by1[~kept].any()
+
+
+# ------------------------------------------------- exp-then-cast (the baseline) --
+
+def test_exp_then_cast_bytes_are_library_cast_of_exp2(oracle_mod):
+    """prob_cast=1: every byte is the library's E4M3 cast of 2^z, z = S c_b -
+    m' + z_off (computed here in fp64 from the oracle's own S and scales); the
+    row max lands on 2^8; and against ExpCast the bytes agree in the
+    proportion the pages give per doubling (79.6%), differing by one code
+    otherwise (on bytes above the subnormal range)."""
+    cfg = synth.custom(1, 1, 256, 64)
+    q, k, v = (a[0, 0] for a in synth.make_inputs(cfg, 9))
+    P = oracle_mod.prepare_head(q, k, v, np.arange(256, dtype=np.int32))
+    out, by, S, z = oracle_mod.attention_head(P, 256, rows=(0, 64), want_bytes=True, prob_cast=1)
+    cb = np.float32(np.float32(P["q_scale"][0] * P["k_scale"][0]) * oracle_mod.C0(64))
+    S0 = S[:, :128].astype(np.float64)
+    t = (S[:, :128].max(1) * cb).astype(np.float32).astype(np.float64)
+    zz = S0 * np.float64(cb) - t[:, None] + 8.0
+    assert np.allclose(z[:, :128], zz, rtol=0, atol=1e-5)
+    ref = torch.from_numpy(np.exp2(z[:, :128].astype(np.float64)).astype(np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(ref, by[:, :128])
+    assert (by[:, :128].max(1) == 120).all()
+    _, bye, _, _ = oracle_mod.attention_head(P, 256, rows=(0, 64), want_bytes=True)
+    big = by[:, :128] >= 16
+    agree = float((bye[:, :128][big] == by[:, :128][big]).mean())
+    assert np.abs(bye[:, :128][big].astype(int) - by[:, :128][big].astype(int)).max() <= 1
+    assert abs(agree - GOLD["expcast_agreement_per_doubling"]["value"]) < 0.05, agree

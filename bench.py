@@ -218,6 +218,19 @@ def main():
                 "fp8_speedup_over_bf16": bf16_ms / attn_ms}
         print("bf16 attention %.3f ms" % bf16_ms, file=sys.stderr, flush=True)
 
+    # the FP8 path ExpCast replaces (fp32 exp2, then the E4M3 conversion), on
+    # the same prepared inputs
+    api.attention(P, out=out, prob_cast=1)
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for _ in range(args.steps):
+        api.attention(P, out=out, prob_cast=1)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    naive_ms = ev[0].elapsed_time(ev[1]) / args.steps
+    exp_then_cast = {"ms": naive_ms, "tflops": flop / naive_ms / 1e9, "expcast_speedup": naive_ms / attn_ms}
+    print("exp-then-cast attention %.3f ms" % naive_ms, file=sys.stderr, flush=True)
+
     # V-Smooth token-ordering ablation on this workload (prepare outputs of
     # the library; statistics averaged over heads)
     from bit_attention_video_smooth_amd.ablation import cube_permutation, value_stats
@@ -259,6 +272,7 @@ def main():
                     "quant_algorithmic_bytes": quant_bytes,
                     "quant_gbs": quant_bytes / quant_ms / 1e6},
         "bf16_attention": bf16,
+        "exp_then_cast_attention": exp_then_cast,
         "skip_softmax": skip,
         "grouping_schedule": grouping_schedule(prep_ms, quant_ms, attn_ms),
         "v_smooth_ablation": ablation,

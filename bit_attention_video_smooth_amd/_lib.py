@@ -53,7 +53,8 @@ class vc_prepared(ctypes.Structure):
 
 
 class vc_attn_params(ctypes.Structure):
-    _fields_ = [("z_off", ctypes.c_int32), ("out_dtype", ctypes.c_int32), ("skip_lambda", ctypes.c_float)]
+    _fields_ = [("z_off", ctypes.c_int32), ("out_dtype", ctypes.c_int32), ("skip_lambda", ctypes.c_float),
+                ("prob_cast", ctypes.c_int32)]
 
 
 _lock = threading.Lock()

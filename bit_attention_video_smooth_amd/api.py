@@ -72,19 +72,20 @@ def prepare(q, k, v, *, perm_in=None, kmeans_k=0, kmeans_iters=8, seed=0, smooth
     return out
 
 
-def attention(prep: Prepared, *, z_off=8, out_dtype=torch.float32, out=None, skip_lambda=0.0, stream=None):
+def attention(prep: Prepared, *, z_off=8, out_dtype=torch.float32, out=None, skip_lambda=0.0, prob_cast=0,
+              stream=None):
     """vc_attention_fwd: O [B,H,L,d] in fp32 or bf16 (skip_lambda: the Skip
-    Softmax threshold, 0 = off)."""
+    Softmax threshold, 0 = off; prob_cast: 0 ExpCast-FP8, 1 exp-then-cast)."""
     B, H, L, d = prep.shape
     if out is None:
         out = torch.empty((B, H, L, d), dtype=out_dtype, device=prep.q8.device)
     od = 1 if out.dtype == torch.bfloat16 else 0
-    _lib.vc_attention_fwd(_lib.shape_of(B, H, L, d), _lib.vc_attn_params(z_off, od, skip_lambda), prep.c(),
+    _lib.vc_attention_fwd(_lib.shape_of(B, H, L, d), _lib.vc_attn_params(z_off, od, skip_lambda, prob_cast), prep.c(),
                           out, stream)
     return out
 
 
-def attention_dump(prep: Prepared, bh: int, q_tile: int, *, z_off=8, skip_lambda=0.0, stream=None):
+def attention_dump(prep: Prepared, bh: int, q_tile: int, *, z_off=8, skip_lambda=0.0, prob_cast=0, stream=None):
     """vc_attention_fwd_dump: returns (O fp32, S [256, Lp] fp32, P [256, Lp] u8)."""
     B, H, L, d = prep.shape
     Lp = nblocks(L) * BLK
@@ -92,7 +93,7 @@ def attention_dump(prep: Prepared, bh: int, q_tile: int, *, z_off=8, skip_lambda
     out = torch.empty((B, H, L, d), dtype=torch.float32, device=dev)
     s = torch.zeros((256, Lp), dtype=torch.float32, device=dev)
     p = torch.zeros((256, Lp), dtype=torch.uint8, device=dev)
-    _lib.vc_attention_fwd_dump(_lib.shape_of(B, H, L, d), _lib.vc_attn_params(z_off, 0, skip_lambda), prep.c(),
+    _lib.vc_attention_fwd_dump(_lib.shape_of(B, H, L, d), _lib.vc_attn_params(z_off, 0, skip_lambda, prob_cast), prep.c(),
                                out, bh, q_tile, s, p, stream)
     return out, s, p
 

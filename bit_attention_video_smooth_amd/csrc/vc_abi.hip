@@ -108,6 +108,8 @@ int attention_common(const vc_shape* shape, const vc_attn_params* params, const 
         return fail(VC_ERR_INVALID, "out_dtype must be 0 (fp32) or 1 (bf16)");
     if (!(params->skip_lambda >= 0.0f && params->skip_lambda <= 1.0f))
         return fail(VC_ERR_INVALID, "skip_lambda must lie in [0, 1]");
+    if (params->prob_cast != 0 && params->prob_cast != 1)
+        return fail(VC_ERR_INVALID, "prob_cast must be 0 (ExpCast-FP8) or 1 (exp-then-cast)");
     if ((r = check_prepared(in, false))) return r;
     if ((r = check_ptr(out, "out"))) return r;
     vc::AttnArgs a{};
@@ -121,6 +123,8 @@ int attention_common(const vc_shape* shape, const vc_attn_params* params, const 
     a.C0 = (float)(1.4426950408889634074 / sqrt((double)shape->d));
     a.KB = (float)(56.0 - 0.35 + 8.0 * (double)params->z_off);
     a.skip_thr = params->skip_lambda > 0.0f ? (float)log2((double)params->skip_lambda) : -INFINITY;
+    a.ZOFF = (float)params->z_off;
+    a.prob_cast = params->prob_cast;
     a.dump_bh = -1;
     a.dump_qt = -1;
     if (dump) {

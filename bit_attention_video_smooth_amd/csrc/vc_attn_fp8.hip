@@ -184,7 +184,7 @@ struct Fp8Loader {
     }
 };
 
-template <int D, bool DUMP, bool SKIP>
+template <int D, bool DUMP, bool SKIP, bool NAIVE>
 struct Fp8Wave {
     using T = Fp8Tile<D>;
     const AttnArgs& a;
@@ -317,7 +317,8 @@ struct Fp8Wave {
         for (int qt = 0; qt < 2; qt++) {
             const float t = __fmul_rn(mx[qt], cb);
             const float mn = fmaxf(m[qt], t);
-            krow[qt] = __fsub_rn(a.KB, 8.0f * mn);
+            // ExpCast: y = fma(S, 8 c_b, KB - 8 m'); exp-then-cast: z = fma(S, c_b, z_off - m')
+            krow[qt] = NAIVE ? __fsub_rn(a.ZOFF, mn) : __fsub_rn(a.KB, 8.0f * mn);
             if (SKIP) {
                 // exp(m~ - m) < lambda, in log2 units; +inf on the first
                 // block.  A rejected row has t < m, so m' = m and alpha = 1,
@@ -334,7 +335,22 @@ struct Fp8Wave {
     __device__ __forceinline__ void softmax_bytes(int kb, float c8, int lim) {
 #pragma unroll
         for (int qt = 0; qt < 2; qt++) {
-            if (!MASKED) {
+            if (NAIVE) {
+                // the path ExpCast replaces: p = 2^z in fp32 (v_exp_f32), then
+                // the hardware E4M3 conversion (round to nearest even), two
+                // bytes per instruction; c8 holds c_b here
+#pragma unroll
+                for (int kt = 0; kt < 8; kt++) {
+                    float p[4];
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[qt][kt][i], c8, krow[qt]));
+                        if (MASKED && !(16 * kt + i < lim)) p[i] = 0.f;  // keys past L keep byte 0
+                    }
+                    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+                    P[qt][kt] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], lo, true);
+                }
+            } else if (!MASKED) {
 #pragma unroll
                 for (int k4 = 0; k4 < 8; k4 += 4) {
                     float y[16];
@@ -378,12 +394,13 @@ struct Fp8Wave {
         const float ks = *reinterpret_cast<const VC_LDS float*>(st + T::KS_OFF);
         cb = __fmul_rn(__fmul_rn(sq, ks), a.C0);
         const int nvalid = L - kb * BLK;  // keys of this block that exist (>= 1)
+        const float cscale = NAIVE ? cb : 8.0f * cb;
         if (nvalid < BLK) {
             softmax_max<true>(cb, nvalid - 4 * g);
-            softmax_bytes<true>(kb, 8.0f * cb, nvalid - 4 * g);
+            softmax_bytes<true>(kb, cscale, nvalid - 4 * g);
         } else {
             softmax_max<false>(cb, 0);
-            softmax_bytes<false>(kb, 8.0f * cb, 0);
+            softmax_bytes<false>(kb, cscale, 0);
         }
         return SKIP && !DUMP && __all(reject[0] && reject[1]);
     }
@@ -486,7 +503,7 @@ struct Fp8Wave {
     }
 };
 
-template <int D, bool OUT_BF16, bool DUMP, bool SKIP>
+template <int D, bool OUT_BF16, bool DUMP, bool SKIP, bool NAIVE>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fp8_kernel(AttnArgs a) {
     using T = Fp8Tile<D>;
     __shared__ __attribute__((aligned(16))) uint8_t st0_[T::STAGE];
@@ -499,7 +516,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fp8_kernel(AttnArgs a) {
     const int bh = pid / a.nqt, qtile = pid % a.nqt;
     // wave index as a scalar (uniform) value
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    Fp8Wave<D, DUMP, SKIP> s(a, bh, qtile, w, lane);
+    Fp8Wave<D, DUMP, SKIP, NAIVE> s(a, bh, qtile, w, lane);
     const Fp8Loader<D> ld(a, bh, w, lane);
     const int nb = a.nb;
 
@@ -544,15 +561,18 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fp8_kernel(AttnArgs a) {
     }
 }
 
-template <int D, bool OB, bool DUMP, bool SKIP>
+template <int D, bool OB, bool DUMP, bool SKIP, bool NAIVE>
 hipError_t launch_t(const AttnArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL((attn_fp8_kernel<D, OB, DUMP, SKIP>), dim3(a.BH * a.nqt), dim3(NW * 64), 0, st, a);
+    hipLaunchKernelGGL((attn_fp8_kernel<D, OB, DUMP, SKIP, NAIVE>), dim3(a.BH * a.nqt), dim3(NW * 64), 0, st, a);
     return hipGetLastError();
 }
 
 template <int D, bool OB, bool DUMP>
 hipError_t launch_s(const AttnArgs& a, hipStream_t st) {
-    return a.skip_thr > -INFINITY ? launch_t<D, OB, DUMP, true>(a, st) : launch_t<D, OB, DUMP, false>(a, st);
+    const bool skip = a.skip_thr > -INFINITY;
+    if (a.prob_cast == 1)
+        return skip ? launch_t<D, OB, DUMP, true, true>(a, st) : launch_t<D, OB, DUMP, false, true>(a, st);
+    return skip ? launch_t<D, OB, DUMP, true, false>(a, st) : launch_t<D, OB, DUMP, false, false>(a, st);
 }
 
 }  // namespace

@@ -45,6 +45,8 @@ struct AttnArgs {
     int L, nb, BH, nqt;
     float C0, KB;
     float skip_thr;  // fp32(log2(lambda)) of Skip Softmax; -infinity: off
+    float ZOFF;      // z_off as fp32 (exp-then-cast bytes)
+    int prob_cast;   // 0 ExpCast-FP8, 1 exp-then-cast
     int dump_bh, dump_qt;
     float* s_dump;
     uint8_t* p_dump;

@@ -131,6 +131,11 @@ typedef struct vc_attn_params {
     float skip_lambda; /* Skip Softmax threshold lambda in [0, 1]; 0 rejects
                           nothing (TensorRT-LLM blog, "Sparse Attention with
                           Skip Softmax") */
+    int32_t prob_cast; /* probability bytes: 0 ExpCast-FP8 (the method);
+                          1 exp-then-cast, the FP8 path ExpCast replaces
+                          (MarkTechPost abstract): z = fma(S, c_b,
+                          z_off - m'), p = 2^z in fp32, E4M3 round to
+                          nearest even.  Other values: -1 */
 } vc_attn_params;
 
 /* Fused VC-Attention forward (agihunt ExpCast-FP8 bullet; MarkTechPost

@@ -117,6 +117,10 @@ def test_attention_rejects_bad_params(lib):
         with pytest.raises(_lib.VCError) as e:
             _lib.vc_attention_fwd(s, _lib.vc_attn_params(z, od), _prep(), FAKE, 0)
         assert e.value.code == _lib.VC_ERR_INVALID
+    for pc in (-1, 2):
+        with pytest.raises(_lib.VCError) as e:
+            _lib.vc_attention_fwd(s, _lib.vc_attn_params(8, 0, 0.0, pc), _prep(), FAKE, 0)
+        assert e.value.code == _lib.VC_ERR_INVALID
     for lam in (-0.1, 1.5, float("nan")):
         with pytest.raises(_lib.VCError) as e:
             _lib.vc_attention_fwd(s, _lib.vc_attn_params(8, 0, lam), _prep(), FAKE, 0)

@@ -138,7 +138,7 @@ def test_prepare_bit_exact(api, shape, v_mode, smooth_k):
 
 # ------------------------------------------------------------ attention ----
 
-def _oracle_out(q, k, v, perm, z_off=8, v_mode=0, rows=None, scores=None, skip_lambda=0.0):
+def _oracle_out(q, k, v, perm, z_off=8, v_mode=0, rows=None, scores=None, skip_lambda=0.0, prob_cast=0):
     """Oracle output; with `scores` [B,H,L,Lp] the oracle runs on those fp32
     scores instead of its exactly rounded ones."""
     B, H, L, d = q.shape
@@ -148,7 +148,8 @@ def _oracle_out(q, k, v, perm, z_off=8, v_mode=0, rows=None, scores=None, skip_l
         for h in range(H):
             o = _oracle_prep(q, k, v, perm, b, h, 1, v_mode)
             sc = None if scores is None else scores[b, h, r0:r1]
-            out[b, h] = oracle.attention_head(o, L, z_off, rows=rows, scores=sc, skip_lambda=skip_lambda)
+            out[b, h] = oracle.attention_head(o, L, z_off, rows=rows, scores=sc, skip_lambda=skip_lambda,
+                                              prob_cast=prob_cast)
     return out
 
 
@@ -359,6 +360,45 @@ def test_attention_skip_softmax_tiny_lambda_changes_nothing(api):
     a = api.attention(P).cpu().numpy()
     b = api.attention(P, skip_lambda=1e-30).cpu().numpy()
     assert np.array_equal(a, b)
+
+
+# ----------------------------------------------------------- exp-then-cast --
+
+@pytest.mark.parametrize("shape", [SHAPES[0], SHAPES[1], SHAPES[4]])
+def test_attention_exp_then_cast_matches_oracle(api, shape):
+    """prob_cast=1 (2^z in fp32 by v_exp_f32, then the hardware E4M3
+    conversion): given the kernel's scores, the bytes of a dumped tile equal
+    the oracle's correctly rounded exp2 cast to E4M3 except where v_exp_f32's
+    last-bit error straddles an E4M3 rounding midpoint (one code, rate below
+    1e-4), and the output is within the given-S bar; end to end within the
+    output bar."""
+    B, H, L, d, grid = shape
+    q, k, v = _inputs(B, H, L, d, 90 + L, grid)
+    perm = synth.random_perms(B, H, L, 13)
+    P = api.prepare(dev_bf16(q), dev_bf16(k), dev_bf16(v), perm_in=torch.from_numpy(perm).cuda())
+    out = api.attention(P, prob_cast=1).cpu().numpy()
+    ref = _oracle_out(q, k, v, perm, prob_cast=1)
+    refS = _oracle_out(q, k, v, perm, scores=_kernel_scores(api, P), prob_cast=1)
+    r, ma = rel_l2(out, ref), float(np.abs(out - ref).max() / np.abs(ref).max())
+    rs, mas = rel_l2(out, refS), float(np.abs(out - refS).max() / np.abs(refS).max())
+    bh = B * H - 1
+    b, h = divmod(bh, H)
+    qt = (L - 1) // 256
+    r0, r1 = qt * 256, L
+    _, S, Pb = api.attention_dump(P, bh, qt, prob_cast=1)
+    S, Pb = S.cpu().numpy()[:r1 - r0], Pb.cpu().numpy()[:r1 - r0]
+    o = _oracle_prep(q, k, v, perm, b, h)
+    _, gby, _, _ = oracle.attention_head(o, L, 8, rows=(r0, r1), want_bytes=True, scores=np.ascontiguousarray(S),
+                                         prob_cast=1)
+    diff = Pb.astype(int) - gby.astype(int)
+    print("exp-then-cast %s: byte mismatch %.2e (max |d| %d); end-to-end rel-L2 %.3g max-abs/max %.3g | "
+          "given kernel S rel-L2 %.3g max-abs/max %.3g"
+          % ((B, H, L, d), float((diff != 0).mean()), np.abs(diff).max(), r, ma, rs, mas))
+    assert np.abs(diff).max() <= 1 and float((diff != 0).mean()) <= 1e-4
+    assert Pb.max() == 120  # the row maximum is 2^8
+    assert rs <= GIVEN_S_REL and mas <= GIVEN_S_MAXABS
+    br, bm = _end_to_end_bar(d)
+    assert r <= br and ma <= bm
 
 
 # ----------------------------------------------------------------- BF16 ----

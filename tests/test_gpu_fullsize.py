@@ -26,7 +26,7 @@ def dev_bf16(u16):
     return torch.from_numpy(np.ascontiguousarray(u16)).view(torch.bfloat16).cuda()
 
 
-@pytest.mark.parametrize("cfg_idx", [1, 2, 4])
+@pytest.mark.parametrize("cfg_idx", [1, 2, 3, 4])
 def test_full_size_sampled(api, cfg_idx):
     cfg = synth.CONFIGS[cfg_idx]
     B, H, L, d = cfg.B, cfg.H, cfg.L, cfg.d

@@ -38,7 +38,8 @@ def _inputs(B, H, L, d, seed, grid=None):
 
 
 SHAPES = [(1, 2, 1024, 64, (4, 16, 16)), (1, 3, 300, 128, None), (2, 2, 129, 64, None),
-          (1, 1, 1, 128, None), (1, 2, 4000, 128, None), (1, 1, 520, 64, None)]
+          (1, 1, 1, 128, None), (1, 2, 4000, 128, None), (1, 1, 520, 64, None),
+          (1, 1, 500, 128, None)]  # 4 blocks (a whole turn of the LDS ring), ragged last block
 
 
 # ----------------------------------------------------------- primitives ----

@@ -185,9 +185,10 @@ __global__ __launch_bounds__(512) void km_assign(const uint16_t* __restrict__ v,
             }
             if (t < KT) stn = nb[c0 + KT + t];
         }
-#pragma unroll
-        for (int ct = 0; ct < KT / 16; ct++) {
-            if (c0 + 16 * ct >= k) break;  // padding tiles (uniform)
+        // 16-centroid tiles of this LDS tile that hold real centroids: all of
+        // them except in the last tile; the full case is one straight block
+        // so that operand reads of one tile overlap the products of another
+        auto ctile = [&](int ct) {
             const int r = 16 * ct + col;
             v8bf ah[NU], al[NU];
 #pragma unroll
@@ -212,6 +213,12 @@ __global__ __launch_bounds__(512) void km_assign(const uint16_t* __restrict__ v,
                     bi[tt] = better ? c0 + 16 * ct + 4 * g + i : bi[tt];
                 }
             }
+        };
+        if (c0 + KT <= k) {
+#pragma unroll
+            for (int ct = 0; ct < KT / 16; ct++) ctile(ct);
+        } else {
+            for (int ct = 0; ct < KT / 16 && c0 + 16 * ct < k; ct++) ctile(ct);
         }
         if (tile + 1 < ntile) {
 #pragma unroll

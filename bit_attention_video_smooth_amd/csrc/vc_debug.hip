@@ -18,7 +18,7 @@ __global__ void debug_expcast_kernel(const float* __restrict__ S, const float* _
 
 __global__ void debug_e4m3_kernel(const float* __restrict__ x, int64_t n, uint8_t* __restrict__ out) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) out[i] = (uint8_t)e4m3_rne(x[i]);
+    if (i < n) out[i] = (uint8_t)(e4m3_pk2<false>(x[i], 0.0f, 0u) & 0xFFu);
 }
 
 // one wave per tile: c = A B^T with A, B [16][128] E4M3 codes

@@ -28,26 +28,24 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 }
 
 // OCP E4M3FN (sign, 4 exponent bits with bias 7, 3 mantissa bits; 0x7E = 448
-// is the largest finite code), saturating round-to-nearest-even, written from
-// the format definition.  Finite inputs only.
-__device__ __forceinline__ uint32_t e4m3_rne(float x) {
-    uint32_t u = __float_as_uint(x);
-    uint32_t s = (u >> 24) & 0x80u;
-    uint32_t a = u & 0x7FFFFFFFu;
-    uint32_t code;
-    if (a >= 0x43E00000u) {  // |x| >= 448
-        code = 0x7Eu;
-    } else if (a < 0x3C800000u) {  // |x| < 2^-6: subnormal grid of step 2^-9
-        code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);  // 0..8, exact scaling
-    } else {
-        uint32_t e = (a >> 23) - 120u;  // fp32 biased exponent -> E4M3 biased exponent
-        uint32_t q = (a >> 20) & 7u;
-        uint32_t rem = a & 0xFFFFFu;
-        uint32_t up = (rem > 0x80000u) | ((rem == 0x80000u) & (q & 1u));
-        code = ((e << 3) | q) + up;  // a carry out of q bumps the exponent
-        code = code > 0x7Eu ? 0x7Eu : code;
-    }
-    return s | code;
+// is the largest finite code), saturating round-to-nearest-even, on the
+// hardware conversion: v_cvt_pk_fp8_f32 rounds to nearest even into E4M3FN
+// (checked against the format's definition on every fp32 exponent and
+// leading-mantissa pattern up to 450 in magnitude, both signs, ties
+// included); the inputs are first clamped to +-448, which is where
+// round-to-nearest already lands every finite value below 464, so the result
+// saturates instead of overflowing.  Two values go into
+// bytes 0, 1 (HI = false) or 2, 3 (HI = true) of `old`.  Finite inputs only.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3_pk2(float a, float b, uint32_t old) {
+    a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+    b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HI);
+}
+
+// four values -> one dword of E4M3 codes, byte i = code of x_i
+__device__ __forceinline__ uint32_t e4m3_pk4(float x0, float x1, float x2, float x3) {
+    return e4m3_pk2<true>(x2, x3, e4m3_pk2<false>(x0, x1, 0u));
 }
 
 // ExpCast-FP8: y = fma(S, c8, krow), then v_cvt_pk_u8_f32, which rounds to

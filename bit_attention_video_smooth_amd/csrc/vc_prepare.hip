@@ -146,12 +146,11 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(const uint16_t* __restric
 #pragma unroll
     for (int j = 0; j < NCH; j++) {
         const int ci = t + 256 * j, row = ci / CPR, cc = ci % CPR;
-        uint32_t lo = 0, hi = 0;
+        float y[8];
 #pragma unroll
-        for (int e = 0; e < 4; e++) {
-            lo |= e4m3_rne(__fmul_rn(vals[j][e], inv)) << (8 * e);
-            hi |= e4m3_rne(__fmul_rn(vals[j][4 + e], inv)) << (8 * e);
-        }
+        for (int e = 0; e < 8; e++) y[e] = __fmul_rn(vals[j][e], inv);
+        const uint32_t lo = e4m3_pk4(y[0], y[1], y[2], y[3]);
+        const uint32_t hi = e4m3_pk4(y[4], y[5], y[6], y[7]);
         *reinterpret_cast<uint2*>(cb + (size_t)row * D + cc * 8) = make_uint2(lo, hi);
     }
 }
@@ -224,16 +223,13 @@ __global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict
         uint32_t w[4];
 #pragma unroll
         for (int e = 0; e < 4; e++) {
-            uint32_t acc = 0;
+            float x[4];
 #pragma unroll
             for (int y = 0; y < 4; y++) {
-                const int pos = part * KPT + q * 16 + e * 4 + y;
-                const int kk = vkey_of_slot(pos);
-                uint32_t code = 0;
-                if (kk < n) code = e4m3_rne(__fmul_rn(__fsub_rn(T[c][kk], mu), inv));
-                acc |= code << (8 * y);
+                const int kk = vkey_of_slot(part * KPT + q * 16 + e * 4 + y);
+                x[y] = kk < n ? __fmul_rn(__fsub_rn(T[c][kk], mu), inv) : 0.0f;  // padded slots: code 0
             }
-            w[e] = acc;
+            w[e] = e4m3_pk4(x[0], x[1], x[2], x[3]);
         }
         *reinterpret_cast<uint4*>(out + part * KPT + q * 16) = make_uint4(w[0], w[1], w[2], w[3]);
     }

@@ -157,10 +157,14 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(const uint16_t* __restric
 
 // ------------------------------------------------------------------------
 // a6: V-Smooth residual quantisation of one permuted 128-token block.
-// Exact block mean per channel (fp64 sum, rounded once), residual in fp32,
-// per-channel scale, E4M3 codes written block-transposed in PV slot order.
-// Grid (nb, B*H), 256 threads.
-// ------------------------------------------------------------------------
+// Wave w holds keys 32 w .. 32 w + 31 of the block (slots in permuted order)
+// and lane l holds channels CPL l .. CPL l + CPL - 1 (CPL = D / 64), so each
+// key's row is one coalesced load across the wave and the values stay in
+// registers: per-channel fp64 sums (exact for bf16 inputs, so the order does
+// not matter) and maxima are combined over the four waves through LDS; the
+// codes are written channel-major in the slot order of the attention
+// kernel's P V operand, where the 32 keys of wave w fill slots
+// 32 b + 8 w .. 32 b + 8 w + 7 of every channel row (b = 0..3).
 template <int D>
 __global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict__ v,
                                                       const int32_t* __restrict__ perm,
@@ -168,70 +172,78 @@ __global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict
                                                       float* __restrict__ vscale,
                                                       float* __restrict__ vmean, int L, int nb,
                                                       int mode) {
-    constexpr int CPR = D / 8;
-    constexpr int NCH = BLK * CPR / 256;
-    constexpr int TPC = 256 / D;         // threads per channel
-    constexpr int KPT = BLK / TPC;       // keys (slots) per thread
-    __shared__ float T[D][BLK + 1];
+    constexpr int CPL = D / 64;  // channels per lane
+    constexpr int KW = BLK / 4;  // keys per wave
+    __shared__ double psum[4][D];
+    __shared__ float pmax[4][D];
     const int b = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63;
     const int i0 = b * BLK;
     const int n = min(BLK, L - i0);
-    const uint16_t* vb = v + (size_t)bh * L * D;
+    const uint16_t* vb = v + (size_t)bh * L * D + CPL * lane;
+    const int32_t* pb = perm + (size_t)bh * L + i0 + KW * w;
+    const int nw = min(KW, max(0, n - KW * w));  // valid keys of this wave
+    float x[KW][CPL];
 #pragma unroll
-    for (int j = 0; j < NCH; j++) {
-        const int ci = t + 256 * j, row = ci / CPR, cc = ci % CPR;
-        float f[8];
-        if (row < n) {
-            const int src = perm[(size_t)bh * L + i0 + row];
-            uint4 w = *reinterpret_cast<const uint4*>(vb + (size_t)src * D + cc * 8);
-            uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                f[2 * e] = bf16_to_f32(ww[e] & 0xFFFFu);
-                f[2 * e + 1] = bf16_to_f32(ww[e] >> 16);
+    for (int i = 0; i < KW; i++) {
+        if (i < nw) {
+            const int src = pb[i];  // uniform across the wave
+            if (CPL == 2) {
+                const uint32_t u = *reinterpret_cast<const uint32_t*>(vb + (size_t)src * D);
+                x[i][0] = bf16_to_f32(u & 0xFFFFu);
+                x[i][CPL - 1] = bf16_to_f32(u >> 16);
+            } else {
+                x[i][0] = bf16_to_f32(vb[(size_t)src * D]);
             }
         } else {
 #pragma unroll
-            for (int e = 0; e < 8; e++) f[e] = 0.0f;
+            for (int e = 0; e < CPL; e++) x[i][e] = 0.0f;
         }
+    }
 #pragma unroll
-        for (int e = 0; e < 8; e++) T[cc * 8 + e][row] = f[e];
+    for (int e = 0; e < CPL; e++) {
+        double s4[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+        for (int i = 0; i < KW; i++) s4[i % 4] += (double)x[i][e];  // padded keys add 0
+        psum[w][CPL * lane + e] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
     }
     __syncthreads();
-    const int c = t / TPC, part = t % TPC;
-    double sum = 0.0;
-    for (int kk = part * KPT; kk < part * KPT + KPT; kk++)
-        if (kk < n) sum += (double)T[c][kk];
+    float mu[CPL], inv[CPL];
 #pragma unroll
-    for (int o = 1; o < TPC; o <<= 1) sum += __shfl_xor(sum, o);
-    const float mu = (float)(sum / (double)n);
-    float amax = 0.0f;
-    for (int kk = part * KPT; kk < part * KPT + KPT; kk++)
-        if (kk < n) amax = fmaxf(amax, fabsf(__fsub_rn(T[c][kk], mu)));
+    for (int e = 0; e < CPL; e++) {
+        const int c = CPL * lane + e;
+        mu[e] = (float)((((psum[0][c] + psum[1][c]) + psum[2][c]) + psum[3][c]) / (double)n);
+        float am = 0.0f;
 #pragma unroll
-    for (int o = 1; o < TPC; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
-    float s, inv;
-    group_scale(amax, mode, s, inv);
-    const size_t gi = ((size_t)bh * nb + b) * D + c;
-    if (part == 0) {
-        vmean[gi] = mu;
-        vscale[gi] = s;
+        for (int i = 0; i < KW; i++)
+            if (i < nw) am = fmaxf(am, fabsf(__fsub_rn(x[i][e], mu[e])));
+        pmax[w][c] = am;
     }
-    uint8_t* out = codes + gi * BLK;
+    __syncthreads();
 #pragma unroll
-    for (int q = 0; q < KPT / 16; q++) {
-        uint32_t w[4];
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-            float x[4];
-#pragma unroll
-            for (int y = 0; y < 4; y++) {
-                const int kk = vkey_of_slot(part * KPT + q * 16 + e * 4 + y);
-                x[y] = kk < n ? __fmul_rn(__fsub_rn(T[c][kk], mu), inv) : 0.0f;  // padded slots: code 0
-            }
-            w[e] = e4m3_pk4(x[0], x[1], x[2], x[3]);
+    for (int e = 0; e < CPL; e++) {
+        const int c = CPL * lane + e;
+        const float A = fmaxf(fmaxf(pmax[0][c], pmax[1][c]), fmaxf(pmax[2][c], pmax[3][c]));
+        float s;
+        group_scale(A, mode, s, inv[e]);
+        const size_t gi = ((size_t)bh * nb + b) * D + c;
+        if (w == 0) {
+            vmean[gi] = mu[e];
+            vscale[gi] = s;
         }
-        *reinterpret_cast<uint4*>(out + part * KPT + q * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+        uint8_t* out = codes + gi * BLK + 8 * w;
+#pragma unroll
+        for (int bb = 0; bb < 4; bb++) {
+            // slots 32 bb + 8 w + j hold keys 32 w + 16 (j / 4) + 4 bb + j % 4
+            float y[8];
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                const int i = 16 * (j / 4) + 4 * bb + j % 4;
+                y[j] = i < nw ? __fmul_rn(__fsub_rn(x[i][e], mu[e]), inv[e]) : 0.0f;  // padded slots: code 0
+            }
+            *reinterpret_cast<uint2*>(out + 32 * bb) =
+                make_uint2(e4m3_pk4(y[0], y[1], y[2], y[3]), e4m3_pk4(y[4], y[5], y[6], y[7]));
+        }
     }
 }
 

@@ -150,7 +150,8 @@ def main():
     total_ms = start.elapsed_time(stop)
     ms_step = total_ms / args.steps
     prep_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    attn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    attn_each = [e[1].elapsed_time(e[2]) for e in evs]
+    attn_ms = float(np.mean(attn_each))
     print("step %.3f ms (prepare %.3f, attention %.3f)" % (ms_step, prep_ms, attn_ms), file=sys.stderr, flush=True)
     if args.v_scale_mode not in (0, 1):
         sys.exit("--v-scale-mode must be 0 or 1")
@@ -264,7 +265,10 @@ def main():
                                % (cfg.name, B, H, L, d, nb, ), "B": B, "H": H, "L": L, "d": d,
                    "v_scale_mode": args.v_scale_mode},
         "frac_fp8_peak_step": flop / ms_step / 1e9 / FP8_PEAK_TFLOPS,
-        "attention": {"ms": attn_ms, "tflops": attn_tflops, "frac_fp8_peak": attn_tflops / FP8_PEAK_TFLOPS},
+        "attention": {"ms": attn_ms, "tflops": attn_tflops, "frac_fp8_peak": attn_tflops / FP8_PEAK_TFLOPS,
+                      "ms_median": float(np.median(attn_each)), "ms_min": float(np.min(attn_each))},
+        "device": {"name": torch.cuda.get_device_name(0),
+                   "compute_units": torch.cuda.get_device_properties(0).multi_processor_count},
         "attention_other_v_scale_mode": {"v_scale_mode": 1 - args.v_scale_mode, "ms": other_ms,
                                          "tflops": flop / other_ms / 1e9,
                                          "frac_fp8_peak": flop / other_ms / 1e9 / FP8_PEAK_TFLOPS},

@@ -8,12 +8,13 @@
 // score tile computed transposed (S^T = K Q^T, v_mfma_f32_16x16x32_bf16) so
 // that each lane holds 32 scores of one query, and the bf16 probabilities a
 // lane produces are its B operand of O^T = V^T P^T; the row sums are a
-// product of a ones tile with those same bf16 probabilities.  K tiles and V
-// rows arrive by direct global->LDS copies one block ahead (K into a
-// double-buffered, XOR-swizzled stage; V rows into one staging buffer); after
-// the copies land, the V rows are transposed LDS->LDS into the next stage's
-// [channel][key-slot] layout between two workgroup barriers, so no copy
-// sits in registers across a block.
+// product of a ones tile with those same bf16 probabilities.  K and V rows
+// arrive row-major by direct global->LDS copies one block ahead into a
+// two-stage ring (16-byte chunks XOR-swizzled per row), and the V^T operand
+// of each product is read straight from the V rows with the gfx950 LDS
+// transpose read (ds_read_b64_tr_b16): a 16-lane group hands in 16 pieces
+// of 4 channels and gets back, per lane, one channel of 4 consecutive keys.
+// One workgroup barrier per block.
 #include "vc_device.hpp"
 #include "vc_internal.hpp"
 #include "vc_lds.hpp"
@@ -28,14 +29,13 @@ constexpr int QW = 32;
 template <int D>
 struct Bf16Tile {
     static constexpr int K_TILE = BLK * D * 2;  // [128 keys][D] bf16
-    static constexpr int V_TILE = D * BLK * 2;  // [D][128 slots] bf16
+    static constexpr int V_TILE = BLK * D * 2;  // [128 keys][D] bf16
     static constexpr int STAGE = K_TILE + V_TILE;
-    static constexpr int LDS = 2 * STAGE + K_TILE;  // two stages + V-row staging
+    static constexpr int LDS = 2 * STAGE;       // two stages
     static constexpr int KCH = D / 8;           // 16-byte chunks per K (or V) row
     static constexpr int NU = D / 32;           // 32-wide slices of the head dim
-    static constexpr int PIECES = K_TILE / 1024;  // 1 KiB pieces of a K tile (or of the V rows)
+    static constexpr int PIECES = K_TILE / 1024;  // 1 KiB pieces of a K (or V) tile
     static constexpr int PPW = PIECES / NW;       // pieces of each per wave
-    static constexpr int VUNITS = (BLK / 4) * (D / 8);  // (4 keys x 8 channels) transpose units
 };
 
 __device__ __forceinline__ v4f mfma_bf16(const v8bf& a, const v8bf& b, const v4f& c) {
@@ -48,25 +48,24 @@ __device__ __forceinline__ v8bf as_bf(u32x4 x) {
     return r;
 }
 
-// Swizzle of the 16-byte chunks of a K row: conflict-free 16-byte operand
-// reads need distinct positions modulo 128 bytes per 8 lanes and modulo 256
-// bytes per 16 lanes (rows r = 0..15 of a tile go to lanes 0..15).
+// Swizzle of the 16-byte chunks of a K or V row: conflict-free 16-byte
+// operand reads need distinct positions modulo 128 bytes per 8 lanes and
+// modulo 256 bytes per 16 lanes (rows r = 0..15 of a tile go to lanes
+// 0..15); the transpose reads of V (16 consecutive keys, two chunks each)
+// then also fall on distinct positions at D = 128.
 template <int D>
 __device__ __forceinline__ int kswz(int r) {
     return D == 128 ? (r & 15) : ((r & 7) ^ ((r >> 3) & 1));
 }
 
-// V^T row (channel c, 256 bytes = 16 chunks of 8 key slots) swizzle.
-__device__ __forceinline__ int vswz(int c) { return (c ^ (c >> 3)) & 15; }
-
-// Copies of block kb: K rows into `sk` (LDS chunk p of row r holds chunk
-// p ^ kswz(r) of the key row) and V rows, unswizzled, into `stg`.  Wave w
-// takes 1 KiB pieces w, w + NW, ... of each.  Rows past L read as zeros.
+// Copies of block kb into `stage`: K rows, then V rows (LDS chunk p of row r
+// holds chunk p ^ kswz(r) of the row).  Wave w takes 1 KiB pieces w,
+// w + NW, ... of each.  Rows past L read as zeros.
 template <int D>
 struct Bf16Loader {
     using T = Bf16Tile<D>;
     v4si rk, rv;
-    uint32_t koff[T::PPW], voff[T::PPW];
+    uint32_t off[T::PPW];
     int w;
     __device__ __forceinline__ Bf16Loader(const AttnBf16Args& a, int bh, int w_, int lane) : w(w_) {
         const uint32_t head = (uint32_t)((size_t)a.L * D * 2);
@@ -76,43 +75,40 @@ struct Bf16Loader {
         for (int i = 0; i < T::PPW; i++) {
             const int p = (i * NW + w) * 64 + lane;  // 16-byte chunk of the tile
             const int r = p / T::KCH, cp = p % T::KCH;
-            koff[i] = (uint32_t)(r * D * 2 + ((cp ^ kswz<D>(r)) << 4));
-            voff[i] = (uint32_t)(p * 16);
+            off[i] = (uint32_t)(r * D * 2 + ((cp ^ kswz<D>(r)) << 4));
         }
     }
-    __device__ __forceinline__ void issue(lds_u8* sk, lds_u8* stg, int kb) const {
+    __device__ __forceinline__ void issue(lds_u8* stage, int kb) const {
         const uint32_t base = (uint32_t)kb * T::K_TILE;
 #pragma unroll
-        for (int i = 0; i < T::PPW; i++) lds_dma16(rk, sk + (i * NW + w) * 1024, koff[i], base);
+        for (int i = 0; i < T::PPW; i++) lds_dma16(rk, stage + (i * NW + w) * 1024, off[i], base);
 #pragma unroll
-        for (int i = 0; i < T::PPW; i++) lds_dma16(rv, stg + (i * NW + w) * 1024, voff[i], base);
+        for (int i = 0; i < T::PPW; i++) lds_dma16(rv, stage + T::K_TILE + (i * NW + w) * 1024, off[i], base);
     }
 };
 
-// V rows of one block (staging, [128 keys][D]) -> V^T tile [D][128 slots]:
-// thread t moves 4 keys x 8 channels; channel c's key slot for key k is the
-// B-operand order of the products (32-key slice u, 16-key half h, 4-key group).
+// V^T operand (A of O^T = V^T P^T) of channel tile ct and 32-key slice u from
+// the row-major V rows: lane (col, g) gets channel 16 ct + col of keys
+// 32 u + 4 g + j (first read) and 32 u + 16 + 4 g + j (second), j = 0..3 --
+// the key order of the lane's bf16 probabilities.  For the transpose read,
+// lane p of each 16-lane group supplies the 8-byte piece of key
+// (4 g + p / 4) + 32 u (+ 16) holding channels 16 ct + 4 (p % 4) .. + 3.
 template <int D>
-__device__ __forceinline__ void transpose_v(const lds_u8* stg, lds_u8* sV, int t) {
-    using T = Bf16Tile<D>;
-    if (t >= T::VUNITS) return;
-    const int kg = t / (D / 8), cc = t % (D / 8);
-    u32x4 r[4];
-#pragma unroll
-    for (int j = 0; j < 4; j++) r[j] = *reinterpret_cast<const VC_LDS u32x4*>(stg + (4 * kg + j) * (D * 2) + cc * 16);
-    const int k0 = 4 * kg;
-    const int u = k0 / 32, h = (k0 % 32) / 16, gq = (k0 % 16) / 4;
-    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-#pragma unroll
-    for (int e = 0; e < 8; e++) {
-        const int c = cc * 8 + e;
-        const int sh = (e & 1) * 16;
-        const uint32_t k0v = (r[0][e >> 1] >> sh) & 0xFFFFu, k1v = (r[1][e >> 1] >> sh) & 0xFFFFu;
-        const uint32_t k2v = (r[2][e >> 1] >> sh) & 0xFFFFu, k3v = (r[3][e >> 1] >> sh) & 0xFFFFu;
-        const int chunk = (4 * u + gq) ^ vswz(c);
-        const u32x2 val = {k0v | (k1v << 16), k2v | (k3v << 16)};
-        *reinterpret_cast<VC_LDS u32x2*>(sV + c * (BLK * 2) + chunk * 16 + h * 8) = val;
-    }
+__device__ __forceinline__ v8bf v_operand_tr(const lds_u8* sV, int ct, int u, int g, int p) {
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    const int kr = 4 * g + (p >> 2);                 // key within the 16-key half
+    const int chunk = (2 * ct + ((p & 3) >> 1)) ^ kswz<D>(kr);  // (32 u + 16 h + kr) has the swizzle of kr
+    const int off = (chunk << 4) | ((p & 1) << 3);
+    const lds_u8* r0 = sV + (32 * u + kr) * (D * 2) + off;
+    const lds_u8* r1 = r0 + 16 * (D * 2);
+    const v4s a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((VC_LDS v4s*)r0);
+    const v4s b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((VC_LDS v4s*)r1);
+    u32x4 x;
+    x[0] = (uint32_t)(uint16_t)a[0] | ((uint32_t)(uint16_t)a[1] << 16);
+    x[1] = (uint32_t)(uint16_t)a[2] | ((uint32_t)(uint16_t)a[3] << 16);
+    x[2] = (uint32_t)(uint16_t)b[0] | ((uint32_t)(uint16_t)b[1] << 16);
+    x[3] = (uint32_t)(uint16_t)b[2] | ((uint32_t)(uint16_t)b[3] << 16);
+    return as_bf(x);
 }
 
 // Running max and bf16 probabilities p = 2^(S c - m') of one block for both
@@ -184,7 +180,6 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnBf16Args a) {
     using T = Bf16Tile<D>;
     __shared__ __attribute__((aligned(16))) uint8_t lds_[T::LDS];
     lds_u8* lds = (lds_u8*)lds_;
-    lds_u8* stg = lds + 2 * T::STAGE;
     const int nwg = a.BH * a.nqt;
     const int pid = xcd_remap(blockIdx.x, nwg);
     const int bh = pid / a.nqt, qtile = pid % a.nqt;
@@ -218,10 +213,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnBf16Args a) {
     const float c = a.C0;
     const Bf16Loader<D> ld(a, bh, w, lane);
 
-    ld.issue(lds, stg, 0);
+    ld.issue(lds, 0);
     wait_vmcnt<0>();
-    block_barrier();
-    transpose_v<D>(stg, lds + T::K_TILE, t);
     block_barrier();
 
     for (int kb = 0; kb < nkb; kb++) {
@@ -229,7 +222,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnBf16Args a) {
         const lds_u8* sV = sK + T::K_TILE;
         lds_u8* nxt = lds + ((kb + 1) & 1) * T::STAGE;
         const bool more = kb + 1 < nkb;
-        if (more) ld.issue(nxt, stg, kb + 1);  // both freed before the last barrier
+        if (more) ld.issue(nxt, kb + 1);  // the stage of block kb - 1, left before the last barrier
 
         v4f S[2][8];
 #pragma unroll
@@ -295,29 +288,23 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(AttnBf16Args a) {
         }
 #pragma unroll
         for (int ct = 0; ct < NCT; ct++) {
-            const int cr = 16 * ct + col;
-            const lds_u8* row = sV + cr * (BLK * 2);
 #pragma unroll
             for (int u = 0; u < 4; u++) {
-                const v8bf vop = as_bf(*reinterpret_cast<const VC_LDS u32x4*>(row + (((4 * u + g) ^ vswz(cr)) << 4)));
+                const v8bf vop = v_operand_tr<D>(sV, ct, u, g, col);
 #pragma unroll
                 for (int qt = 0; qt < 2; qt++) O[qt][ct] = mfma_bf16(vop, pop[qt][u], O[qt][ct]);
             }
         }
         // V operand reads one channel tile ahead of the products
         __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);  // row sums
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
         for (int ct = 0; ct < NCT; ct++) {
-            if (ct + 1 < NCT) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+            if (ct + 1 < NCT) __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
         }
-        if (more) {
-            // block kb + 1 has landed (K in its stage, V rows in the staging
-            // buffer); transpose the V rows into its stage
+        if (more) {  // block kb + 1 has landed in its stage
             wait_vmcnt<0>();
-            block_barrier();
-            transpose_v<D>(stg, nxt + T::K_TILE, t);
             block_barrier();
         }
     }

@@ -80,8 +80,8 @@ def attention(prep: Prepared, *, z_off=8, out_dtype=torch.float32, out=None, ski
     if out is None:
         out = torch.empty((B, H, L, d), dtype=out_dtype, device=prep.q8.device)
     od = 1 if out.dtype == torch.bfloat16 else 0
-    _lib.vc_attention_fwd(_lib.shape_of(B, H, L, d), _lib.vc_attn_params(z_off, od, skip_lambda, prob_cast), prep.c(),
-                          out, stream)
+    params = _lib.vc_attn_params(z_off, od, skip_lambda, prob_cast)
+    _lib.vc_attention_fwd(_lib.shape_of(B, H, L, d), params, prep.c(), out, stream)
     return out
 
 
@@ -93,8 +93,8 @@ def attention_dump(prep: Prepared, bh: int, q_tile: int, *, z_off=8, skip_lambda
     out = torch.empty((B, H, L, d), dtype=torch.float32, device=dev)
     s = torch.zeros((256, Lp), dtype=torch.float32, device=dev)
     p = torch.zeros((256, Lp), dtype=torch.uint8, device=dev)
-    _lib.vc_attention_fwd_dump(_lib.shape_of(B, H, L, d), _lib.vc_attn_params(z_off, 0, skip_lambda, prob_cast), prep.c(),
-                               out, bh, q_tile, s, p, stream)
+    params = _lib.vc_attn_params(z_off, 0, skip_lambda, prob_cast)
+    _lib.vc_attention_fwd_dump(_lib.shape_of(B, H, L, d), params, prep.c(), out, bh, q_tile, s, p, stream)
     return out, s, p
 
 

@@ -181,7 +181,8 @@ int vc_debug_expcast(const float* S, const float* c8, const float* krow, int64_t
                      uint8_t* bytes, hipStream_t stream);
 
 /* E4M3 encoding alone, with the device function the preprocessing kernels
- * use: saturating round-to-nearest-even (OCP E4M3FN, bias 7). */
+ * use: saturating round-to-nearest-even (OCP E4M3FN, bias 7), i.e. the
+ * hardware conversion on inputs clamped to +-448. */
 int vc_debug_e4m3_encode(const float* x, int64_t n, uint8_t* codes, hipStream_t stream);
 
 /* One FP8 matrix-core product per 16x16 tile: for t < n_tiles,

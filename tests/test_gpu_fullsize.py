@@ -96,5 +96,6 @@ def test_full_size_kmeans_objective(api, cfg_idx):
     nb = (L + 127) // 128
     b, h = divmod(B * H - 1, H)
     J = oracle.kmeans(v[b, h], nb, 8, oracle.head_seed(cfg_idx, b, h, H))[2]
-    print("%s k-means head %d: gpu J %.7g oracle J %.7g ratio %.6f" % (cfg.name, B * H - 1, obj[b, h], J, obj[b, h] / J))
+    print("%s k-means head %d: gpu J %.7g oracle J %.7g ratio %.6f"
+          % (cfg.name, B * H - 1, obj[b, h], J, obj[b, h] / J))
     assert abs(obj[b, h] / J - 1) <= 0.01

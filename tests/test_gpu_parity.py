@@ -93,7 +93,8 @@ def test_fp8_matrix_core_sum_error_bound(api):
     a = rng.choice(codes, size=(n, 16, 128)).astype(np.uint8)
     b = rng.choice(codes, size=(n, 16, 128)).astype(np.uint8)
     # narrow range: codes 0x30..0x47 (|x| in [0.5, 4)), every partial sum exact in fp32
-    an = rng.integers(0x30, 0x48, (n, 16, 128)).astype(np.uint8) | (rng.integers(0, 2, (n, 16, 128)).astype(np.uint8) << 7)
+    sign = rng.integers(0, 2, (n, 16, 128)).astype(np.uint8) << 7
+    an = rng.integers(0x30, 0x48, (n, 16, 128)).astype(np.uint8) | sign
     bn = rng.integers(0x30, 0x48, (n, 16, 128)).astype(np.uint8)
     for (x, y, exact_expected) in ((a, b, False), (an, bn, True)):
         c = api.mfma_fp8(torch.from_numpy(x).cuda(), torch.from_numpy(y).cuda()).cpu().numpy()
@@ -134,7 +135,8 @@ def test_prepare_bit_exact(api, shape, v_mode, smooth_k):
                 x, y = g[n][b, h], o[n]
                 if not np.array_equal(x.view(np.uint8), y.view(np.uint8)):
                     idx = np.argwhere(x != y)[:5]
-                    pytest.fail("%s mismatch at %s: gpu %s oracle %s" % (n, idx.tolist(), x[tuple(idx.T)], y[tuple(idx.T)]))
+                    pytest.fail("%s mismatch at %s: gpu %s oracle %s"
+                                % (n, idx.tolist(), x[tuple(idx.T)], y[tuple(idx.T)]))
 
 
 # ------------------------------------------------------------ attention ----

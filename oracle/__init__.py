@@ -72,6 +72,8 @@ def lib():
             L.vco_c0.argtypes = [i32]
             L.vco_attention_rows.argtypes = [i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P,
                                              i32, i32, P, P, P, P, P, f32]
+            L.vco_sage_prepare_head.argtypes = [P, P, P, i32, i32, i32, i32, P, P, P, P, P, P]
+            L.vco_sage_rows.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P, P, i32, i32, P, P, P, P]
             L.vco_num_threads.restype = i32
             L.vco_prepare.argtypes = [i32, i32, i32, i32, i32, i32, u64, i32, i32, P, P, P, P,
                                       P, P, P, P, P, P, P, P, P]
@@ -307,6 +309,57 @@ def attention_exact_blockwise(qf, kf_perm, v_perm, v_mean, skip_lambda: float = 
                              _p(qf), _p(kf), _p(rf), 0, L, _p(out), None, None, None, None,
                              skip_threshold(skip_lambda))
     return out
+
+
+# --------------------------------------------------------------------------
+# SAGE-style baseline (TensorRT-LLM blog, "Quantized Attention": QK^T in
+# INT8 or FP8, PV in FP8, q/k/v block sizes 1/16/1 with the V scale per
+# channel).  The readings where the blog is silent are listed in vc_oracle.c.
+# --------------------------------------------------------------------------
+
+SAGE_QK = {"int8": 1, "fp8": 0}
+
+
+def sage_prepare_head(q, k, v, qk_dtype: str = "int8", smooth_k: int = 1):
+    """One head, sequence order.  q, k, v: bf16 bits [L, d].  Returns q8, k8
+    [Lp, d] (INT8 two's complement or E4M3 bytes), v8 [nb, d, 128] E4M3
+    (natural slot order), q_scale [Lp], k_scale [Lp/16], v_scale [d]."""
+    q, k, v = (_c(a, np.uint16) for a in (q, k, v))
+    L, d = q.shape
+    nb = nblocks(L)
+    Lp = nb * BLK
+    o = dict(q8=np.empty((Lp, d), np.uint8), k8=np.empty((Lp, d), np.uint8),
+             v8=np.empty((nb, d, BLK), np.uint8), q_scale=np.empty(Lp, np.float32),
+             k_scale=np.empty(Lp // 16, np.float32), v_scale=np.empty(d, np.float32))
+    lib().vco_sage_prepare_head(_p(q), _p(k), _p(v), L, d, SAGE_QK[qk_dtype], smooth_k,
+                                _p(o["q8"]), _p(o["k8"]), _p(o["v8"]), _p(o["q_scale"]),
+                                _p(o["k_scale"]), _p(o["v_scale"]))
+    return o
+
+
+def sage_attention_head(prep: dict, L: int, qk_dtype: str = "int8", z_off: int = 8, prob_cast: int = 1,
+                        rows=None, want_bytes=False, scores=None):
+    """SAGE-style attention for one head from sage_prepare_head() output.
+    Returns O [r1-r0, d] fp32 (with want_bytes also the P bytes and scores
+    [r1-r0, Lp]).  scores: optional fp32 [r1-r0, Lp] in place of the exact
+    Q8 K8^T sums.  prob_cast 1: exp-then-cast P bytes; 0: ExpCast."""
+    if prob_cast not in (0, 1):
+        raise ValueError("prob_cast must be 0 or 1")
+    q8, k8, v8 = (_c(prep[n], np.uint8) for n in ("q8", "k8", "v8"))
+    qs, ks, vs = (_c(prep[n], np.float32) for n in ("q_scale", "k_scale", "v_scale"))
+    d = q8.shape[1]
+    Lp = k8.shape[0]
+    r0, r1 = (0, L) if rows is None else rows
+    out = np.empty((r1 - r0, d), np.float32)
+    by = np.empty((r1 - r0, Lp), np.uint8) if want_bytes else None
+    S = np.empty((r1 - r0, Lp), np.float32) if want_bytes else None
+    sin = None
+    if scores is not None:
+        sin = _c(scores, np.float32)
+        assert sin.shape == (r1 - r0, Lp)
+    lib().vco_sage_rows(prob_cast, SAGE_QK[qk_dtype], L, d, z_off, _p(q8), _p(k8), _p(v8), _p(qs), _p(ks),
+                        _p(vs), r0, r1, _p(out), _p(by), _p(S), _p(sin))
+    return (out, by, S) if want_bytes else out
 
 
 def num_threads() -> int:

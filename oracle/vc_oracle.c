@@ -550,6 +550,215 @@ void vco_attention_rows(int mode, int L, int d, int z_off,
 }
 
 /* ------------------------------------------------------------------------ */
+/* SAGE-style quantised attention, the baseline of [TRT] "Quantized          */
+/* Attention": five settings fix it -- QK^T in INT8 (the blog's choice) or   */
+/* FP8, PV in FP8 E4M3, one Q scale per query token (q block size 1), one K  */
+/* scale per 16 consecutive keys (k block size 16), and one V scale per      */
+/* channel of a head, taken over all of its tokens (v block size 1).         */
+/* Readings where the blog is silent:                                       */
+/*  - a scale is amax / qmax with qmax = 127 (INT8) or 448 (E4M3), and the   */
+/*    same zero rule as above (amax < 2^-100: scale 0, codes 0);            */
+/*  - INT8 codes: round to nearest, ties to even, of fp32(x * inv), clamped  */
+/*    to [-127, 127], stored as two's-complement bytes;                     */
+/*  - K is smoothed by its per-channel mean when smooth_k is set (the       */
+/*    SageAttention line smooths K; the softmax does not change);           */
+/*  - tokens stay in sequence order and there are no block means;           */
+/*  - the score coefficient of query i and key j is                         */
+/*    c_ij = fp32(fp32(s_q,i C0) s_k,j/16);                                  */
+/*  - P bytes come from the exp-then-cast path (prob_cast 1, the FP8 path    */
+/*    of the SageAttention line) or from ExpCast (prob_cast 0), with the     */
+/*    same running maximum and z_off as the V-Smooth path.                  */
+/* ------------------------------------------------------------------------ */
+
+static void vco_sage_scale(float A, float qmax, float* s, float* inv)
+{
+    if (!((double)A >= ldexp(1.0, -100))) { *s = 0.0f; *inv = 0.0f; return; }
+    volatile float num = qmax;
+    *s = A / num;
+    *inv = num / A;
+}
+
+static inline uint8_t vco_i8_code(float x, float inv)
+{
+    volatile float y = x * inv; /* one IEEE single multiply */
+    double a = vco_rne(fabs((double)y));
+    if (a > 127.0) a = 127.0;
+    int v = (y < 0.0f) ? -(int)a : (int)a;
+    return (uint8_t)(int8_t)v;
+}
+
+static inline double vco_i8_value(uint8_t b) { return (double)(int8_t)b; }
+
+/* One head.  q,k,v: bf16 bits [L, d].  Outputs: q8 [Lp, d] and k8 [Lp, d]   */
+/* (INT8 or E4M3 codes, sequence order), v8 [nb, d, 128] E4M3 codes in       */
+/* natural slot order, q_scale [Lp], k_scale [Lp / 16], v_scale [d].  Padded  */
+/* tokens (>= L) get code 0 and scale 0 and take no part in any amax.       */
+void vco_sage_prepare_head(const uint16_t* q, const uint16_t* k, const uint16_t* v, int L, int d,
+                           int qk_int8, int smooth_k, uint8_t* q8, uint8_t* k8, uint8_t* v8,
+                           float* q_scale, float* k_scale, float* v_scale)
+{
+    int nb = (L + VCO_BLK - 1) / VCO_BLK;
+    int Lp = nb * VCO_BLK;
+    float qmax = qk_int8 ? 127.0f : 448.0f;
+    float* kbar = (float*)calloc((size_t)d, sizeof(float));
+    if (smooth_k) vco_k_mean(k, L, d, kbar);
+    float* buf = (float*)malloc(sizeof(float) * 16 * d);
+
+    /* Q: one scale per token */
+    for (int i = 0; i < Lp; i++) {
+        float A = 0.0f, s, inv;
+        for (int c = 0; c < d && i < L; c++) {
+            float t = fabsf(vco_bf16(q[(int64_t)i * d + c]));
+            if (t > A) A = t;
+        }
+        vco_sage_scale(A, qmax, &s, &inv);
+        q_scale[i] = (i < L) ? s : 0.0f;
+        for (int c = 0; c < d; c++) {
+            uint8_t code = 0;
+            if (i < L) {
+                float x = vco_bf16(q[(int64_t)i * d + c]);
+                code = qk_int8 ? vco_i8_code(x, inv) : vco_quant(x, inv);
+            }
+            q8[(int64_t)i * d + c] = code;
+        }
+    }
+
+    /* K: K' = fp32(K - kbar), one scale per 16 consecutive tokens */
+    for (int g = 0; g < Lp / 16; g++) {
+        float A = 0.0f, s, inv;
+        for (int r = 0; r < 16; r++) {
+            int i = 16 * g + r;
+            for (int c = 0; c < d; c++) {
+                volatile float t = (i < L) ? vco_bf16(k[(int64_t)i * d + c]) - kbar[c] : 0.0f;
+                buf[r * d + c] = t;
+                if (fabsf(t) > A) A = fabsf(t);
+            }
+        }
+        vco_sage_scale(A, qmax, &s, &inv);
+        k_scale[g] = s;
+        for (int r = 0; r < 16; r++) {
+            int i = 16 * g + r;
+            for (int c = 0; c < d; c++) {
+                uint8_t code = 0;
+                if (i < L) code = qk_int8 ? vco_i8_code(buf[r * d + c], inv) : vco_quant(buf[r * d + c], inv);
+                k8[(int64_t)i * d + c] = code;
+            }
+        }
+    }
+
+    /* V: one E4M3 scale per channel over the head's tokens */
+    for (int c = 0; c < d; c++) {
+        float A = 0.0f, s, inv;
+        for (int i = 0; i < L; i++) {
+            float t = fabsf(vco_bf16(v[(int64_t)i * d + c]));
+            if (t > A) A = t;
+        }
+        vco_sage_scale(A, 448.0f, &s, &inv);
+        v_scale[c] = s;
+        for (int b = 0; b < nb; b++)
+            for (int j = 0; j < VCO_BLK; j++) {
+                int i = b * VCO_BLK + j;
+                v8[((int64_t)b * d + c) * VCO_BLK + j] = (i < L) ? vco_quant(vco_bf16(v[(int64_t)i * d + c]), inv) : 0;
+            }
+    }
+    free(buf);
+    free(kbar);
+}
+
+/* Blockwise SAGE attention for query rows [r0, r1) of one head, from the    */
+/* output of vco_sage_prepare_head.  Per row i, for each 128-key block b in  */
+/* ascending order:                                                          */
+/*   S_j   = fp32(exact sum_c qhat_ic khat_jc)   (or S_in, as above)         */
+/*   c_j   = fp32(fp32(s_q,i C0) s_k,j/16)                                   */
+/*   t     = max over valid j of fp32(S_j c_j);  m' = max(m, t)             */
+/*   bytes = ExpCast(S_j, fp32(8 c_j), fp32(KB - 8 m'))       (prob_cast 0)  */
+/*         | E4M3(fp32(2^fmaf(S_j, c_j, fp32(z_off - m'))))   (prob_cast 1)  */
+/*   l_b   = sum_j decode(byte_j);  acc_c = fp32(exact sum_j p_j vhat_jc)    */
+/*   alpha = 2^(m - m') (0 on the first block)                              */
+/*   O     = alpha O + acc;  l = alpha l + l_b       (double)                */
+/* and the output is O_c s_v,c / l.  bytes_out / S_out as in                */
+/* vco_attention_rows (may be NULL).                                         */
+void vco_sage_rows(int prob_cast, int qk_int8, int L, int d, int z_off,
+                   const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                   const float* q_scale, const float* k_scale, const float* v_scale,
+                   int r0, int r1, float* out, uint8_t* bytes_out, float* S_out, const float* S_in)
+{
+    int nb = (L + VCO_BLK - 1) / VCO_BLK;
+    int64_t Lp = (int64_t)nb * VCO_BLK;
+    double dec[256];
+    for (int t = 0; t < 256; t++) dec[t] = vco_e4m3_decode((uint8_t)t);
+    float C0 = vco_c0(d);
+    float KB = vco_kb(z_off);
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int i = r0; i < r1; i++) {
+        double* qrow = (double*)malloc(sizeof(double) * d);
+        double* O = (double*)calloc((size_t)d, sizeof(double));
+        float* S = (float*)malloc(sizeof(float) * VCO_BLK);
+        float* cj = (float*)malloc(sizeof(float) * VCO_BLK);
+        double* p = (double*)malloc(sizeof(double) * VCO_BLK);
+        for (int c = 0; c < d; c++) {
+            uint8_t b = q8[(int64_t)i * d + c];
+            qrow[c] = qk_int8 ? vco_i8_value(b) : dec[b];
+        }
+        volatile float sqc = q_scale[i] * C0;
+        double m = -INFINITY, l = 0.0;
+        for (int b = 0; b < nb; b++) {
+            int n = (L - b * VCO_BLK < VCO_BLK) ? L - b * VCO_BLK : VCO_BLK;
+            float t = -INFINITY;
+            for (int j = 0; j < n; j++) {
+                int64_t kr = (int64_t)(b * VCO_BLK + j) * d;
+                if (S_in) {
+                    S[j] = S_in[(int64_t)(i - r0) * Lp + b * VCO_BLK + j];
+                } else {
+                    double acc = 0.0;
+                    for (int c = 0; c < d; c++)
+                        acc += qrow[c] * (qk_int8 ? vco_i8_value(k8[kr + c]) : dec[k8[kr + c]]);
+                    S[j] = (float)acc;
+                }
+                volatile float cc = sqc * k_scale[(b * VCO_BLK + j) / 16];
+                cj[j] = cc;
+                volatile float x = S[j] * cc;
+                if (x > t) t = x;
+            }
+            float mnf = (m == -INFINITY || t > (float)m) ? t : (float)m;
+            double m_new = mnf;
+            volatile float e8 = 8.0f * mnf;
+            volatile float krow = KB - e8;
+            volatile float zrow = (float)z_off - mnf;
+            double ell = 0.0;
+            for (int j = 0; j < VCO_BLK; j++) {
+                uint8_t by = 0;
+                if (j < n) {
+                    if (prob_cast == 0) {
+                        volatile float c8 = 8.0f * cj[j];
+                        by = vco_expcast1(S[j], c8, krow);
+                    } else {
+                        by = vco_e4m3_encode((float)exp2((double)fmaf(S[j], cj[j], zrow)));
+                    }
+                }
+                int64_t o = (int64_t)(i - r0) * Lp + b * VCO_BLK + j;
+                if (bytes_out) bytes_out[o] = by;
+                if (S_out) S_out[o] = (j < n) ? S[j] : 0.0f;
+                p[j] = dec[by];
+                if (j < n) ell += p[j];
+            }
+            double alpha = (m == -INFINITY) ? 0.0 : exp2(m - m_new);
+            for (int c = 0; c < d; c++) {
+                int64_t vr = ((int64_t)b * d + c) * VCO_BLK;
+                double acc = 0.0;
+                for (int j = 0; j < n; j++) acc += p[j] * dec[v8[vr + j]];
+                O[c] = alpha * O[c] + (double)(float)acc;
+            }
+            l = alpha * l + ell;
+            m = m_new;
+        }
+        for (int c = 0; c < d; c++) out[(int64_t)(i - r0) * d + c] = (float)((double)v_scale[c] * O[c] / l);
+        free(qrow); free(O); free(S); free(cj); free(p);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Whole-tensor drivers over B*H heads (OpenMP over heads).                  */
 /* ------------------------------------------------------------------------ */
 

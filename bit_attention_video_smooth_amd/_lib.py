@@ -23,8 +23,12 @@ VC_ERR_HIP = -4
 
 EXPORTS = ["vc_version", "vc_last_error", "vc_prepared_sizes", "vsmooth_workspace_bytes",
            "vsmooth_prepare", "vc_attention_fwd", "vc_attention_fwd_dump",
-           "vc_attention_fwd_bf16", "vc_debug_expcast", "vc_debug_e4m3_encode",
-           "vc_debug_mfma_fp8"]
+           "vc_attention_fwd_bf16", "vc_sage_prepared_sizes", "vc_sage_workspace_bytes",
+           "vc_sage_prepare", "vc_sage_attention_fwd", "vc_sage_attention_fwd_dump",
+           "vc_debug_expcast", "vc_debug_e4m3_encode", "vc_debug_mfma_fp8"]
+
+VC_SAGE_QK_INT8 = 0
+VC_SAGE_QK_FP8 = 1
 
 
 class VCError(RuntimeError):
@@ -57,6 +61,16 @@ class vc_attn_params(ctypes.Structure):
                 ("prob_cast", ctypes.c_int32)]
 
 
+class vc_sage_params(ctypes.Structure):
+    _fields_ = [("qk_dtype", ctypes.c_int32), ("v_dtype", ctypes.c_int32), ("q_block_size", ctypes.c_int32),
+                ("k_block_size", ctypes.c_int32), ("v_block_size", ctypes.c_int32), ("smooth_k", ctypes.c_int32)]
+
+
+class vc_sage_prepared(ctypes.Structure):
+    _fields_ = [("q8", ctypes.c_void_p), ("k8", ctypes.c_void_p), ("v8", ctypes.c_void_p),
+                ("q_scale", ctypes.c_void_p), ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p)]
+
+
 _lock = threading.Lock()
 _lib = None
 
@@ -82,6 +96,12 @@ def load():
         L.vc_attention_fwd.argtypes = [S, AP, PR, P, P]
         L.vc_attention_fwd_dump.argtypes = [S, AP, PR, P, i32, i32, P, P, P]
         L.vc_attention_fwd_bf16.argtypes = [S, P, P, P, P, i32, P]
+        SP, SR = ctypes.POINTER(vc_sage_params), ctypes.POINTER(vc_sage_prepared)
+        L.vc_sage_prepared_sizes.argtypes = [S, ctypes.POINTER(sz)]
+        L.vc_sage_workspace_bytes.argtypes = [S, ctypes.POINTER(sz)]
+        L.vc_sage_prepare.argtypes = [S, SP, P, P, P, SR, P, sz, P]
+        L.vc_sage_attention_fwd.argtypes = [S, SP, AP, SR, P, P]
+        L.vc_sage_attention_fwd_dump.argtypes = [S, SP, AP, SR, P, i32, i32, P, P, P]
         L.vc_debug_expcast.argtypes = [P, P, P, i64, P, P]
         L.vc_debug_e4m3_encode.argtypes = [P, i64, P, P]
         L.vc_debug_mfma_fp8.argtypes = [P, P, P, i32, P]
@@ -162,6 +182,40 @@ def vc_attention_fwd_dump(shape, params, prep, out, bh, q_tile, s_dump, p_dump, 
 def vc_attention_fwd_bf16(shape, q, k, v, out, out_dtype=0, stream=None):
     _check(load().vc_attention_fwd_bf16(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
                                         out_dtype, _stream(stream)))
+
+
+def make_sage_params(qk_dtype=VC_SAGE_QK_INT8, smooth_k=1) -> vc_sage_params:
+    """The recipe's fixed fields: v_dtype FP8 E4M3, q/k/v block sizes 1/16/1."""
+    return vc_sage_params(qk_dtype, 0, 1, 16, 1, smooth_k)
+
+
+def vc_sage_prepared_sizes(shape: vc_shape):
+    arr = (ctypes.c_size_t * 6)()
+    _check(load().vc_sage_prepared_sizes(ctypes.byref(shape), arr))
+    return list(arr)
+
+
+def vc_sage_workspace_bytes(shape: vc_shape) -> int:
+    n = ctypes.c_size_t()
+    _check(load().vc_sage_workspace_bytes(ctypes.byref(shape), ctypes.byref(n)))
+    return n.value
+
+
+def vc_sage_prepare(shape, params: vc_sage_params, q, k, v, out: vc_sage_prepared, ws, ws_bytes, stream=None):
+    _check(load().vc_sage_prepare(ctypes.byref(shape), ctypes.byref(params), _ptr(q), _ptr(k), _ptr(v),
+                                  ctypes.byref(out), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def vc_sage_attention_fwd(shape, sage: vc_sage_params, params: vc_attn_params, prep: vc_sage_prepared, out,
+                          stream=None):
+    _check(load().vc_sage_attention_fwd(ctypes.byref(shape), ctypes.byref(sage), ctypes.byref(params),
+                                        ctypes.byref(prep), _ptr(out), _stream(stream)))
+
+
+def vc_sage_attention_fwd_dump(shape, sage, params, prep, out, bh, q_tile, s_dump, p_dump, stream=None):
+    _check(load().vc_sage_attention_fwd_dump(ctypes.byref(shape), ctypes.byref(sage), ctypes.byref(params),
+                                             ctypes.byref(prep), _ptr(out), bh, q_tile, _ptr(s_dump),
+                                             _ptr(p_dump), _stream(stream)))
 
 
 def vc_debug_expcast(S, c8, krow, n, out, stream=None):

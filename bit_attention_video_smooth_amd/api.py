@@ -98,6 +98,84 @@ def attention_dump(prep: Prepared, bh: int, q_tile: int, *, z_off=8, skip_lambda
     return out, s, p
 
 
+# ----------------------------------------------- SAGE-style baseline --
+
+SAGE_QK = {"int8": _lib.VC_SAGE_QK_INT8, "fp8": _lib.VC_SAGE_QK_FP8}
+
+
+@dataclasses.dataclass
+class SagePrepared:
+    shape: tuple
+    qk_dtype: str
+    smooth_k: int
+    q8: torch.Tensor
+    k8: torch.Tensor
+    v8: torch.Tensor
+    q_scale: torch.Tensor
+    k_scale: torch.Tensor
+    v_scale: torch.Tensor
+
+    def c(self) -> _lib.vc_sage_prepared:
+        return _lib.vc_sage_prepared(*(t.data_ptr() for t in (
+            self.q8, self.k8, self.v8, self.q_scale, self.k_scale, self.v_scale)))
+
+    def params(self) -> _lib.vc_sage_params:
+        return _lib.make_sage_params(SAGE_QK[self.qk_dtype], self.smooth_k)
+
+
+def sage_prepare(q, k, v, *, qk_dtype="int8", smooth_k=1, out: SagePrepared | None = None,
+                 ws: torch.Tensor | None = None, stream=None) -> SagePrepared:
+    """vc_sage_prepare on bf16 [B,H,L,d] device tensors (qk_dtype "int8" or
+    "fp8"; q/k/v block sizes 1/16/1, V in FP8 E4M3)."""
+    B, H, L, d = q.shape
+    for t in (q, k, v):
+        assert t.dtype == torch.bfloat16 and t.is_contiguous() and t.shape == q.shape
+    if qk_dtype not in SAGE_QK:
+        raise ValueError("qk_dtype must be 'int8' or 'fp8'")
+    shape = _lib.shape_of(B, H, L, d)
+    if out is None:
+        nb = nblocks(L)
+        Lp = nb * BLK
+        u8 = dict(dtype=torch.uint8, device=q.device)
+        f32 = dict(dtype=torch.float32, device=q.device)
+        out = SagePrepared((B, H, L, d), qk_dtype, smooth_k,
+                           torch.empty((B, H, Lp, d), **u8), torch.empty((B, H, Lp, d), **u8),
+                           torch.empty((B, H, nb, d, BLK), **u8), torch.empty((B, H, Lp), **f32),
+                           torch.empty((B, H, Lp // 16), **f32), torch.empty((B, H, d), **f32))
+    else:
+        out.qk_dtype, out.smooth_k = qk_dtype, smooth_k
+    if ws is None:
+        ws = torch.empty(max(_lib.vc_sage_workspace_bytes(shape), 16), dtype=torch.uint8, device=q.device)
+    _lib.vc_sage_prepare(shape, out.params(), q, k, v, out.c(), ws, ws.numel(), stream)
+    return out
+
+
+def sage_attention(prep: SagePrepared, *, z_off=8, prob_cast=1, out_dtype=torch.float32, out=None, stream=None):
+    """vc_sage_attention_fwd: O [B,H,L,d] (prob_cast 1: exp-then-cast bytes,
+    the SageAttention line's FP8 P; 0: ExpCast)."""
+    B, H, L, d = prep.shape
+    if out is None:
+        out = torch.empty((B, H, L, d), dtype=out_dtype, device=prep.q8.device)
+    od = 1 if out.dtype == torch.bfloat16 else 0
+    params = _lib.vc_attn_params(z_off, od, 0.0, prob_cast)
+    _lib.vc_sage_attention_fwd(_lib.shape_of(B, H, L, d), prep.params(), params, prep.c(), out, stream)
+    return out
+
+
+def sage_attention_dump(prep: SagePrepared, bh: int, q_tile: int, *, z_off=8, prob_cast=1, stream=None):
+    """vc_sage_attention_fwd_dump: (O fp32, S [256, Lp] fp32, P [256, Lp] u8)."""
+    B, H, L, d = prep.shape
+    Lp = nblocks(L) * BLK
+    dev = prep.q8.device
+    out = torch.empty((B, H, L, d), dtype=torch.float32, device=dev)
+    s = torch.zeros((256, Lp), dtype=torch.float32, device=dev)
+    p = torch.zeros((256, Lp), dtype=torch.uint8, device=dev)
+    params = _lib.vc_attn_params(z_off, 0, 0.0, prob_cast)
+    _lib.vc_sage_attention_fwd_dump(_lib.shape_of(B, H, L, d), prep.params(), params, prep.c(), out, bh, q_tile,
+                                    s, p, stream)
+    return out, s, p
+
+
 def attention_bf16(q, k, v, *, out_dtype=torch.float32, out=None, stream=None):
     """vc_attention_fwd_bf16 on bf16 [B,H,L,d] device tensors."""
     B, H, L, d = q.shape

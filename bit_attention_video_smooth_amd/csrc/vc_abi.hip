@@ -139,6 +139,82 @@ int attention_common(const vc_shape* shape, const vc_attn_params* params, const 
     return hip_status(vc::launch_attn_fp8(a, shape->d, params->out_dtype, dump, stream), "vc_attention_fwd");
 }
 
+int check_sage_params(const vc_sage_params* p) {
+    if (p == nullptr) return fail(VC_ERR_INVALID, "sage params is NULL");
+    if (p->qk_dtype != VC_SAGE_QK_INT8 && p->qk_dtype != VC_SAGE_QK_FP8)
+        return fail(VC_ERR_UNSUPPORTED, "qk_dtype=%d (supported: 0 INT8, 1 FP8)", p->qk_dtype);
+    if (p->v_dtype != 0) return fail(VC_ERR_UNSUPPORTED, "v_dtype=%d (only 0, FP8 E4M3, is supported)", p->v_dtype);
+    if (p->q_block_size != 1 || p->k_block_size != 16 || p->v_block_size != 1)
+        return fail(VC_ERR_UNSUPPORTED, "q/k/v block sizes %d/%d/%d (only 1/16/1 are supported)", p->q_block_size,
+                    p->k_block_size, p->v_block_size);
+    if (p->smooth_k != 0 && p->smooth_k != 1) return fail(VC_ERR_INVALID, "smooth_k must be 0 or 1");
+    return VC_OK;
+}
+
+int check_sage_prepared(const vc_sage_prepared* p) {
+    if (p == nullptr) return fail(VC_ERR_INVALID, "prepared is NULL");
+    int r;
+    if ((r = check_ptr(p->q8, "q8")) || (r = check_ptr(p->k8, "k8")) || (r = check_ptr(p->v8, "v8")) ||
+        (r = check_ptr(p->q_scale, "q_scale")) || (r = check_ptr(p->k_scale, "k_scale")) ||
+        (r = check_ptr(p->v_scale, "v_scale")))
+        return r;
+    return VC_OK;
+}
+
+int nvchunks(const vc_shape* s) { return (s->L + vc::SAGE_VCHUNK - 1) / vc::SAGE_VCHUNK; }
+
+size_t sage_ws(const vc_shape* s) {
+    const size_t BH = (size_t)s->B * s->H;
+    const int ns = vc::k_mean_splits((int)BH, s->L);
+    return a256(BH * ns * s->d * sizeof(double)) + a256(BH * s->d * sizeof(float)) +
+           a256(BH * nvchunks(s) * s->d * sizeof(float)) + a256(BH * s->d * sizeof(float));
+}
+
+int sage_attention_common(const vc_shape* shape, const vc_sage_params* sp, const vc_attn_params* params,
+                          const vc_sage_prepared* in, void* out, int32_t bh, int32_t q_tile, float* s_dump,
+                          uint8_t* p_dump, bool dump, hipStream_t stream) {
+    int r;
+    if ((r = check_shape(shape))) return r;
+    if ((r = check_sage_params(sp))) return r;
+    if (params == nullptr) return fail(VC_ERR_INVALID, "params is NULL");
+    if (params->z_off < 0 || params->z_off > 8) return fail(VC_ERR_INVALID, "z_off=%d out of [0, 8]", params->z_off);
+    if (params->out_dtype != 0 && params->out_dtype != 1)
+        return fail(VC_ERR_INVALID, "out_dtype must be 0 (fp32) or 1 (bf16)");
+    if (params->skip_lambda != 0.0f)
+        return fail(VC_ERR_UNSUPPORTED, "skip_lambda must be 0 for the SAGE baseline (it runs dense)");
+    if (params->prob_cast != 0 && params->prob_cast != 1)
+        return fail(VC_ERR_INVALID, "prob_cast must be 0 (ExpCast-FP8) or 1 (exp-then-cast)");
+    if ((r = check_sage_prepared(in))) return r;
+    if ((r = check_ptr(out, "out"))) return r;
+    vc::AttnArgs a{};
+    a.q8 = in->q8; a.k8 = in->k8; a.v8 = in->v8;
+    a.q_scale = in->q_scale; a.k_scale = in->k_scale; a.v_scale = in->v_scale; a.v_mean = nullptr;
+    a.out = out;
+    a.L = shape->L;
+    a.nb = nblk(shape);
+    a.BH = shape->B * shape->H;
+    a.nqt = (shape->L + vc::ATTN_BM - 1) / vc::ATTN_BM;
+    a.C0 = (float)(1.4426950408889634074 / sqrt((double)shape->d));
+    a.KB = (float)(56.0 - 0.35 + 8.0 * (double)params->z_off);
+    a.skip_thr = -INFINITY;
+    a.ZOFF = (float)params->z_off;
+    a.prob_cast = params->prob_cast;
+    a.dump_bh = -1;
+    a.dump_qt = -1;
+    if (dump) {
+        if (bh < 0 || bh >= a.BH) return fail(VC_ERR_INVALID, "bh=%d out of range", bh);
+        if (q_tile < 0 || q_tile >= a.nqt) return fail(VC_ERR_INVALID, "q_tile=%d out of range", q_tile);
+        if ((r = check_ptr(s_dump, "s_dump")) || (r = check_ptr(p_dump, "p_dump"))) return r;
+        a.dump_bh = bh;
+        a.dump_qt = q_tile;
+        a.s_dump = s_dump;
+        a.p_dump = p_dump;
+    }
+    return hip_status(vc::launch_attn_sage(a, shape->d, params->out_dtype, dump, sp->qk_dtype == VC_SAGE_QK_INT8,
+                                           stream),
+                      "vc_sage_attention_fwd");
+}
+
 }  // namespace
 
 extern "C" {
@@ -257,6 +333,71 @@ int vc_attention_fwd_bf16(const vc_shape* shape, const void* q, const void* k, c
     a.nqt = (shape->L + vc::ATTN_BM - 1) / vc::ATTN_BM;
     a.C0 = (float)(1.4426950408889634074 / sqrt((double)shape->d));
     return hip_status(vc::launch_attn_bf16(a, shape->d, out_dtype, stream), "vc_attention_fwd_bf16");
+}
+
+int vc_sage_prepared_sizes(const vc_shape* s, size_t bytes[6]) {
+    int r;
+    if ((r = check_shape(s))) return r;
+    if (bytes == nullptr) return fail(VC_ERR_INVALID, "bytes is NULL");
+    const size_t BH = (size_t)s->B * s->H, nb = nblk(s), Lp = nb * 128, d = s->d;
+    bytes[0] = BH * Lp * d;
+    bytes[1] = BH * Lp * d;
+    bytes[2] = BH * nb * d * 128;
+    bytes[3] = BH * Lp * 4;
+    bytes[4] = BH * (Lp / 16) * 4;
+    bytes[5] = BH * d * 4;
+    return ok();
+}
+
+int vc_sage_workspace_bytes(const vc_shape* shape, size_t* bytes) {
+    int r;
+    if ((r = check_shape(shape))) return r;
+    if (bytes == nullptr) return fail(VC_ERR_INVALID, "bytes is NULL");
+    *bytes = sage_ws(shape);
+    return ok();
+}
+
+int vc_sage_prepare(const vc_shape* shape, const vc_sage_params* params, const void* q, const void* k,
+                    const void* v, const vc_sage_prepared* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+    int r;
+    if ((r = check_shape(shape))) return r;
+    if ((r = check_sage_params(params))) return r;
+    if ((r = check_ptr(q, "q")) || (r = check_ptr(k, "k")) || (r = check_ptr(v, "v"))) return r;
+    if ((r = check_sage_prepared(out))) return r;
+    const size_t need = sage_ws(shape);
+    if (ws == nullptr || ws_bytes < need)
+        return fail(VC_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws_bytes, need);
+    if (!aligned16(ws)) return fail(VC_ERR_INVALID, "ws is not 16-byte aligned");
+    const size_t BH = (size_t)shape->B * shape->H;
+    const int ns = vc::k_mean_splits((int)BH, shape->L);
+    uint8_t* wp = static_cast<uint8_t*>(ws);
+    vc::SageArgs a{};
+    a.B = shape->B; a.H = shape->H; a.L = shape->L; a.d = shape->d; a.nb = nblk(shape);
+    a.qk_int8 = params->qk_dtype == VC_SAGE_QK_INT8;
+    a.smooth_k = params->smooth_k;
+    a.q = q; a.k = k; a.v = v;
+    a.q8 = out->q8; a.k8 = out->k8; a.v8 = out->v8;
+    a.q_scale = out->q_scale; a.k_scale = out->k_scale; a.v_scale = out->v_scale;
+    a.nvchunk = nvchunks(shape);
+    a.kpartial = reinterpret_cast<double*>(wp);
+    wp += a256(BH * ns * shape->d * sizeof(double));
+    a.kbar = reinterpret_cast<float*>(wp);
+    wp += a256(BH * shape->d * sizeof(float));
+    a.vpart = reinterpret_cast<float*>(wp);
+    wp += a256(BH * a.nvchunk * shape->d * sizeof(float));
+    a.vinv = reinterpret_cast<float*>(wp);
+    return hip_status(vc::launch_sage_prepare(a, stream), "vc_sage_prepare");
+}
+
+int vc_sage_attention_fwd(const vc_shape* shape, const vc_sage_params* sage, const vc_attn_params* params,
+                          const vc_sage_prepared* in, void* out, hipStream_t stream) {
+    return sage_attention_common(shape, sage, params, in, out, -1, -1, nullptr, nullptr, false, stream);
+}
+
+int vc_sage_attention_fwd_dump(const vc_shape* shape, const vc_sage_params* sage, const vc_attn_params* params,
+                               const vc_sage_prepared* in, void* out, int32_t bh, int32_t q_tile, float* s_dump,
+                               uint8_t* p_dump, hipStream_t stream) {
+    return sage_attention_common(shape, sage, params, in, out, bh, q_tile, s_dump, p_dump, true, stream);
 }
 
 int vc_debug_expcast(const float* S, const float* c8, const float* krow, int64_t n, uint8_t* bytes,

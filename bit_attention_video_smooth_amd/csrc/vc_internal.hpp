@@ -19,6 +19,22 @@ struct PrepareArgs {
     float* kbar;       // workspace [B*H, d]
 };
 
+// SAGE-style quantisation (sequence order): q8/k8 [BH, Lp, d] INT8 or E4M3,
+// v8 [BH, nb, d, 128] E4M3 in the P V slot order, q_scale [BH, Lp],
+// k_scale [BH, Lp/16], v_scale [BH, d]
+struct SageArgs {
+    int B, H, L, d, nb;
+    int qk_int8, smooth_k;
+    const void *q, *k, *v;
+    uint8_t *q8, *k8, *v8;
+    float *q_scale, *k_scale, *v_scale;
+    double* kpartial;  // workspace [B*H, nsplit, d]
+    float* kbar;       // workspace [B*H, d]
+    float* vpart;      // workspace [B*H, nvchunk, d] per-chunk channel amax
+    float* vinv;       // workspace [B*H, d] 448 / channel amax
+    int nvchunk;
+};
+
 struct KmeansArgs {
     int B, H, L, d, k, iters;
     uint64_t seed;
@@ -67,8 +83,15 @@ void kmeans_carve(KmeansArgs& a, void* ws);
 hipError_t launch_copy_perm(const int32_t* src, int32_t* dst, size_t n, double* obj, size_t nobj,
                             hipStream_t st);
 hipError_t launch_prepare_quant(const PrepareArgs& a, hipStream_t st);
+// per-channel K mean (kbar = 0 when smooth is 0); kpartial [BH, k_mean_splits, d]
+hipError_t launch_k_mean(const void* k, double* kpartial, float* kbar, int BH, int L, int d, int smooth,
+                         hipStream_t st);
+constexpr int SAGE_VCHUNK = 1024;  // tokens per partial channel amax
+hipError_t launch_sage_prepare(const SageArgs& a, hipStream_t st);
 hipError_t launch_kmeans(const KmeansArgs& a, hipStream_t st);
 hipError_t launch_attn_fp8(const AttnArgs& a, int d, int out_bf16, bool dump, hipStream_t st);
+// SAGE recipe: q_scale [BH, Lp], k_scale [BH, Lp/16], v_scale [BH, d]; v_mean unused
+hipError_t launch_attn_sage(const AttnArgs& a, int d, int out_bf16, bool dump, bool qk_int8, hipStream_t st);
 hipError_t launch_attn_bf16(const AttnBf16Args& a, int d, int out_bf16, hipStream_t st);
 hipError_t launch_debug_expcast(const float* S, const float* c8, const float* krow, int64_t n,
                                 uint8_t* out, hipStream_t st);

@@ -275,15 +275,29 @@ int k_mean_splits(int BH, int L) {
 }
 
 template <int D>
+static void launch_k_mean_t(const void* k, double* kpartial, float* kbar, int BH, int L, int smooth,
+                            hipStream_t st) {
+    const int nsplit = k_mean_splits(BH, L);
+    if (smooth) {
+        hipLaunchKernelGGL((k_colsum_partial<D>), dim3(nsplit, BH), dim3(256), 0, st,
+                           (const uint16_t*)k, kpartial, L, nsplit);
+    }
+    hipLaunchKernelGGL((k_mean_finalize<D>), dim3(BH), dim3(D), 0, st, kpartial, kbar, L, nsplit, smooth);
+}
+
+hipError_t launch_k_mean(const void* k, double* kpartial, float* kbar, int BH, int L, int d, int smooth,
+                         hipStream_t st) {
+    if (d == 128)
+        launch_k_mean_t<128>(k, kpartial, kbar, BH, L, smooth, st);
+    else
+        launch_k_mean_t<64>(k, kpartial, kbar, BH, L, smooth, st);
+    return hipGetLastError();
+}
+
+template <int D>
 static hipError_t launch_prepare_quant_t(const PrepareArgs& a, hipStream_t st) {
     const int BH = a.B * a.H;
-    const int nsplit = k_mean_splits(BH, a.L);
-    if (a.smooth_k) {
-        hipLaunchKernelGGL((k_colsum_partial<D>), dim3(nsplit, BH), dim3(256), 0, st,
-                           (const uint16_t*)a.k, a.kpartial, a.L, nsplit);
-    }
-    hipLaunchKernelGGL((k_mean_finalize<D>), dim3(BH), dim3(D), 0, st, a.kpartial, a.kbar, a.L,
-                       nsplit, a.smooth_k);
+    launch_k_mean_t<D>(a.k, a.kpartial, a.kbar, BH, a.L, a.smooth_k, st);
     hipLaunchKernelGGL((quant_qk_kernel<D, false>), dim3(a.nb, BH), dim3(256), 0, st,
                        (const uint16_t*)a.q, (const int32_t*)nullptr, (const float*)nullptr,
                        a.q8, a.q_scale, a.L, a.nb);

@@ -174,6 +174,79 @@ int vc_attention_fwd_dump(const vc_shape* shape, const vc_attn_params* params,
 int vc_attention_fwd_bf16(const vc_shape* shape, const void* q, const void* k, const void* v,
                           void* out, int32_t out_dtype, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * SAGE-style quantised attention, the baseline that the TensorRT-LLM blog
+ * configures in "Quantized Attention" with five fields: the QK^T format
+ * (INT8, the blog's choice, or FP8), the PV format (FP8 E4M3), the query
+ * block (1: one Q scale per query token), the key block (16: one K scale per
+ * 16 consecutive keys) and the V block (1: one V scale per channel of a
+ * head, taken over all its tokens).  Tokens stay in sequence order; there is
+ * no k-means and no block mean.  Readings where the blog is silent: a scale
+ * is amax / 127 (INT8) or amax / 448 (E4M3) by IEEE division (0 with all
+ * codes 0 when amax < 2^-100); INT8 codes round fp32(x / scale) computed as
+ * fp32(x * fp32(127 / amax)) to the nearest integer, ties to even, clamped to
+ * +-127; K is smoothed by its per-channel mean when smooth_k is 1.
+ * ------------------------------------------------------------------------ */
+enum { VC_SAGE_QK_INT8 = 0, VC_SAGE_QK_FP8 = 1 };
+
+typedef struct vc_sage_params {
+    int32_t qk_dtype;     /* VC_SAGE_QK_INT8 or VC_SAGE_QK_FP8; others: -2 */
+    int32_t v_dtype;      /* 0: FP8 E4M3 (the only PV format); others: -2 */
+    int32_t q_block_size; /* must be 1, else -2 */
+    int32_t k_block_size; /* must be 16, else -2 */
+    int32_t v_block_size; /* must be 1 (one scale per channel), else -2 */
+    int32_t smooth_k;     /* 1: subtract the per-channel mean of K first; 0: off */
+} vc_sage_params;
+
+/* Output of vc_sage_prepare, input of vc_sage_attention_fwd (device memory,
+ * sequence order).  v8 uses the block-transposed layout of vc_prepared with
+ * slot k = token k (no permutation). */
+typedef struct vc_sage_prepared {
+    uint8_t* q8;    /* [B,H,Lp,d] INT8 (two's complement) or E4M3 codes of Q */
+    uint8_t* k8;    /* [B,H,Lp,d] codes of K (- kbar when smooth_k) */
+    uint8_t* v8;    /* [B,H,nb,d,128] E4M3 codes of V */
+    float* q_scale; /* [B,H,Lp] one scale per token (0 past L) */
+    float* k_scale; /* [B,H,Lp/16] one scale per 16 tokens */
+    float* v_scale; /* [B,H,d] one scale per channel */
+} vc_sage_prepared;
+
+/* Byte sizes of the six vc_sage_prepared buffers, in the struct's order. */
+int vc_sage_prepared_sizes(const vc_shape* shape, size_t bytes[6]);
+
+/* Workspace that vc_sage_prepare needs for this shape. */
+int vc_sage_workspace_bytes(const vc_shape* shape, size_t* bytes);
+
+/* SAGE-style quantisation of bf16 q, k, v [B,H,L,d] into `out` (scales and
+ * codes as described above; padded tokens >= L get code 0 and scale 0).
+ * ws: ws_bytes >= vc_sage_workspace_bytes(), else -3. */
+int vc_sage_prepare(const vc_shape* shape, const vc_sage_params* params, const void* q,
+                    const void* k, const void* v, const vc_sage_prepared* out, void* ws,
+                    size_t ws_bytes, hipStream_t stream);
+
+/* SAGE-style attention forward on the scaffold of vc_attention_fwd (the same
+ * 128-key blocks, online softmax and matrix-core products).  Per query row i
+ * and block b:
+ *   S = Q8 K8^T (INT8 or FP8 matrix cores; INT8 sums are exact);
+ *   c_ij = fp32(fp32(s_q,i * log2(e)/sqrt(d)) * s_k,j/16);
+ *   m' = max(m, max_j fp32(S_ij c_ij));
+ *   bytes: exp-then-cast, E4M3(2^fma(S, c, z_off - m')) (prob_cast 1, the
+ *   FP8 path of the SageAttention line), or ExpCast, fma(S, 8c, KB - 8 m')
+ *   (prob_cast 0), as in vc_attn_params;
+ *   l_b = row sum of P;  acc = P V8_b;
+ *   O = 2^(m - m') O + acc;  l = 2^(m - m') l + l_b;
+ * output s_v (.) O / l, [B,H,L,d].  params->skip_lambda must be 0 (-2
+ * otherwise): the baseline runs dense. */
+int vc_sage_attention_fwd(const vc_shape* shape, const vc_sage_params* sage,
+                          const vc_attn_params* params, const vc_sage_prepared* in, void* out,
+                          hipStream_t stream);
+
+/* vc_sage_attention_fwd plus the scores and bytes of one 256-query tile, as
+ * vc_attention_fwd_dump.  A checking aid. */
+int vc_sage_attention_fwd_dump(const vc_shape* shape, const vc_sage_params* sage,
+                               const vc_attn_params* params, const vc_sage_prepared* in, void* out,
+                               int32_t bh, int32_t q_tile, float* s_dump, uint8_t* p_dump,
+                               hipStream_t stream);
+
 /* ExpCast-FP8 alone, with the device function the attention kernel uses:
  * bytes[i] = min(max(rne(fma(S[i], c8[i], krow[i])), 0), 126).  A checking
  * aid for the byte map (MarkTechPost abstract). */

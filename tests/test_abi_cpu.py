@@ -148,3 +148,62 @@ def test_debug_entry_points_validate(lib):
     _lib.vc_debug_e4m3_encode(FAKE, 0, FAKE, 0)  # n == 0 is a no-op
     with pytest.raises(_lib.VCError):
         _lib.vc_debug_mfma_fp8(FAKE, 0, FAKE, 1, 0)
+
+
+def _sprep(**over):
+    f = dict(q8=FAKE, k8=FAKE, v8=FAKE, q_scale=FAKE, k_scale=FAKE, v_scale=FAKE)
+    f.update(over)
+    return _lib.vc_sage_prepared(*[f[n] for n, _ in _lib.vc_sage_prepared._fields_])
+
+
+def test_sage_sizes_and_workspace(lib):
+    s = _lib.shape_of(2, 3, 300, 64)
+    nb, Lp = 3, 384
+    assert _lib.vc_sage_prepared_sizes(s) == [6 * Lp * 64, 6 * Lp * 64, 6 * nb * 64 * 128, 6 * Lp * 4,
+                                              6 * (Lp // 16) * 4, 6 * 64 * 4]
+    assert _lib.vc_sage_workspace_bytes(s) >= 6 * 64 * (8 + 4 + 4 + 4)
+
+
+def test_sage_rejects_bad_recipe(lib):
+    s = _lib.shape_of(1, 1, 256, 64)
+    ap = _lib.vc_attn_params(8, 0, 0.0, 1)
+    for field, val in [("qk_dtype", 2), ("v_dtype", 1), ("q_block_size", 2), ("k_block_size", 128),
+                       ("v_block_size", 16)]:
+        p = _lib.make_sage_params()
+        setattr(p, field, val)
+        with pytest.raises(_lib.VCError) as e:
+            _lib.vc_sage_attention_fwd(s, p, ap, _sprep(), FAKE, 0)
+        assert e.value.code == _lib.VC_ERR_UNSUPPORTED, field
+        with pytest.raises(_lib.VCError) as e:
+            _lib.vc_sage_prepare(s, p, FAKE, FAKE, FAKE, _sprep(), FAKE, 1 << 30, 0)
+        assert e.value.code == _lib.VC_ERR_UNSUPPORTED, field
+    p = _lib.make_sage_params(smooth_k=2)
+    with pytest.raises(_lib.VCError) as e:
+        _lib.vc_sage_prepare(s, p, FAKE, FAKE, FAKE, _sprep(), FAKE, 1 << 30, 0)
+    assert e.value.code == _lib.VC_ERR_INVALID
+
+
+def test_sage_rejects_bad_arguments(lib):
+    s = _lib.shape_of(1, 2, 1000, 128)
+    p = _lib.make_sage_params()
+    need = _lib.vc_sage_workspace_bytes(s)
+    with pytest.raises(_lib.VCError) as e:
+        _lib.vc_sage_prepare(s, p, FAKE, FAKE, FAKE, _sprep(), FAKE, need - 1, 0)
+    assert e.value.code == _lib.VC_ERR_WORKSPACE
+    with pytest.raises(_lib.VCError) as e:
+        _lib.vc_sage_prepare(s, p, FAKE, FAKE + 8, FAKE, _sprep(), FAKE, need, 0)
+    assert e.value.code == _lib.VC_ERR_INVALID
+    with pytest.raises(_lib.VCError) as e:
+        _lib.vc_sage_attention_fwd(s, p, _lib.vc_attn_params(8, 0, 0.5, 1), _sprep(), FAKE, 0)
+    assert e.value.code == _lib.VC_ERR_UNSUPPORTED  # the baseline runs dense
+    for pc in (-1, 2):
+        with pytest.raises(_lib.VCError) as e:
+            _lib.vc_sage_attention_fwd(s, p, _lib.vc_attn_params(8, 0, 0.0, pc), _sprep(), FAKE, 0)
+        assert e.value.code == _lib.VC_ERR_INVALID
+    with pytest.raises(_lib.VCError) as e:
+        _lib.vc_sage_attention_fwd(s, p, _lib.vc_attn_params(8, 0, 0.0, 1), _sprep(v_scale=0), FAKE, 0)
+    assert e.value.code == _lib.VC_ERR_INVALID
+    with pytest.raises(_lib.VCError) as e:
+        _lib.vc_sage_attention_fwd_dump(s, p, _lib.vc_attn_params(8, 0, 0.0, 1), _sprep(), FAKE, 2, 0, FAKE,
+                                        FAKE, 0)
+    assert e.value.code == _lib.VC_ERR_INVALID

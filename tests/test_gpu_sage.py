@@ -1,0 +1,172 @@
+"""GPU parity of the SAGE-style baseline (TensorRT-LLM blog, "Quantized
+Attention": QK^T in INT8 or FP8 with one Q scale per token and one K scale
+per 16 keys, PV in FP8 with one V scale per channel) against the oracle, on
+the same seeded inputs, through the C ABI.
+
+Bars: codes and scales bit-exact; INT8 scores are exact integer sums, so the
+kernel's scores equal the oracle's and its ExpCast bytes are bit-exact
+(exp-then-cast bytes: one-code differences where v_exp_f32's last-bit error
+straddles an E4M3 midpoint, rate below 1e-4); FP8 scores are checked given
+the kernel's own scores, like the V-Smooth path; outputs within the given-S
+bar (rel-L2 1e-4, max-abs 1e-3 of max) and, end to end, within the output
+bar (rel-L2 1e-3, max-abs 1e-2; twice that at d = 64)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_attention_video_smooth_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+GIVEN_S_REL, GIVEN_S_MAXABS = 1e-4, 1e-3
+REL_L2, MAXABS = 1e-3, 1e-2
+
+SHAPES = [(1, 2, 1024, 64, (4, 16, 16)), (1, 3, 300, 128, None), (2, 2, 129, 64, None),
+          (1, 1, 1, 128, None), (1, 2, 4000, 128, None), (1, 1, 520, 64, None),
+          (1, 1, 500, 128, None)]
+
+
+@pytest.fixture(scope="module")
+def api():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    from bit_attention_video_smooth_amd import api as a
+    a._lib.load()
+    return a
+
+
+def dev_bf16(u16):
+    return torch.from_numpy(np.ascontiguousarray(u16)).view(torch.bfloat16).cuda()
+
+
+def rel_l2(a, b):
+    return float(np.linalg.norm((a - b).ravel()) / np.linalg.norm(b.ravel()))
+
+
+def _inputs(B, H, L, d, seed, grid=None):
+    return synth.make_inputs(synth.custom(B, H, L, d, grid=grid), seed)
+
+
+def _end_to_end_bar(d):
+    return (REL_L2, MAXABS) if d == 128 else (2 * REL_L2, 2 * MAXABS)
+
+
+def _oracle_out(q, k, v, qk, smooth_k=1, prob_cast=1, z_off=8, scores=None):
+    B, H, L, d = q.shape
+    out = np.empty((B, H, L, d), np.float32)
+    for b in range(B):
+        for h in range(H):
+            o = oracle.sage_prepare_head(q[b, h], k[b, h], v[b, h], qk, smooth_k)
+            sc = None if scores is None else np.ascontiguousarray(scores[b, h])
+            out[b, h] = oracle.sage_attention_head(o, L, qk, z_off=z_off, prob_cast=prob_cast, scores=sc)
+    return out
+
+
+def _kernel_scores(api, P, prob_cast):
+    B, H, L, d = P.shape
+    nqt = (L + 255) // 256
+    Lp = ((L + 127) // 128) * 128
+    S = np.zeros((B, H, nqt * 256, Lp), np.float32)
+    for bh in range(B * H):
+        for qt in range(nqt):
+            _, s, _ = api.sage_attention_dump(P, bh, qt, prob_cast=prob_cast)
+            S[bh // H, bh % H, qt * 256:(qt + 1) * 256] = s.cpu().numpy()
+    return S[:, :, :L]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("qk,smooth_k", [("int8", 1), ("fp8", 1), ("int8", 0)])
+def test_sage_prepare_bit_exact(api, shape, qk, smooth_k):
+    B, H, L, d, grid = shape
+    q, k, v = _inputs(B, H, L, d, 200 + L, grid)
+    P = api.sage_prepare(dev_bf16(q), dev_bf16(k), dev_bf16(v), qk_dtype=qk, smooth_k=smooth_k)
+    torch.cuda.synchronize()
+    g = {n: getattr(P, n).cpu().numpy() for n in ("q8", "k8", "q_scale", "k_scale", "v_scale")}
+    g["v8"] = api.v_codes_natural(P.v8).cpu().numpy()
+    for b in range(B):
+        for h in range(H):
+            o = oracle.sage_prepare_head(q[b, h], k[b, h], v[b, h], qk, smooth_k)
+            for n in ("q8", "k8", "v8", "q_scale", "k_scale", "v_scale"):
+                x, y = g[n][b, h], o[n]
+                assert x.shape == y.shape, n
+                if not np.array_equal(x.view(np.uint8), y.view(np.uint8)):
+                    idx = np.argwhere(x != y)[:5]
+                    pytest.fail("%s %s mismatch at %s: gpu %s oracle %s"
+                                % (qk, n, idx.tolist(), x[tuple(idx.T)], y[tuple(idx.T)]))
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("qk", ["int8", "fp8"])
+@pytest.mark.parametrize("prob_cast", [1, 0])
+def test_sage_attention_matches_oracle(api, shape, qk, prob_cast):
+    B, H, L, d, grid = shape
+    q, k, v = _inputs(B, H, L, d, 300 + L, grid)
+    P = api.sage_prepare(dev_bf16(q), dev_bf16(k), dev_bf16(v), qk_dtype=qk)
+    out = api.sage_attention(P, prob_cast=prob_cast).cpu().numpy()
+    ref = _oracle_out(q, k, v, qk, prob_cast=prob_cast)
+    S = _kernel_scores(api, P, prob_cast)
+    refS = ref if qk == "int8" else _oracle_out(q, k, v, qk, prob_cast=prob_cast, scores=S)
+    r, ma = rel_l2(out, ref), float(np.abs(out - ref).max() / np.abs(ref).max())
+    rs, mas = rel_l2(out, refS), float(np.abs(out - refS).max() / np.abs(refS).max())
+    print("sage %s prob_cast=%d %s: end-to-end rel-L2 %.3g max-abs/max %.3g | given kernel S rel-L2 %.3g "
+          "max-abs/max %.3g" % (qk, prob_cast, (B, H, L, d), r, ma, rs, mas))
+    assert np.all(np.isfinite(out))
+    assert rs <= GIVEN_S_REL and mas <= GIVEN_S_MAXABS
+    br, bm = _end_to_end_bar(d)
+    assert r <= br and ma <= bm
+
+
+@pytest.mark.parametrize("shape", [SHAPES[0], SHAPES[1], SHAPES[4], SHAPES[5]])
+@pytest.mark.parametrize("prob_cast", [0, 1])
+def test_sage_int8_scores_exact_and_bytes(api, shape, prob_cast):
+    """INT8 scores: the two 16x16x64 integer products per tile give the exact
+    sum, so the dumped scores equal the oracle's; the bytes then follow."""
+    B, H, L, d, grid = shape
+    q, k, v = _inputs(B, H, L, d, 400 + L, grid)
+    P = api.sage_prepare(dev_bf16(q), dev_bf16(k), dev_bf16(v), qk_dtype="int8")
+    nqt = (L + 255) // 256
+    for bh, qt in sorted({(0, 0), (B * H - 1, nqt - 1)}):
+        b, h = divmod(bh, H)
+        _, S, Pb = api.sage_attention_dump(P, bh, qt, prob_cast=prob_cast)
+        r0, r1 = qt * 256, min(L, qt * 256 + 256)
+        n = r1 - r0
+        S, Pb = S.cpu().numpy()[:n], Pb.cpu().numpy()[:n]
+        o = oracle.sage_prepare_head(q[b, h], k[b, h], v[b, h], "int8")
+        _, rby, rS = oracle.sage_attention_head(o, L, "int8", prob_cast=prob_cast, rows=(r0, r1), want_bytes=True)
+        assert np.array_equal(S, rS), "INT8 scores differ from the exact sums"
+        diff = Pb.astype(int) - rby.astype(int)
+        frac = float((diff != 0).mean())
+        print("sage int8 dump %s bh=%d qt=%d prob_cast=%d: byte mismatch %.2e" % ((B, H, L, d), bh, qt,
+                                                                                 prob_cast, frac))
+        if prob_cast == 0:
+            assert frac == 0.0
+        else:
+            assert np.abs(diff).max() <= 1 and frac <= 1e-4
+        assert Pb.max() == 120  # the row maximum is 2^8
+
+
+def test_sage_bf16_output(api):
+    B, H, L, d, grid = SHAPES[0]
+    q, k, v = _inputs(B, H, L, d, 7, grid)
+    P = api.sage_prepare(dev_bf16(q), dev_bf16(k), dev_bf16(v))
+    o32 = api.sage_attention(P).cpu().numpy()
+    o16 = api.sage_attention(P, out_dtype=torch.bfloat16).float().cpu().numpy()
+    assert np.array_equal(o16, torch.from_numpy(o32).to(torch.bfloat16).float().numpy())
+
+
+def test_sage_and_vsmooth_near_exact_attention(api):
+    """Both recipes on one tiny head: within the quantisation band of the
+    fp64 softmax attention (a sanity check of the whole path)."""
+    B, H, L, d, grid = SHAPES[0]
+    q, k, v = _inputs(B, H, L, d, 8, grid)
+    qd, kd, vd = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    sage = api.sage_attention(api.sage_prepare(qd, kd, vd)).cpu().numpy()
+    vc = api.attention(api.prepare(qd, kd, vd)).cpu().numpy()
+    for b in range(B):
+        for h in range(H):
+            ref = oracle.attention_f64(oracle.bf16_to_f32(q[b, h]), oracle.bf16_to_f32(k[b, h]),
+                                       oracle.bf16_to_f32(v[b, h]))
+            rs, rv = rel_l2(sage[b, h], ref), rel_l2(vc[b, h], ref)
+            print("head %d: SAGE rel-L2 %.4f, V-Smooth rel-L2 %.4f against fp64" % (h, rs, rv))
+            assert rs < 6e-2 and rv < 6e-2

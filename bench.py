@@ -36,6 +36,7 @@ def parse():
     p.add_argument("--cpu-rows", type=int, default=-1, help="query rows of the CPU oracle sample (-1: auto)")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--no-bf16", action="store_true")
+    p.add_argument("--no-sage", action="store_true", help="skip the SAGE-style baseline leg")
     p.add_argument("--v-scale-mode", type=int, default=0)
     p.add_argument("--skip-lambda", type=float, default=0.5,
                    help="Skip Softmax threshold of the extra, reported (not timed-step) attention run; 0: none")
@@ -48,6 +49,7 @@ def parse():
 # Sources the attention kernel is built from; the committed HBM-traffic
 # summary records their hash and is ignored once any of them changes.
 KERNEL_SOURCES = ["bit_attention_video_smooth_amd/csrc/vc_attn_fp8.hip",
+                  "bit_attention_video_smooth_amd/csrc/vc_attn_fp8_kernel.hpp",
                   "bit_attention_video_smooth_amd/csrc/vc_device.hpp",
                   "bit_attention_video_smooth_amd/csrc/vc_lds.hpp",
                   "bit_attention_video_smooth_amd/csrc/vc_internal.hpp",
@@ -232,9 +234,41 @@ def main():
     exp_then_cast = {"ms": naive_ms, "tflops": flop / naive_ms / 1e9, "expcast_speedup": naive_ms / attn_ms}
     print("exp-then-cast attention %.3f ms" % naive_ms, file=sys.stderr, flush=True)
 
+    # SAGE-style baseline (TensorRT-LLM blog, "Quantized Attention": one Q
+    # scale per token, one K scale per 16 keys, INT8 or FP8 QK^T, FP8 PV with
+    # one V scale per channel, exp-then-cast P) on the same inputs
+    sage = None
+    SP = None
+    if not args.no_sage:
+        sage = {}
+        sws = torch.empty(max(16, api._lib.vc_sage_workspace_bytes(api._lib.shape_of(B, H, L, d))),
+                          dtype=torch.uint8, device="cuda")
+        for qk in ("int8", "fp8"):
+            SP = api.sage_prepare(q, k, v, qk_dtype=qk, out=SP, ws=sws)
+            api.sage_attention(SP, out=out)
+            torch.cuda.synchronize()
+            ev[0].record(stream)
+            for _ in range(args.steps):
+                api.sage_prepare(q, k, v, qk_dtype=qk, out=SP, ws=sws)
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            sp_ms = ev[0].elapsed_time(ev[1]) / args.steps
+            ev[0].record(stream)
+            for _ in range(args.steps):
+                api.sage_attention(SP, out=out)
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            sa_ms = ev[0].elapsed_time(ev[1]) / args.steps
+            sage["qk_" + qk] = {"prepare_ms": sp_ms, "attention_ms": sa_ms, "tflops": flop / sa_ms / 1e9,
+                                "vc_attention_speedup": sa_ms / attn_ms,
+                                "vc_speedup_with_prepare": (sp_ms + sa_ms) / (quant_ms + attn_ms)}
+            print("sage %s: prepare %.3f ms, attention %.3f ms" % (qk, sp_ms, sa_ms), file=sys.stderr, flush=True)
+        sage["note"] = ("P bytes by exp-then-cast; vc_speedup_with_prepare compares against the V-Smooth "
+                        "prepare without k-means (permutation reused)")
+
     # V-Smooth token-ordering ablation on this workload (prepare outputs of
     # the library; statistics averaged over heads)
-    from bit_attention_video_smooth_amd.ablation import cube_permutation, value_stats
+    from bit_attention_video_smooth_amd.ablation import cube_permutation, sage_value_stats, value_stats
     ablation = {}
     orders = {"sequence": torch.arange(L, dtype=torch.int32, device="cuda").expand(B, H, L).contiguous(),
               "static_cube_2x8x8": torch.from_numpy(cube_permutation(cfg.grid)).cuda().expand(B, H, L).contiguous(),
@@ -246,6 +280,9 @@ def main():
         ablation[name] = {"energy_removed": float(st["energy_removed"].mean()),
                           "v_rel_err": float(st["v_rel_err"].mean())}
     del Pa
+    if SP is not None:  # the SAGE recipe's V codes: one scale per channel, no block mean
+        ablation["sage_per_channel"] = {"v_rel_err": float(sage_value_stats(SP, v)["v_rel_err"].mean())}
+        del SP
 
     attn_tflops = flop / attn_ms / 1e9
     res = {
@@ -277,6 +314,7 @@ def main():
                     "quant_gbs": quant_bytes / quant_ms / 1e6},
         "bf16_attention": bf16,
         "exp_then_cast_attention": exp_then_cast,
+        "sage_baseline": sage,
         "skip_softmax": skip,
         "grouping_schedule": grouping_schedule(prep_ms, quant_ms, attn_ms),
         "v_smooth_ablation": ablation,

@@ -58,3 +58,22 @@ def value_stats(P: api.Prepared, v: torch.Tensor) -> dict:
             energy[b, h] = float(1.0 - resid / tot)
             err[b, h] = float(torch.sqrt(e / tot))
     return {"energy_removed": energy, "v_rel_err": err}
+
+
+@torch.no_grad()
+def sage_value_stats(P: api.SagePrepared, v: torch.Tensor) -> dict:
+    """Relative error |v_hat - v| / |v| per (batch, head) of the SAGE-style V
+    codes, v_hat = s_c * decode(code) with one scale per channel and no
+    block mean (TensorRT-LLM blog, "Quantized Attention", v block size 1).
+    Returns numpy float64 [B,H]."""
+    B, H, L, d = P.shape
+    codes = api.v_codes_natural(P.v8)  # [B,H,nb,d,128]
+    err = np.empty((B, H))
+    for b in range(B):
+        for h in range(H):
+            x = v[b, h].double()                                              # [L,d]
+            dec = codes[b, h].view(torch.float8_e4m3fn).float().double()      # [nb,d,128]
+            dec = dec.transpose(1, 2).reshape(-1, d)[:L]                       # [L,d]
+            xhat = P.v_scale[b, h].double()[None, :] * dec
+            err[b, h] = float(torch.sqrt(((xhat - x) ** 2).sum() / (x * x).sum()))
+    return {"v_rel_err": err}

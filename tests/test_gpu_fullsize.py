@@ -99,3 +99,32 @@ def test_full_size_kmeans_objective(api, cfg_idx):
     print("%s k-means head %d: gpu J %.7g oracle J %.7g ratio %.6f"
           % (cfg.name, B * H - 1, obj[b, h], J, obj[b, h] / J))
     assert abs(obj[b, h] / J - 1) <= 0.01
+
+
+@pytest.mark.parametrize("cfg_idx,qk", [(2, "int8"), (2, "fp8"), (4, "int8")])
+def test_full_size_sage_sampled(api, cfg_idx, qk):
+    """The SAGE-style baseline at full size, as the benchmark runs it
+    (exp-then-cast P): sampled heads bit-exact, sampled query tiles (first
+    and ragged last) against the oracle."""
+    cfg = synth.CONFIGS[cfg_idx]
+    B, H, L, d = cfg.B, cfg.H, cfg.L, cfg.d
+    q, k, v = synth.make_inputs(cfg, cfg_idx)
+    P = api.sage_prepare(dev_bf16(q), dev_bf16(k), dev_bf16(v), qk_dtype=qk)
+    out = api.sage_attention(P, prob_cast=1)
+    torch.cuda.synchronize()
+    last_tile = ((L - 1) // 256) * 256
+    bar = (1e-4, 1e-3) if qk == "int8" else (1e-3, 1e-2)  # INT8 scores are exact
+    for bh in sorted({0, B * H - 1}):
+        b, h = divmod(bh, H)
+        o = oracle.sage_prepare_head(q[b, h], k[b, h], v[b, h], qk)
+        for n in ("q8", "k8", "q_scale", "k_scale", "v_scale"):
+            assert np.array_equal(getattr(P, n)[b, h].cpu().numpy(), o[n]), n
+        assert np.array_equal(api.v_codes_natural(P.v8[b, h]).cpu().numpy(), o["v8"])
+        for r0 in (0, last_tile):
+            r1 = min(L, r0 + 256)
+            ref = oracle.sage_attention_head(o, L, qk, prob_cast=1, rows=(r0, r1))
+            got = out[b, h, r0:r1].cpu().numpy()
+            rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+            ma = float(np.abs(got - ref).max() / np.abs(ref).max())
+            print("sage %s %s bh=%d rows %d-%d: rel-L2 %.3g max-abs/max %.3g" % (qk, cfg.name, bh, r0, r1, rel, ma))
+            assert rel <= bar[0] and ma <= bar[1]

@@ -170,3 +170,21 @@ def test_sage_and_vsmooth_near_exact_attention(api):
             rs, rv = rel_l2(sage[b, h], ref), rel_l2(vc[b, h], ref)
             print("head %d: SAGE rel-L2 %.4f, V-Smooth rel-L2 %.4f against fp64" % (h, rs, rv))
             assert rs < 6e-2 and rv < 6e-2
+
+
+def test_sage_value_stats_match_oracle(api):
+    """The ablation's SAGE V error (s_c * decode(code) against v) from the
+    library's codes equals the same statistic of the oracle's codes."""
+    from bit_attention_video_smooth_amd.ablation import sage_value_stats
+    B, H, L, d, grid = SHAPES[1]
+    q, k, v = _inputs(B, H, L, d, 9, grid)
+    vd = dev_bf16(v)
+    st = sage_value_stats(api.sage_prepare(dev_bf16(q), dev_bf16(k), vd), vd)["v_rel_err"]
+    for b in range(B):
+        for h in range(H):
+            o = oracle.sage_prepare_head(q[b, h], k[b, h], v[b, h], "int8")
+            x = oracle.bf16_to_f32(v[b, h]).astype(np.float64)
+            dec = oracle.e4m3_decode(o["v8"]).transpose(0, 2, 1).reshape(-1, d)[:L]
+            xh = o["v_scale"].astype(np.float64)[None, :] * dec
+            ref = np.sqrt(((xh - x) ** 2).sum() / (x * x).sum())
+            assert abs(st[b, h] - ref) <= 1e-9 * ref, (st[b, h], ref)

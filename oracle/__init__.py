@@ -62,6 +62,8 @@ def lib():
             L.vco_k_mean.argtypes = [P, i32, i32, P]
             L.vco_kmeans.restype = ctypes.c_double
             L.vco_kmeans.argtypes = [P, i32, i32, i32, i32, u64, P, P, P]
+            L.vco_kmeans_warm.restype = ctypes.c_double
+            L.vco_kmeans_warm.argtypes = [P, i32, i32, i32, i32, P, P, P, P]
             L.vco_stable_perm.argtypes = [P, i32, i32, P]
             L.vco_prepare_head.argtypes = [P, P, P, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P]
             L.vco_expcast.argtypes = [P, i64, f32, f32, P]
@@ -150,6 +152,22 @@ def kmeans(v_bf16_head: np.ndarray, k: int, iters: int, seed_bh: int, history: b
     C = np.empty((k, d), np.float32)
     hist = np.empty(iters + 1, np.float64) if history else None
     J = lib().vco_kmeans(_p(v), L, d, k, iters, seed_bh, _p(a), _p(C), _p(hist))
+    return (a, C, hist) if history else (a, C, J)
+
+
+def kmeans_warm(v_bf16_head: np.ndarray, init: np.ndarray, iters: int, history: bool = False):
+    """Lloyd k-means on one head's value rows started from the given
+    centroids init [k, d] (the previous grouping's centroids, carried across
+    denoising steps).  Returns (assign, centroids, J) or, with history=True,
+    (assign, centroids, J_hist[iters+1])."""
+    v = _c(v_bf16_head, np.uint16)
+    C0_ = _c(init, np.float32)
+    L, d = v.shape
+    k = C0_.shape[0]
+    a = np.empty(L, np.int32)
+    C = np.empty((k, d), np.float32)
+    hist = np.empty(iters + 1, np.float64) if history else None
+    J = lib().vco_kmeans_warm(_p(v), L, d, k, iters, _p(C0_), _p(a), _p(C), _p(hist))
     return (a, C, hist) if history else (a, C, J)
 
 

@@ -218,16 +218,16 @@ static double vco_objective(const float* x, int L, int d, const float* C, const 
     return J;
 }
 
-double vco_kmeans(const uint16_t* v, int L, int d, int k, int iters, uint64_t seed_bh,
-                  int32_t* assign, float* centroids, double* J_hist)
+/* Lloyd rounds from the given centroids (updated in place): each round
+ * assigns every row to its nearest centroid, then moves each non-empty
+ * cluster's centroid to the fp32-rounded fp64 mean of its members.  Returns
+ * J of the last assignment with the updated centroids (iters = 0: one
+ * assignment, centroids unchanged). */
+static double vco_lloyd(const float* x, int L, int d, int k, int iters, float* centroids, int32_t* assign,
+                        double* J_hist)
 {
-    float* x = (float*)malloc(sizeof(float) * (size_t)L * d);
-    int32_t* idx = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
     double* sum = (double*)malloc(sizeof(double) * (size_t)k * d);
     int64_t* cnt = (int64_t*)malloc(sizeof(int64_t) * (size_t)k);
-    for (int64_t i = 0; i < (int64_t)L * d; i++) x[i] = vco_bf16(v[i]);
-    vco_kmeans_init_indices(L, k, seed_bh, idx);
-    for (int c = 0; c < k; c++) memcpy(centroids + (int64_t)c * d, x + (int64_t)idx[c] * d, sizeof(float) * d);
     if (J_hist) {
         vco_assign(x, L, d, centroids, k, assign);
         J_hist[0] = vco_objective(x, L, d, centroids, assign);
@@ -253,7 +253,34 @@ double vco_kmeans(const uint16_t* v, int L, int d, int k, int iters, uint64_t se
         vco_assign(x, L, d, centroids, k, assign);
         J = vco_objective(x, L, d, centroids, assign);
     }
-    free(x); free(idx); free(sum); free(cnt);
+    free(sum); free(cnt);
+    return J;
+}
+
+double vco_kmeans(const uint16_t* v, int L, int d, int k, int iters, uint64_t seed_bh,
+                  int32_t* assign, float* centroids, double* J_hist)
+{
+    float* x = (float*)malloc(sizeof(float) * (size_t)L * d);
+    int32_t* idx = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
+    for (int64_t i = 0; i < (int64_t)L * d; i++) x[i] = vco_bf16(v[i]);
+    vco_kmeans_init_indices(L, k, seed_bh, idx);
+    for (int c = 0; c < k; c++) memcpy(centroids + (int64_t)c * d, x + (int64_t)idx[c] * d, sizeof(float) * d);
+    double J = vco_lloyd(x, L, d, k, iters, centroids, assign, J_hist);
+    free(x); free(idx);
+    return J;
+}
+
+/* k-means warm-started from caller centroids (a reading of the MarkTechPost
+ * abstract's grouping amortised across denoising steps: the clusters of one
+ * step seed the next): init [k, d] fp32, then the same Lloyd rounds. */
+double vco_kmeans_warm(const uint16_t* v, int L, int d, int k, int iters, const float* init,
+                       int32_t* assign, float* centroids, double* J_hist)
+{
+    float* x = (float*)malloc(sizeof(float) * (size_t)L * d);
+    for (int64_t i = 0; i < (int64_t)L * d; i++) x[i] = vco_bf16(v[i]);
+    memcpy(centroids, init, sizeof(float) * (size_t)k * d);
+    double J = vco_lloyd(x, L, d, k, iters, centroids, assign, J_hist);
+    free(x);
     return J;
 }
 

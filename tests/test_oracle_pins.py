@@ -584,3 +584,24 @@ def test_exp_then_cast_bytes_are_library_cast_of_exp2(oracle_mod):
     agree = float((bye[:, :128][big] == by[:, :128][big]).mean())
     assert np.abs(bye[:, :128][big].astype(int) - by[:, :128][big].astype(int)).max() <= 1
     assert abs(agree - GOLD["expcast_agreement_per_doubling"]["value"]) < 0.05, agree
+
+
+def test_kmeans_warm_start_composes(oracle_mod):
+    """Lloyd rounds compose: 8 rounds from the seeded init equal 4 rounds
+    followed by 4 more warm-started from the centroids those left (same
+    assignment, centroids and objective); a warm start with 0 rounds is the
+    nearest-centroid assignment of the given centroids."""
+    cfg = synth.CONFIGS[0]
+    q, k, v = synth.make_inputs(cfg, 0)
+    vh = v[0, 0]
+    a8, C8, J8 = oracle_mod.kmeans(vh, 8, 8, 99)
+    a4, C4, J4 = oracle_mod.kmeans(vh, 8, 4, 99)
+    aw, Cw, Jw = oracle_mod.kmeans_warm(vh, C4, 4)
+    assert np.array_equal(aw, a8) and np.array_equal(Cw, C8) and Jw == J8
+    a0, C0_, J0 = oracle_mod.kmeans_warm(vh, C8, 0)
+    x = oracle_mod.bf16_to_f32(vh).astype(np.float64)
+    d2 = ((x[:, None, :] - C8.astype(np.float64)[None]) ** 2).sum(-1)
+    assert np.array_equal(a0, d2.argmin(1)) and np.array_equal(C0_, C8)
+    # warm-starting from converged centroids does not raise the objective
+    _, _, hist = oracle_mod.kmeans_warm(vh, C8, 4, history=True)
+    assert np.all(np.diff(hist) <= 1e-9 * hist[0]) and hist[-1] <= J8 * (1 + 1e-12)

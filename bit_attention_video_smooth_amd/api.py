@@ -56,19 +56,35 @@ def workspace(B, H, L, d, *, kmeans_k=0, kmeans_iters=8, device="cuda") -> torch
 
 def prepare(q, k, v, *, perm_in=None, kmeans_k=0, kmeans_iters=8, seed=0, smooth_k=1,
             v_scale_mode=0, out: Prepared | None = None, ws: torch.Tensor | None = None,
+            centroids_in: torch.Tensor | None = None, centroids_out: torch.Tensor | None = None,
             stream=None) -> Prepared:
-    """vsmooth_prepare on bf16 [B,H,L,d] device tensors."""
+    """vsmooth_prepare on bf16 [B,H,L,d] device tensors; with centroids_in
+    and/or centroids_out (fp32 [B,H,k,d]) vsmooth_prepare_warm, whose k-means
+    starts from centroids_in (None: the seeded init) and leaves its final
+    centroids in centroids_out (may be the same tensor)."""
     B, H, L, d = q.shape
     for t in (q, k, v):
         assert t.dtype == torch.bfloat16 and t.is_contiguous() and t.shape == q.shape
     if perm_in is not None:
         assert perm_in.dtype == torch.int32 and perm_in.is_contiguous() and tuple(perm_in.shape) == (B, H, L)
+    warm = centroids_in is not None or centroids_out is not None
+    if warm:
+        if perm_in is not None:
+            raise ValueError("centroids and perm_in exclude each other (a warm start runs k-means)")
+        kk = kmeans_k if kmeans_k > 0 else nblocks(L)
+        for t in (centroids_in, centroids_out):
+            if t is not None:
+                assert t.dtype == torch.float32 and t.is_contiguous() and tuple(t.shape) == (B, H, kk, d)
     shape = _lib.shape_of(B, H, L, d)
     params = _lib.make_params(kmeans_k, kmeans_iters, seed, smooth_k, v_scale_mode)
     out = out if out is not None else alloc_prepared(B, H, L, d, q.device)
     if ws is None:
         ws = workspace(B, H, L, d, kmeans_k=kmeans_k, kmeans_iters=kmeans_iters, device=q.device)
-    _lib.vsmooth_prepare(shape, params, q, k, v, perm_in, out.c(), ws, ws.numel(), stream)
+    if warm:
+        _lib.vsmooth_prepare_warm(shape, params, q, k, v, centroids_in, centroids_out, out.c(), ws, ws.numel(),
+                                  stream)
+    else:
+        _lib.vsmooth_prepare(shape, params, q, k, v, perm_in, out.c(), ws, ws.numel(), stream)
     return out
 
 

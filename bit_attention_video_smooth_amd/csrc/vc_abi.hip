@@ -215,6 +215,65 @@ int sage_attention_common(const vc_shape* shape, const vc_sage_params* sp, const
                       "vc_sage_attention_fwd");
 }
 
+int prepare_common(const vc_shape* shape, const vsmooth_params* params, const void* q, const void* k,
+                   const void* v, const int32_t* perm_in, const float* cent_in, float* cent_out,
+                   const vc_prepared* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+    int r, kk;
+    if ((r = check_shape(shape))) return r;
+    if ((r = check_params(shape, params, &kk))) return r;
+    if ((r = check_ptr(q, "q")) || (r = check_ptr(k, "k")) || (r = check_ptr(v, "v"))) return r;
+    if ((r = check_prepared(out, false))) return r;
+    if ((r = check_ptr(out->perm, "perm"))) return r;
+    if (perm_in != nullptr && (r = check_ptr(perm_in, "perm_in"))) return r;
+    if (out->kmeans_obj != nullptr && (r = check_ptr(out->kmeans_obj, "kmeans_obj"))) return r;
+    if (cent_in != nullptr && (r = check_ptr(cent_in, "centroids_in"))) return r;
+    if (cent_out != nullptr && (r = check_ptr(cent_out, "centroids_out"))) return r;
+    const bool km = perm_in == nullptr;
+    const size_t need = prepare_ws(shape, km, kk);
+    if (ws == nullptr || ws_bytes < need)
+        return fail(VC_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws_bytes, need);
+    if (!aligned16(ws)) return fail(VC_ERR_INVALID, "ws is not 16-byte aligned");
+
+    const size_t BH = (size_t)shape->B * shape->H;
+    const int ns = vc::k_mean_splits((int)BH, shape->L);
+    uint8_t* wp = static_cast<uint8_t*>(ws);
+    vc::PrepareArgs a{};
+    a.B = shape->B; a.H = shape->H; a.L = shape->L; a.d = shape->d; a.nb = nblk(shape);
+    a.smooth_k = params->smooth_k;
+    a.v_mode = params->v_scale_mode;
+    a.q = q; a.k = k; a.v = v;
+    a.perm = out->perm;
+    a.q8 = out->q8; a.k8 = out->k8; a.v8 = out->v8;
+    a.q_scale = out->q_scale; a.k_scale = out->k_scale; a.v_scale = out->v_scale; a.v_mean = out->v_mean;
+    a.kpartial = reinterpret_cast<double*>(wp);
+    wp += a256(BH * ns * shape->d * sizeof(double));
+    a.kbar = reinterpret_cast<float*>(wp);
+    wp += a256(BH * shape->d * sizeof(float));
+
+    hipError_t e;
+    if (km) {
+        vc::KmeansArgs m{};
+        m.B = shape->B; m.H = shape->H; m.L = shape->L; m.d = shape->d;
+        m.k = kk;
+        m.iters = params->kmeans_iters;
+        m.seed = params->seed;
+        m.v = v;
+        m.perm = out->perm;
+        m.obj = out->kmeans_obj;
+        m.cent_in = cent_in;
+        m.cent_out = cent_out;
+        vc::kmeans_carve(m, wp);
+        e = vc::launch_kmeans(m, stream);
+        if (e != hipSuccess) return hip_status(e, "k-means");
+    } else {
+        // plain kernels rather than memcpy/memset nodes, so the call can be graph-captured
+        e = vc::launch_copy_perm(perm_in, out->perm, BH * (size_t)shape->L, out->kmeans_obj, BH, stream);
+        if (e != hipSuccess) return hip_status(e, "perm copy");
+    }
+    return hip_status(vc::launch_prepare_quant(a, stream), "vsmooth_prepare");
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -252,55 +311,14 @@ int vsmooth_workspace_bytes(const vc_shape* shape, const vsmooth_params* params,
 int vsmooth_prepare(const vc_shape* shape, const vsmooth_params* params, const void* q, const void* k,
                     const void* v, const int32_t* perm_in, const vc_prepared* out, void* ws,
                     size_t ws_bytes, hipStream_t stream) {
-    int r, kk;
-    if ((r = check_shape(shape))) return r;
-    if ((r = check_params(shape, params, &kk))) return r;
-    if ((r = check_ptr(q, "q")) || (r = check_ptr(k, "k")) || (r = check_ptr(v, "v"))) return r;
-    if ((r = check_prepared(out, false))) return r;
-    if ((r = check_ptr(out->perm, "perm"))) return r;
-    if (perm_in != nullptr && (r = check_ptr(perm_in, "perm_in"))) return r;
-    if (out->kmeans_obj != nullptr && (r = check_ptr(out->kmeans_obj, "kmeans_obj"))) return r;
-    const bool km = perm_in == nullptr;
-    const size_t need = prepare_ws(shape, km, kk);
-    if (ws == nullptr || ws_bytes < need)
-        return fail(VC_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws_bytes, need);
-    if (!aligned16(ws)) return fail(VC_ERR_INVALID, "ws is not 16-byte aligned");
+    return prepare_common(shape, params, q, k, v, perm_in, nullptr, nullptr, out, ws, ws_bytes, stream);
+}
 
-    const size_t BH = (size_t)shape->B * shape->H;
-    const int ns = vc::k_mean_splits((int)BH, shape->L);
-    uint8_t* wp = static_cast<uint8_t*>(ws);
-    vc::PrepareArgs a{};
-    a.B = shape->B; a.H = shape->H; a.L = shape->L; a.d = shape->d; a.nb = nblk(shape);
-    a.smooth_k = params->smooth_k;
-    a.v_mode = params->v_scale_mode;
-    a.q = q; a.k = k; a.v = v;
-    a.perm = out->perm;
-    a.q8 = out->q8; a.k8 = out->k8; a.v8 = out->v8;
-    a.q_scale = out->q_scale; a.k_scale = out->k_scale; a.v_scale = out->v_scale; a.v_mean = out->v_mean;
-    a.kpartial = reinterpret_cast<double*>(wp);
-    wp += a256(BH * ns * shape->d * sizeof(double));
-    a.kbar = reinterpret_cast<float*>(wp);
-    wp += a256(BH * shape->d * sizeof(float));
-
-    hipError_t e;
-    if (km) {
-        vc::KmeansArgs m{};
-        m.B = shape->B; m.H = shape->H; m.L = shape->L; m.d = shape->d;
-        m.k = kk;
-        m.iters = params->kmeans_iters;
-        m.seed = params->seed;
-        m.v = v;
-        m.perm = out->perm;
-        m.obj = out->kmeans_obj;
-        vc::kmeans_carve(m, wp);
-        e = vc::launch_kmeans(m, stream);
-        if (e != hipSuccess) return hip_status(e, "k-means");
-    } else {
-        // plain kernels rather than memcpy/memset nodes, so the call can be graph-captured
-        e = vc::launch_copy_perm(perm_in, out->perm, BH * (size_t)shape->L, out->kmeans_obj, BH, stream);
-        if (e != hipSuccess) return hip_status(e, "perm copy");
-    }
-    return hip_status(vc::launch_prepare_quant(a, stream), "vsmooth_prepare");
+int vsmooth_prepare_warm(const vc_shape* shape, const vsmooth_params* params, const void* q, const void* k,
+                         const void* v, const float* centroids_in, float* centroids_out, const vc_prepared* out,
+                         void* ws, size_t ws_bytes, hipStream_t stream) {
+    return prepare_common(shape, params, q, k, v, nullptr, centroids_in, centroids_out, out, ws, ws_bytes,
+                          stream);
 }
 
 int vc_attention_fwd(const vc_shape* shape, const vc_attn_params* params, const vc_prepared* in,

@@ -41,6 +41,8 @@ struct KmeansArgs {
     const void* v;         // bf16 [B,H,L,d]
     int32_t* perm;         // out [B,H,L]
     double* obj;           // out [B,H] or null
+    const float* cent_in;  // [B,H,k,d] initial centroids, or null (seeded init)
+    float* cent_out;       // [B,H,k,d] final centroids, or null
     // workspace
     float* cent;           // [BH, kpad, d] fp32 centroids
     uint16_t* cent_hi;     // [BH, kpad, d] bf16 high part

@@ -52,6 +52,21 @@ __global__ void km_init(const uint16_t* __restrict__ v, float* __restrict__ cent
         cent[((size_t)bh * kpad + c) * d + e] = bf16_to_f32(v[((size_t)bh * L + j) * d + e]);
 }
 
+// warm start: caller centroids [BH, k, d] into the padded workspace rows, and
+// the final centroids back out (plain copy kernels, so a captured graph holds
+// no copy nodes)
+__global__ void km_init_from(const float* __restrict__ src, float* __restrict__ cent, int d, int k, int kpad) {
+    const int c = blockIdx.x, bh = blockIdx.y;
+    for (int e = threadIdx.x; e < d; e += blockDim.x)
+        cent[((size_t)bh * kpad + c) * d + e] = src[((size_t)bh * k + c) * d + e];
+}
+
+__global__ void km_copy_out(const float* __restrict__ cent, float* __restrict__ dst, int d, int k, int kpad) {
+    const int c = blockIdx.x, bh = blockIdx.y;
+    for (int e = threadIdx.x; e < d; e += blockDim.x)
+        dst[((size_t)bh * k + c) * d + e] = cent[((size_t)bh * kpad + c) * d + e];
+}
+
 // fp32 centroids -> bf16 high and low parts (round to nearest even) and the
 // squared norm (padding rows: zeros and +inf norm, never chosen)
 __global__ void km_split(const float* __restrict__ cent, uint16_t* __restrict__ hi,
@@ -439,8 +454,11 @@ hipError_t launch_kmeans_t(const KmeansArgs& a, hipStream_t st) {
     const int BH = a.B * a.H;
     const uint16_t* v = static_cast<const uint16_t*>(a.v);
     const int ntile = (a.L + ATOK - 1) / ATOK;
-    hipLaunchKernelGGL(km_init, dim3(a.k, BH), dim3(64), 0, st, v, a.cent, a.L, D, a.k, a.kpad, a.H,
-                       a.seed);
+    if (a.cent_in != nullptr)
+        hipLaunchKernelGGL(km_init_from, dim3(a.k, BH), dim3(64), 0, st, a.cent_in, a.cent, D, a.k, a.kpad);
+    else
+        hipLaunchKernelGGL(km_init, dim3(a.k, BH), dim3(64), 0, st, v, a.cent, a.L, D, a.k, a.kpad, a.H,
+                           a.seed);
     const int rounds = a.iters > 0 ? a.iters : 1;
     for (int it = 0; it < rounds; it++) {
         hipLaunchKernelGGL(km_split, dim3(a.kpad, BH), dim3(64), 0, st, a.cent, a.cent_hi, a.cent_lo,
@@ -457,6 +475,8 @@ hipError_t launch_kmeans_t(const KmeansArgs& a, hipStream_t st) {
             hipLaunchKernelGGL((km_update<D>), dim3(a.k, BH), dim3(256), 0, st, v, a.perm, a.counts,
                                a.offsets, a.cent, a.L, a.k, a.kpad);
     }
+    if (a.cent_out != nullptr)
+        hipLaunchKernelGGL(km_copy_out, dim3(a.k, BH), dim3(64), 0, st, a.cent, a.cent_out, D, a.k, a.kpad);
     if (a.obj) {
         hipLaunchKernelGGL((km_objective<D>), dim3(a.nchunk, BH), dim3(256), 0, st, v, a.assign, a.cent,
                            a.obj_part, a.L, a.kpad, a.nchunk);

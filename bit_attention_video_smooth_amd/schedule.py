@@ -12,6 +12,11 @@ s < ceil(group_frac * N) and s is a multiple of `reuse`; every other step
 takes the permutation of the latest grouping (so after the first quarter the
 permutation is frozen).  Each attention layer keeps its own permutation.
 
+Optionally (warm_start=True) each grouping after the first starts k-means
+from the centroids the previous grouping ended with, instead of the seeded
+init: the clusters of adjacent denoising steps are close, so the Lloyd
+rounds start near their fixed point.
+
 Host logic only: every step still runs the library's prepare (with or
 without k-means) and attention kernels.
 """
@@ -58,10 +63,12 @@ class VCAttentionLayer:
     """One attention layer's state across the denoising steps: the prepared
     buffers, the prepare workspace and the current permutation (in
     `prepared.perm`).  `forward` runs one step: prepare (with k-means on a
-    grouping step, else with the layer's permutation) and attention."""
+    grouping step, else with the layer's permutation) and attention.  With
+    warm_start the layer also keeps the k-means centroids of its latest
+    grouping and starts the next grouping from them."""
 
     def __init__(self, B, H, L, d, schedule: GroupingSchedule, *, seed=0, kmeans_iters=8, v_scale_mode=0,
-                 z_off=8, skip_lambda=0.0, device="cuda"):
+                 z_off=8, skip_lambda=0.0, warm_start=False, device="cuda"):
         self.shape = (B, H, L, d)
         self.schedule = schedule
         self.seed, self.kmeans_iters, self.v_scale_mode = seed, kmeans_iters, v_scale_mode
@@ -70,14 +77,21 @@ class VCAttentionLayer:
         self.ws = api.workspace(B, H, L, d, kmeans_iters=kmeans_iters, device=device)
         self.out = torch.empty((B, H, L, d), dtype=torch.float32, device=device)
         self.grouped_at = None  # step of the latest grouping
+        self.warm_start = warm_start
+        self.centroids = (torch.empty((B, H, api.nblocks(L), d), dtype=torch.float32, device=device)
+                          if warm_start else None)
 
     def forward(self, q, k, v, step: int, stream=None) -> torch.Tensor:
         if tuple(q.shape) != self.shape:
             raise ValueError("shape %s, layer built for %s" % (tuple(q.shape), self.shape))
         regroup = self.schedule.regroup(step) or self.grouped_at is None
-        api.prepare(q, k, v, perm_in=None if regroup else self.prepared.perm, kmeans_iters=self.kmeans_iters,
-                    seed=self.seed, v_scale_mode=self.v_scale_mode, out=self.prepared, ws=self.ws,
-                    stream=stream)
+        common = dict(kmeans_iters=self.kmeans_iters, seed=self.seed, v_scale_mode=self.v_scale_mode,
+                      out=self.prepared, ws=self.ws, stream=stream)
+        if regroup and self.warm_start:
+            api.prepare(q, k, v, centroids_in=None if self.grouped_at is None else self.centroids,
+                        centroids_out=self.centroids, **common)
+        else:
+            api.prepare(q, k, v, perm_in=None if regroup else self.prepared.perm, **common)
         if regroup:
             self.grouped_at = step
         return api.attention(self.prepared, z_off=self.z_off, out=self.out, skip_lambda=self.skip_lambda,

@@ -123,6 +123,20 @@ int vsmooth_prepare(const vc_shape* shape, const vsmooth_params* params, const v
                     const void* k, const void* v, const int32_t* perm_in,
                     const vc_prepared* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* vsmooth_prepare with the k-means state carried across calls (denoising
+ * steps), a reading of the MarkTechPost abstract's grouping amortised over
+ * the schedule: the clusters found at one grouping step start the next.
+ * Always runs k-means (there is no perm_in).  centroids_in: NULL for the
+ * seeded init, else fp32 [B,H,k,d] initial centroids (k = kmeans_k, or nb
+ * when kmeans_k <= 0).  centroids_out: NULL, or fp32 [B,H,k,d] that receives
+ * the centroids after the last Lloyd round (the member means of the final
+ * assignment); it may be centroids_in itself.  Everything else, including
+ * the workspace size, as vsmooth_prepare. */
+int vsmooth_prepare_warm(const vc_shape* shape, const vsmooth_params* params, const void* q,
+                         const void* k, const void* v, const float* centroids_in,
+                         float* centroids_out, const vc_prepared* out, void* ws, size_t ws_bytes,
+                         hipStream_t stream);
+
 /* Attention parameters. */
 typedef struct vc_attn_params {
     int32_t z_off;     /* ExpCast offset in 0..8: the running row maximum is

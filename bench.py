@@ -259,6 +259,7 @@ def main():
                 "objective_ratio_vs_seeded_8": {"mean": float(ratio.mean()), "max": float(ratio.max())},
                 "drift": "v + 0.05 N(0,1) between the two steps"}
         del v2
+        api.prepare(q, k, v, seed=args.config, v_scale_mode=args.v_scale_mode, out=P, ws=ws)  # restore P
         print("warm start: prepare %.3f ms, objective ratio %.4f" % (warm_ms, float(ratio.mean())),
               file=sys.stderr, flush=True)
 

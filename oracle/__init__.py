@@ -73,7 +73,13 @@ def lib():
             L.vco_c0.restype = f32
             L.vco_c0.argtypes = [i32]
             L.vco_attention_rows.argtypes = [i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P,
-                                             i32, i32, P, P, P, P, P, f32]
+                                             i32, i32, P, P, P, P, P, f32, P]
+            L.vco_e2m1_decode.restype = ctypes.c_double
+            L.vco_e2m1_decode.argtypes = [ctypes.c_uint8]
+            L.vco_e2m1_encode_array.argtypes = [P, P, i64]
+            L.vco_e8m0_exp.restype = i32
+            L.vco_e8m0_exp.argtypes = [ctypes.c_double]
+            L.vco_prepare_head_fp4v.argtypes = [P, P, P, i32, i32, i32, P, P, P, P, P, P, P, P]
             L.vco_sage_prepare_head.argtypes = [P, P, P, i32, i32, i32, i32, P, P, P, P, P, P]
             L.vco_sage_rows.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P, P, i32, i32, P, P, P, P]
             L.vco_num_threads.restype = i32
@@ -299,7 +305,7 @@ def attention_head(prep: dict, L: int, z_off: int = 8, rows=None, want_bytes=Fal
         assert sin.shape == (r1 - r0, Lp)
     lib().vco_attention_rows(2 if prob_cast else 0, L, d, z_off, _p(q8), _p(k8), _p(v8), _p(qs), _p(ks), _p(vs),
                              _p(vm), None, None, None, r0, r1, _p(out), _p(by), _p(S), _p(y), _p(sin),
-                             skip_threshold(skip_lambda))
+                             skip_threshold(skip_lambda), None)
     return (out, by, S, y) if want_bytes else out
 
 
@@ -325,7 +331,7 @@ def attention_exact_blockwise(qf, kf_perm, v_perm, v_mean, skip_lambda: float = 
     out = np.empty((L, d), np.float32)
     lib().vco_attention_rows(1, L, d, 8, None, None, None, None, None, None, _p(vm),
                              _p(qf), _p(kf), _p(rf), 0, L, _p(out), None, None, None, None,
-                             skip_threshold(skip_lambda))
+                             skip_threshold(skip_lambda), None)
     return out
 
 
@@ -378,6 +384,71 @@ def sage_attention_head(prep: dict, L: int, qk_dtype: str = "int8", z_off: int =
     lib().vco_sage_rows(prob_cast, SAGE_QK[qk_dtype], L, d, z_off, _p(q8), _p(k8), _p(v8), _p(qs), _p(ks),
                         _p(vs), r0, r1, _p(out), _p(by), _p(S), _p(sin))
     return (out, by, S) if want_bytes else out
+
+
+# --------------------------------------------------------------------------
+# 4-bit V-Smooth (MarkTechPost abstract: 4-bit V-Smooth; ExpCast applies to
+# the 8-bit kernel only): E2M1 residual and probabilities with power-of-two
+# (E8M0) scales per 32-key group.  Readings in vc_oracle.c.
+# --------------------------------------------------------------------------
+
+def e2m1_decode(c) -> np.ndarray:
+    c = np.asarray(c, np.uint8)
+    table = np.array([lib().vco_e2m1_decode(t) for t in range(16)], np.float64)
+    return table[c & 15]
+
+
+def e2m1_encode(x) -> np.ndarray:
+    x = _c(x, np.float64)
+    out = np.empty(x.shape, np.uint8)
+    lib().vco_e2m1_encode_array(_p(x), _p(out), x.size)
+    return out
+
+
+def e8m0_exp(A: float) -> int:
+    return int(lib().vco_e8m0_exp(float(A)))
+
+
+def prepare_head_fp4v(q, k, v, perm, smooth_k: int = 1):
+    """As prepare_head, with the V residual in E2M1: v4 [nb, d, 128] codes
+    (natural key order) and v_exp [nb, d, 4] (e + 127 per key group) in
+    place of v8 and v_scale."""
+    q, k, v = (_c(a, np.uint16) for a in (q, k, v))
+    perm = _c(perm, np.int32)
+    L, d = q.shape
+    nb = nblocks(L)
+    Lp = nb * BLK
+    o = dict(q8=np.empty((Lp, d), np.uint8), k8=np.empty((Lp, d), np.uint8),
+             v4=np.empty((nb, d, BLK), np.uint8), v_exp=np.empty((nb, d, 4), np.uint8),
+             q_scale=np.empty(nb, np.float32), k_scale=np.empty(nb, np.float32),
+             v_mean=np.empty((nb, d), np.float32))
+    lib().vco_prepare_head_fp4v(_p(q), _p(k), _p(v), L, d, smooth_k, _p(perm), _p(o["q8"]), _p(o["k8"]),
+                                _p(o["v4"]), _p(o["v_exp"]), _p(o["q_scale"]), _p(o["k_scale"]),
+                                _p(o["v_mean"]))
+    return o
+
+
+def attention_head_fp4v(prep: dict, L: int, z_off: int = 8, rows=None, want_bytes=False, scores=None):
+    """4-bit P V (mode 3) for one head from prepare_head_fp4v() output.
+    Returns O [r1-r0, d] fp32 (with want_bytes also the E2M1 codes of P, the
+    scores and the values phat, each [r1-r0, Lp])."""
+    q8, k8, v4, ve = (_c(prep[n], np.uint8) for n in ("q8", "k8", "v4", "v_exp"))
+    qs, ks, vm = (_c(prep[n], np.float32) for n in ("q_scale", "k_scale", "v_mean"))
+    d = q8.shape[1]
+    Lp = k8.shape[0]
+    r0, r1 = (0, L) if rows is None else rows
+    out = np.empty((r1 - r0, d), np.float32)
+    by = np.empty((r1 - r0, Lp), np.uint8) if want_bytes else None
+    S = np.empty((r1 - r0, Lp), np.float32) if want_bytes else None
+    y = np.empty((r1 - r0, Lp), np.float32) if want_bytes else None
+    sin = None
+    if scores is not None:
+        sin = _c(scores, np.float32)
+        assert sin.shape == (r1 - r0, Lp)
+    lib().vco_attention_rows(3, L, d, z_off, _p(q8), _p(k8), _p(v4), _p(qs), _p(ks), None, _p(vm),
+                             None, None, None, r0, r1, _p(out), _p(by), _p(S), _p(y), _p(sin),
+                             np.float32(-np.inf), _p(ve))
+    return (out, by, S, y) if want_bytes else out
 
 
 def num_threads() -> int:

@@ -119,6 +119,52 @@ void vco_e4m3_decode_array(const uint8_t* b, double* out, int64_t n)
 }
 
 /* ------------------------------------------------------------------------ */
+/* E2M1 (the 4-bit element format of the OCP MX formats, FP4), written from   */
+/* the format: sign bit, 2 exponent bits with bias 1, 1 mantissa bit;        */
+/* exponent field 0 is subnormal (value = m / 2).  Magnitudes 0, 0.5, 1,     */
+/* 1.5, 2, 3, 4, 6; no infinities, no NaN.                                  */
+/* ------------------------------------------------------------------------ */
+
+double vco_e2m1_decode(uint8_t c)
+{
+    int s = (c >> 3) & 1, e = (c >> 1) & 3, m = c & 1;
+    double v = (e == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return s ? -v : v;
+}
+
+/* Saturating round-to-nearest-even: the nearest of the eight magnitudes,
+ * a tie going to the code whose mantissa bit is 0; |x| >= 6 gives 6. */
+uint8_t vco_e2m1_encode(double x)
+{
+    uint8_t s = (x < 0.0 || (x == 0.0 && signbit(x))) ? 8 : 0;
+    double a = fabs(x);
+    if (a >= 6.0) return s | 7;
+    int best = 0;
+    for (int c = 1; c < 8; c++) {
+        double dc = fabs(a - vco_e2m1_decode((uint8_t)c)), db = fabs(a - vco_e2m1_decode((uint8_t)best));
+        if (dc < db || (dc == db && (c & 1) == 0)) best = c;
+    }
+    return s | (uint8_t)best;
+}
+
+void vco_e2m1_encode_array(const double* x, uint8_t* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; i++) out[i] = vco_e2m1_encode(x[i]);
+}
+
+/* Power-of-two (E8M0) scale of an FP4 group with amax A: the least e with
+ * A <= 6 * 2^e, so no element clips; A < 2^-100 gives e = -127 and the
+ * group's codes are all 0. */
+int vco_e8m0_exp(double A)
+{
+    if (!(A >= ldexp(1.0, -100))) return -127;
+    int e = (int)floor(log2(A)) - 4;
+    while (!(A <= 6.0 * ldexp(1.0, e))) e++;
+    while (e > -127 && A <= 6.0 * ldexp(1.0, e - 1)) e--;
+    return e;
+}
+
+/* ------------------------------------------------------------------------ */
 /* SplitMix64 (Steele, Lea & Flood, OOPSLA 2014; finaliser "Mix13" of        */
 /* D. Stafford as in Vigna's public-domain reference).  Output i (0-based)    */
 /* of the stream started at `seed` is mix(seed + (i+1)*gamma): a counter-     */
@@ -403,6 +449,53 @@ void vco_prepare_head(const uint16_t* q, const uint16_t* k, const uint16_t* v, i
 }
 
 /* ------------------------------------------------------------------------ */
+/* 4-bit V-Smooth ([MTP] abstract: 4-bit V-Smooth on workstation cards;     */
+/* ExpCast has no 4-bit form).  Readings: Q and K as the 8-bit path (per-    */
+/* block FP8); the same exact block mean; the residual r = fp32(v - mean)   */
+/* quantised to E2M1 with one power-of-two scale per (block, channel, key   */
+/* group), the group of key kk in its block being (kk mod 16) div 4 -- the  */
+/* 32-key blocks along k of the matrix-core product that consumes it.       */
+/* Outputs as vco_prepare_head, except v4 [nb, d, 128] (one E2M1 code per    */
+/* byte, natural key order, 0 for padded keys) and v_exp [nb, d, 4] (e +     */
+/* 127 of each group's scale 2^e) in place of v8 / v_scale.                 */
+/* ------------------------------------------------------------------------ */
+
+void vco_prepare_head_fp4v(const uint16_t* q, const uint16_t* k, const uint16_t* v, int L, int d,
+                           int smooth_k, const int32_t* perm, uint8_t* q8, uint8_t* k8, uint8_t* v4,
+                           uint8_t* v_exp, float* q_scale, float* k_scale, float* v_mean)
+{
+    int nb = (L + VCO_BLK - 1) / VCO_BLK;
+    uint8_t* v8 = (uint8_t*)malloc((size_t)nb * d * VCO_BLK);
+    float* vs = (float*)malloc(sizeof(float) * (size_t)nb * d);
+    vco_prepare_head(q, k, v, L, d, smooth_k, 0, perm, q8, k8, v8, q_scale, k_scale, vs, v_mean, NULL);
+    free(v8);
+    free(vs);
+    float r[VCO_BLK];
+    for (int b = 0; b < nb; b++) {
+        int i0 = b * VCO_BLK;
+        int n = (L - i0 < VCO_BLK) ? L - i0 : VCO_BLK;
+        for (int c = 0; c < d; c++) {
+            float mu = v_mean[(int64_t)b * d + c];
+            for (int j = 0; j < VCO_BLK; j++) {
+                volatile float t = (j < n) ? vco_bf16(v[(int64_t)perm[i0 + j] * d + c]) - mu : 0.0f;
+                r[j] = t;
+            }
+            for (int g = 0; g < 4; g++) {
+                double A = 0.0;
+                for (int j = 0; j < n; j++)
+                    if ((j % 16) / 4 == g && fabs((double)r[j]) > A) A = fabs((double)r[j]);
+                int e = vco_e8m0_exp(A);
+                v_exp[((int64_t)b * d + c) * 4 + g] = (uint8_t)(e + 127);
+                for (int j = 0; j < VCO_BLK; j++)
+                    if ((j % 16) / 4 == g)
+                        v4[((int64_t)b * d + c) * VCO_BLK + j] =
+                            (j < n && e > -127) ? vco_e2m1_encode(ldexp((double)r[j], -e)) : 0;
+            }
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* ExpCast-FP8 ([MTP] abstract, [AIK]): y = fma(S, c8, krow) with            */
 /* c8 = 8 c_b and krow = KB - 8 m; byte = min(max(rne(y), 0), 126).          */
 /* ------------------------------------------------------------------------ */
@@ -447,6 +540,13 @@ float vco_c0(int d) { return (float)(1.4426950408889634074 / sqrt((double)d)); }
 /*   2^z correctly rounded to fp32, E4M3 round to nearest even ([MTP]       */
 /*   abstract: ExpCast is compared with computing the FP32 exponential and  */
 /*   casting it to FP8).                                                    */
+/* mode 3 (4-bit P V, with vco_prepare_head_fp4v inputs): p_j as mode 2     */
+/*   before the cast, fp32(2^z_j); per key group G of the block (key j in   */
+/*   group (j mod 16) div 4), e_G = the E8M0 rule on max_{j in G} p_j and     */
+/*   phat_j = 2^e_G E2M1(p_j / 2^e_G); l_b = sum phat_j; acc_c = fp32(sum_j  */
+/*   phat_j rhat_jc), rhat_jc = 2^(v_exp - 127) E2M1 code value; O = alpha O */
+/*   + acc + l_b mu_b (no separate V scale).  bytes_out holds the E2M1 codes */
+/*   and y_out the values phat.                                             */
 /* mode 1 (exact algebra, for checking the blockwise bookkeeping):          */
 /*   qhat, khat, rhat are the real values (scales 1), S is a double sum,      */
 /*   p_j = 2^(S_j C0 - m') in double; the rest as in mode 0.  With mode 1 the */
@@ -478,7 +578,7 @@ void vco_attention_rows(int mode, int L, int d, int z_off,
                         const float* v_scale, const float* v_mean,
                         const double* qf, const double* kf, const double* rf,
                         int r0, int r1, float* out, uint8_t* bytes_out, float* S_out,
-                        float* y_out, const float* S_in, float skip_thr)
+                        float* y_out, const float* S_in, float skip_thr, const uint8_t* v_exp)
 {
     int nb = (L + VCO_BLK - 1) / VCO_BLK;
     int64_t Lp = (int64_t)nb * VCO_BLK;
@@ -497,6 +597,7 @@ void vco_attention_rows(int mode, int L, int d, int z_off,
         double* p = (double*)malloc(sizeof(double) * VCO_BLK);
         for (int c = 0; c < d; c++)
             qrow[c] = (mode != 1) ? dec[q8[(int64_t)i * d + c]] : qf[(int64_t)i * d + c];
+        double* p4 = (double*)malloc(sizeof(double) * VCO_BLK);
         double m = -INFINITY, l = 0.0;
         for (int b = 0; b < nb; b++) {
             int n = (L - b * VCO_BLK < VCO_BLK) ? L - b * VCO_BLK : VCO_BLK;
@@ -515,7 +616,7 @@ void vco_attention_rows(int mode, int L, int d, int z_off,
                 Sd[j] = acc;
                 S[j] = (float)acc;
             }
-            if (mode == 0 || mode == 2) {
+            if (mode == 0 || mode == 2 || mode == 3) {
                 volatile float sqk = q_scale[i / VCO_BLK] * k_scale[b];
                 volatile float cb = sqk * C0;
                 float mx = -INFINITY;
@@ -538,7 +639,28 @@ void vco_attention_rows(int mode, int L, int d, int z_off,
                 volatile float krow = KB - e8;
                 volatile float c8 = 8.0f * cb;
                 volatile float zrow = (float)z_off - mnf;
-                for (int j = 0; j < VCO_BLK; j++) {
+                if (mode == 3) {
+                    /* fp32 probabilities, then one E8M0 scale and E2M1 codes per key group */
+                    for (int j = 0; j < VCO_BLK; j++) p4[j] = (j < n) ? (double)(float)exp2((double)fmaf(S[j], cb, zrow)) : 0.0;
+                    for (int g = 0; g < 4; g++) {
+                        double A = 0.0;
+                        for (int j = 0; j < n; j++)
+                            if ((j % 16) / 4 == g && p4[j] > A) A = p4[j];
+                        int e = vco_e8m0_exp(A);
+                        for (int j = 0; j < VCO_BLK; j++) {
+                            if ((j % 16) / 4 != g) continue;
+                            uint8_t code = (j < n && e > -127) ? vco_e2m1_encode(ldexp(p4[j], -e)) : 0;
+                            double ph = vco_e2m1_decode(code) * ldexp(1.0, e);
+                            int64_t o = (int64_t)(i - r0) * Lp + b * VCO_BLK + j;
+                            if (bytes_out) bytes_out[o] = code;
+                            if (S_out) S_out[o] = (j < n) ? S[j] : 0.0f;
+                            if (y_out) y_out[o] = (float)ph;
+                            p[j] = ph;
+                            if (j < n) ell += ph;
+                        }
+                    }
+                }
+                for (int j = 0; j < VCO_BLK && mode != 3; j++) {
                     uint8_t by = 0;
                     if (j < n)
                         by = (mode == 0) ? vco_expcast1(S[j], c8, krow)
@@ -562,9 +684,15 @@ void vco_attention_rows(int mode, int L, int d, int z_off,
             for (int c = 0; c < d; c++) {
                 int64_t vr = ((int64_t)b * d + c) * VCO_BLK;
                 double acc = 0.0;
-                for (int j = 0; j < n; j++)
-                    acc += p[j] * ((mode != 1) ? dec[v8[vr + j]] : rf[vr + j]);
-                double sv = (mode != 1) ? (double)v_scale[(int64_t)b * d + c] : 1.0;
+                for (int j = 0; j < n; j++) {
+                    double rv;
+                    if (mode == 3)
+                        rv = vco_e2m1_decode(v8[vr + j]) * ldexp(1.0, (int)v_exp[((int64_t)b * d + c) * 4 + (j % 16) / 4] - 127);
+                    else
+                        rv = (mode != 1) ? dec[v8[vr + j]] : rf[vr + j];
+                    acc += p[j] * rv;
+                }
+                double sv = (mode == 1 || mode == 3) ? 1.0 : (double)v_scale[(int64_t)b * d + c];
                 double accr = (mode != 1) ? (double)(float)acc : acc;
                 O[c] = alpha * O[c] + sv * accr + ell * (double)v_mean[(int64_t)b * d + c];
             }
@@ -572,7 +700,7 @@ void vco_attention_rows(int mode, int L, int d, int z_off,
             m = m_new;
         }
         for (int c = 0; c < d; c++) out[(int64_t)(i - r0) * d + c] = (float)(O[c] / l);
-        free(qrow); free(O); free(Sd); free(S); free(p);
+        free(qrow); free(O); free(Sd); free(S); free(p); free(p4);
     }
 }
 

@@ -24,6 +24,7 @@ sys.path.insert(0, ROOT)
 
 FP8_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 matrix peak
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense BF16 matrix peak
+FP4_PEAK_TFLOPS = 10100.0  # MI355X dense FP4 matrix peak
 HBM_PEAK_GBS = 8000.0
 
 
@@ -38,6 +39,7 @@ def parse():
     p.add_argument("--no-bf16", action="store_true")
     p.add_argument("--no-sage", action="store_true", help="skip the SAGE-style baseline leg")
     p.add_argument("--no-warm", action="store_true", help="skip the k-means warm-start leg")
+    p.add_argument("--no-fp4", action="store_true", help="skip the 4-bit V-Smooth leg")
     p.add_argument("--v-scale-mode", type=int, default=0)
     p.add_argument("--skip-lambda", type=float, default=0.5,
                    help="Skip Softmax threshold of the extra, reported (not timed-step) attention run; 0: none")
@@ -263,6 +265,32 @@ def main():
         print("warm start: prepare %.3f ms, objective ratio %.4f" % (warm_ms, float(ratio.mean())),
               file=sys.stderr, flush=True)
 
+    # 4-bit V-Smooth (E2M1 residual and probabilities, power-of-two scales per
+    # 32-key group, scaled FP4 matrix cores) on the same inputs and permutation
+    fp4 = None
+    P4 = None
+    if not args.no_fp4:
+        P4 = api.alloc_prepared(B, H, L, d)
+        api.prepare(q, k, v, perm_in=P.perm, out=P4, ws=ws, v_format=1)
+        api.attention(P4, out=out)
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for _ in range(args.steps):
+            api.prepare(q, k, v, perm_in=P.perm, out=P4, ws=ws, v_format=1)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        p4_ms = ev[0].elapsed_time(ev[1]) / args.steps
+        ev[0].record(stream)
+        for _ in range(args.steps):
+            api.attention(P4, out=out)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        a4_ms = ev[0].elapsed_time(ev[1]) / args.steps
+        fp4 = {"prepare_ms_without_kmeans": p4_ms, "attention_ms": a4_ms, "tflops": flop / a4_ms / 1e9,
+               "frac_fp4_peak": flop / a4_ms / 1e9 / FP4_PEAK_TFLOPS,
+               "vs_fp8_expcast": attn_ms / a4_ms, "vs_fp8_exp_then_cast": naive_ms / a4_ms}
+        print("fp4 V-Smooth: prepare %.3f ms, attention %.3f ms" % (p4_ms, a4_ms), file=sys.stderr, flush=True)
+
     # SAGE-style baseline (TensorRT-LLM blog, "Quantized Attention": one Q
     # scale per token, one K scale per 16 keys, INT8 or FP8 QK^T, FP8 PV with
     # one V scale per channel, exp-then-cast P) on the same inputs
@@ -297,7 +325,8 @@ def main():
 
     # V-Smooth token-ordering ablation on this workload (prepare outputs of
     # the library; statistics averaged over heads)
-    from bit_attention_video_smooth_amd.ablation import cube_permutation, sage_value_stats, value_stats
+    from bit_attention_video_smooth_amd.ablation import (cube_permutation, fp4_value_stats, sage_value_stats,
+                                                         value_stats)
     ablation = {}
     orders = {"sequence": torch.arange(L, dtype=torch.int32, device="cuda").expand(B, H, L).contiguous(),
               "static_cube_2x8x8": torch.from_numpy(cube_permutation(cfg.grid)).cuda().expand(B, H, L).contiguous(),
@@ -309,6 +338,9 @@ def main():
         ablation[name] = {"energy_removed": float(st["energy_removed"].mean()),
                           "v_rel_err": float(st["v_rel_err"].mean())}
     del Pa
+    if P4 is not None:  # the 4-bit residual in k-means order
+        ablation["kmeans_fp4_residual"] = {"v_rel_err": float(fp4_value_stats(P4, v)["v_rel_err"].mean())}
+        del P4
     if SP is not None:  # the SAGE recipe's V codes: one scale per channel, no block mean
         ablation["sage_per_channel"] = {"v_rel_err": float(sage_value_stats(SP, v)["v_rel_err"].mean())}
         del SP
@@ -344,6 +376,7 @@ def main():
         "bf16_attention": bf16,
         "exp_then_cast_attention": exp_then_cast,
         "sage_baseline": sage,
+        "fp4_v_smooth": fp4,
         "skip_softmax": skip,
         "grouping_schedule": grouping_schedule(prep_ms, quant_ms, attn_ms),
         "kmeans_warm_start": warm,

@@ -45,7 +45,7 @@ class vc_shape(ctypes.Structure):
 class vsmooth_params(ctypes.Structure):
     _fields_ = [("block", ctypes.c_int32), ("kmeans_k", ctypes.c_int32),
                 ("kmeans_iters", ctypes.c_int32), ("smooth_k", ctypes.c_int32),
-                ("v_scale_mode", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("v_scale_mode", ctypes.c_int32), ("v_format", ctypes.c_int32),
                 ("seed", ctypes.c_uint64)]
 
 
@@ -58,7 +58,7 @@ class vc_prepared(ctypes.Structure):
 
 class vc_attn_params(ctypes.Structure):
     _fields_ = [("z_off", ctypes.c_int32), ("out_dtype", ctypes.c_int32), ("skip_lambda", ctypes.c_float),
-                ("prob_cast", ctypes.c_int32)]
+                ("prob_cast", ctypes.c_int32), ("v_format", ctypes.c_int32)]
 
 
 class vc_sage_params(ctypes.Structure):
@@ -138,8 +138,8 @@ def shape_of(B, H, L, d) -> vc_shape:
     return vc_shape(B, H, L, d)
 
 
-def make_params(kmeans_k=0, kmeans_iters=8, seed=0, smooth_k=1, v_scale_mode=0) -> vsmooth_params:
-    return vsmooth_params(128, kmeans_k, kmeans_iters, smooth_k, v_scale_mode, 0, seed & (2**64 - 1))
+def make_params(kmeans_k=0, kmeans_iters=8, seed=0, smooth_k=1, v_scale_mode=0, v_format=0) -> vsmooth_params:
+    return vsmooth_params(128, kmeans_k, kmeans_iters, smooth_k, v_scale_mode, v_format, seed & (2**64 - 1))
 
 
 # ---------------------------------------------------------------- C names --

@@ -77,3 +77,26 @@ def sage_value_stats(P: api.SagePrepared, v: torch.Tensor) -> dict:
             xhat = P.v_scale[b, h].double()[None, :] * dec
             err[b, h] = float(torch.sqrt(((xhat - x) ** 2).sum() / (x * x).sum()))
     return {"v_rel_err": err}
+
+
+@torch.no_grad()
+def fp4_value_stats(P: api.Prepared, v: torch.Tensor) -> dict:
+    """Relative error |v_hat - v| / |v| per (batch, head) of a 4-bit prepare:
+    v_hat = mean_b + 2^e * E2M1(code), one power-of-two scale per (block,
+    channel, key group).  Returns numpy float64 [B,H]."""
+    B, H, L, d = P.shape
+    nb = api.nblocks(L)
+    codes, exps = api.v4_codes_natural(P)                   # [B,H,nb,d,128], [B,H,nb,d,4]
+    table = torch.tensor([0, 0.5, 1, 1.5, 2, 3, 4, 6, -0.0, -0.5, -1, -1.5, -2, -3, -4, -6],
+                         dtype=torch.float64, device=v.device)
+    group = (torch.arange(api.BLK, device=v.device) % 16) // 4  # key group of each in-block key
+    err = np.empty((B, H))
+    for b in range(B):
+        for h in range(H):
+            x = v[b, h].float()[P.perm[b, h].long()].double()                  # permuted rows [L,d]
+            sc = torch.ldexp(torch.ones((), dtype=torch.float64, device=v.device),
+                             exps[b, h].long()[..., group] - 127)               # [nb,d,128]
+            xhat = P.v_mean[b, h].double()[:, :, None] + table[codes[b, h].long()] * sc
+            xhat = xhat.transpose(1, 2).reshape(-1, d)[:L]
+            err[b, h] = float(torch.sqrt(((xhat - x) ** 2).sum() / (x * x).sum()))
+    return {"v_rel_err": err}

@@ -27,6 +27,7 @@ class Prepared:
     v_mean: torch.Tensor
     perm: torch.Tensor
     kmeans_obj: torch.Tensor
+    v_format: int = 0  # 0: E4M3 residual; 1: E2M1 residual (v8 / v_scale hold packed codes / E8M0 bytes)
 
     def c(self) -> _lib.vc_prepared:
         return _lib.vc_prepared(*(t.data_ptr() for t in (
@@ -57,7 +58,7 @@ def workspace(B, H, L, d, *, kmeans_k=0, kmeans_iters=8, device="cuda") -> torch
 def prepare(q, k, v, *, perm_in=None, kmeans_k=0, kmeans_iters=8, seed=0, smooth_k=1,
             v_scale_mode=0, out: Prepared | None = None, ws: torch.Tensor | None = None,
             centroids_in: torch.Tensor | None = None, centroids_out: torch.Tensor | None = None,
-            stream=None) -> Prepared:
+            v_format=0, stream=None) -> Prepared:
     """vsmooth_prepare on bf16 [B,H,L,d] device tensors; with centroids_in
     and/or centroids_out (fp32 [B,H,k,d]) vsmooth_prepare_warm, whose k-means
     starts from centroids_in (None: the seeded init) and leaves its final
@@ -76,8 +77,9 @@ def prepare(q, k, v, *, perm_in=None, kmeans_k=0, kmeans_iters=8, seed=0, smooth
             if t is not None:
                 assert t.dtype == torch.float32 and t.is_contiguous() and tuple(t.shape) == (B, H, kk, d)
     shape = _lib.shape_of(B, H, L, d)
-    params = _lib.make_params(kmeans_k, kmeans_iters, seed, smooth_k, v_scale_mode)
+    params = _lib.make_params(kmeans_k, kmeans_iters, seed, smooth_k, v_scale_mode, v_format)
     out = out if out is not None else alloc_prepared(B, H, L, d, q.device)
+    out.v_format = v_format
     if ws is None:
         ws = workspace(B, H, L, d, kmeans_k=kmeans_k, kmeans_iters=kmeans_iters, device=q.device)
     if warm:
@@ -88,20 +90,26 @@ def prepare(q, k, v, *, perm_in=None, kmeans_k=0, kmeans_iters=8, seed=0, smooth
     return out
 
 
-def attention(prep: Prepared, *, z_off=8, out_dtype=torch.float32, out=None, skip_lambda=0.0, prob_cast=0,
+def _prob_cast(prep: Prepared, prob_cast):
+    return (1 if prep.v_format == 1 else 0) if prob_cast is None else prob_cast
+
+
+def attention(prep: Prepared, *, z_off=8, out_dtype=torch.float32, out=None, skip_lambda=0.0, prob_cast=None,
               stream=None):
     """vc_attention_fwd: O [B,H,L,d] in fp32 or bf16 (skip_lambda: the Skip
-    Softmax threshold, 0 = off; prob_cast: 0 ExpCast-FP8, 1 exp-then-cast)."""
+    Softmax threshold, 0 = off; prob_cast: 0 ExpCast-FP8, 1 exp-then-cast,
+    default 0, or 1 for a 4-bit prepare, which needs it)."""
     B, H, L, d = prep.shape
     if out is None:
         out = torch.empty((B, H, L, d), dtype=out_dtype, device=prep.q8.device)
     od = 1 if out.dtype == torch.bfloat16 else 0
-    params = _lib.vc_attn_params(z_off, od, skip_lambda, prob_cast)
+    params = _lib.vc_attn_params(z_off, od, skip_lambda, _prob_cast(prep, prob_cast), prep.v_format)
     _lib.vc_attention_fwd(_lib.shape_of(B, H, L, d), params, prep.c(), out, stream)
     return out
 
 
-def attention_dump(prep: Prepared, bh: int, q_tile: int, *, z_off=8, skip_lambda=0.0, prob_cast=0, stream=None):
+def attention_dump(prep: Prepared, bh: int, q_tile: int, *, z_off=8, skip_lambda=0.0, prob_cast=None,
+                   stream=None):
     """vc_attention_fwd_dump: returns (O fp32, S [256, Lp] fp32, P [256, Lp] u8)."""
     B, H, L, d = prep.shape
     Lp = nblocks(L) * BLK
@@ -109,7 +117,7 @@ def attention_dump(prep: Prepared, bh: int, q_tile: int, *, z_off=8, skip_lambda
     out = torch.empty((B, H, L, d), dtype=torch.float32, device=dev)
     s = torch.zeros((256, Lp), dtype=torch.float32, device=dev)
     p = torch.zeros((256, Lp), dtype=torch.uint8, device=dev)
-    params = _lib.vc_attn_params(z_off, 0, skip_lambda, prob_cast)
+    params = _lib.vc_attn_params(z_off, 0, skip_lambda, _prob_cast(prep, prob_cast), prep.v_format)
     _lib.vc_attention_fwd_dump(_lib.shape_of(B, H, L, d), params, prep.c(), out, bh, q_tile, s, p, stream)
     return out, s, p
 
@@ -230,6 +238,17 @@ def key_of_slot():
     import numpy as np
     pos = np.arange(BLK)
     return 16 * ((pos % 32) // 4) + 4 * (pos // 32) + (pos % 4)
+
+
+def v4_codes_natural(prep: Prepared):
+    """The E2M1 residual of a 4-bit prepare: (codes [B,H,nb,d,128] one code
+    per byte in natural key order, E8M0 bytes [B,H,nb,d,4])."""
+    B, H, L, d = prep.shape
+    nb = nblocks(L)
+    packed = prep.v8.reshape(-1)[:B * H * nb * d * BLK // 2].view(B, H, nb, d, BLK // 2)
+    slots = torch.stack([packed & 0xF, packed >> 4], dim=-1).reshape(B, H, nb, d, BLK)
+    exps = prep.v_scale.view(torch.uint8).view(B, H, nb, d, 4)
+    return v_codes_natural(slots), exps
 
 
 def v_codes_natural(v8):

@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libvcattn.so")
 SOURCES = ["vc_abi.hip", "vc_prepare.hip", "vc_sage_prepare.hip", "vc_kmeans.hip", "vc_attn_fp8.hip",
-           "vc_attn_sage.hip", "vc_attn_bf16.hip", "vc_debug.hip"]
+           "vc_attn_sage.hip", "vc_attn_fp4.hip", "vc_attn_bf16.hip", "vc_debug.hip"]
 ARCH = os.environ.get("VC_OFFLOAD_ARCH", "gfx950")
 
 
@@ -36,7 +36,7 @@ def flags():
 
 # NaN inputs are outside the library's contract; without NaN semantics the
 # compiler drops the quieting moves it otherwise puts around every max.
-EXTRA = {"vc_attn_fp8.hip": ["-fno-honor-nans"], "vc_attn_sage.hip": ["-fno-honor-nans"],
+EXTRA = {"vc_attn_fp8.hip": ["-fno-honor-nans"], "vc_attn_sage.hip": ["-fno-honor-nans"], "vc_attn_fp4.hip": ["-fno-honor-nans"],
          "vc_attn_bf16.hip": ["-fno-honor-nans"],
          "vc_kmeans.hip": ["-fno-honor-nans"]}
 

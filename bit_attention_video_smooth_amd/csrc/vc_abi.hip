@@ -68,7 +68,9 @@ int check_params(const vc_shape* s, const vsmooth_params* p, int* kk) {
     if (p->smooth_k != 0 && p->smooth_k != 1) return fail(VC_ERR_INVALID, "smooth_k must be 0 or 1");
     if (p->v_scale_mode != 0 && p->v_scale_mode != 1)
         return fail(VC_ERR_INVALID, "v_scale_mode must be 0 or 1");
-    if (p->reserved != 0) return fail(VC_ERR_INVALID, "reserved must be 0");
+    if (p->v_format != 0 && p->v_format != 1) return fail(VC_ERR_INVALID, "v_format must be 0 or 1");
+    if (p->v_format == 1 && p->v_scale_mode != 0)
+        return fail(VC_ERR_INVALID, "v_scale_mode must be 0 with v_format 1 (FP4 scales are powers of two)");
     const int k = p->kmeans_k > 0 ? p->kmeans_k : nblk(s);
     if (k > s->L) return fail(VC_ERR_INVALID, "kmeans_k=%d exceeds L=%d", k, s->L);
     if (k > 16384) return fail(VC_ERR_INVALID, "kmeans_k=%d exceeds 16384", k);
@@ -110,6 +112,12 @@ int attention_common(const vc_shape* shape, const vc_attn_params* params, const 
         return fail(VC_ERR_INVALID, "skip_lambda must lie in [0, 1]");
     if (params->prob_cast != 0 && params->prob_cast != 1)
         return fail(VC_ERR_INVALID, "prob_cast must be 0 (ExpCast-FP8) or 1 (exp-then-cast)");
+    if (params->v_format != 0 && params->v_format != 1)
+        return fail(VC_ERR_INVALID, "v_format must be 0 (E4M3) or 1 (E2M1)");
+    if (params->v_format == 1 && params->prob_cast != 1)
+        return fail(VC_ERR_UNSUPPORTED, "v_format 1 needs prob_cast 1 (ExpCast has no 4-bit form)");
+    if (params->v_format == 1 && params->skip_lambda != 0.0f)
+        return fail(VC_ERR_UNSUPPORTED, "skip_lambda must be 0 with v_format 1");
     if ((r = check_prepared(in, false))) return r;
     if ((r = check_ptr(out, "out"))) return r;
     vc::AttnArgs a{};
@@ -136,6 +144,8 @@ int attention_common(const vc_shape* shape, const vc_attn_params* params, const 
         a.s_dump = s_dump;
         a.p_dump = p_dump;
     }
+    if (params->v_format == 1)
+        return hip_status(vc::launch_attn_fp4v(a, shape->d, params->out_dtype, dump, stream), "vc_attention_fwd");
     return hip_status(vc::launch_attn_fp8(a, shape->d, params->out_dtype, dump, stream), "vc_attention_fwd");
 }
 
@@ -182,6 +192,7 @@ int sage_attention_common(const vc_shape* shape, const vc_sage_params* sp, const
         return fail(VC_ERR_INVALID, "out_dtype must be 0 (fp32) or 1 (bf16)");
     if (params->skip_lambda != 0.0f)
         return fail(VC_ERR_UNSUPPORTED, "skip_lambda must be 0 for the SAGE baseline (it runs dense)");
+    if (params->v_format != 0) return fail(VC_ERR_UNSUPPORTED, "v_format must be 0 for the SAGE baseline");
     if (params->prob_cast != 0 && params->prob_cast != 1)
         return fail(VC_ERR_INVALID, "prob_cast must be 0 (ExpCast-FP8) or 1 (exp-then-cast)");
     if ((r = check_sage_prepared(in))) return r;
@@ -241,6 +252,7 @@ int prepare_common(const vc_shape* shape, const vsmooth_params* params, const vo
     a.B = shape->B; a.H = shape->H; a.L = shape->L; a.d = shape->d; a.nb = nblk(shape);
     a.smooth_k = params->smooth_k;
     a.v_mode = params->v_scale_mode;
+    a.v_format = params->v_format;
     a.q = q; a.k = k; a.v = v;
     a.perm = out->perm;
     a.q8 = out->q8; a.k8 = out->k8; a.v8 = out->v8;

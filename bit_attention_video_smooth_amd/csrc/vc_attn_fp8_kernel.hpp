@@ -63,7 +63,8 @@ namespace {
 enum : int {
     REC_VC = 0,       // V-Smooth: FP8 Q/K, one scale per 128-token block, block means
     REC_SAGE_F8 = 1,  // SAGE: FP8 Q/K codes, per-token Q and per-16-key K scales
-    REC_SAGE_I8 = 2   // SAGE: INT8 Q/K codes, same scales
+    REC_SAGE_I8 = 2,  // SAGE: INT8 Q/K codes, same scales
+    REC_VC4 = 3       // 4-bit V-Smooth: E2M1 residual and probabilities, E8M0 scales per 32-key group
 };
 
 constexpr int NW = 8;    // waves per workgroup (group 0 = waves 0-3 also copy)
@@ -74,6 +75,8 @@ template <int D>
 struct Fp8Tile {
     static constexpr int K_TILE = BLK * D;      // bytes of one K8 block  [128 keys][D]
     static constexpr int V_TILE = D * BLK;      // bytes of one V8 block  [D][128 slots]
+    static constexpr int V4_TILE = D * BLK / 2; // bytes of one E2M1 V block [D][64]
+    static constexpr int LPTV = V4_TILE / 4096; // E2M1 V chunks per loading thread
     static constexpr int SV_OFF = K_TILE + V_TILE;
     // each loading wave keeps a private 1 KiB copy of the block's per-channel
     // scales and means and a 256-byte window of K scales (readers use wave 0's)
@@ -190,10 +193,13 @@ __device__ __forceinline__ uint32_t dma_offset(int w, int lane, int row_bytes) {
 // Every copy runs with all 64 lanes, so each loading wave issues exactly
 // NLD copies per block and the wait counts below are exact.  Buffer
 // descriptors cover one head: reads past it return zeros.
-template <int D, bool SAGE>
+template <int D, int MODE>
 struct Fp8Loader {
     using T = Fp8Tile<D>;
-    static constexpr int NLD = 2 * T::LPT + (SAGE ? 1 : 2);
+    static constexpr bool SAGE = MODE == REC_SAGE_F8 || MODE == REC_SAGE_I8;
+    static constexpr bool FP4V = MODE == REC_VC4;
+    static constexpr int NVC = FP4V ? T::LPTV : T::LPT;  // V copies per loading thread
+    static constexpr int NLD = T::LPT + NVC + (SAGE ? 1 : 2);
     static constexpr int NC = D / 4;  // 16-byte chunks of D floats
     v4si rk, rv, rks;
     const float *vs, *vm;
@@ -202,7 +208,8 @@ struct Fp8Loader {
     __device__ __forceinline__ Fp8Loader(const AttnArgs& a, int bh, int w_, int lane_) : w(w_), lane(lane_) {
         const size_t Lp = (size_t)a.nb * BLK;
         rk = make_rsrc(a.k8 + (size_t)bh * Lp * D, (uint32_t)(Lp * D));
-        rv = make_rsrc(a.v8 + (size_t)bh * a.nb * D * BLK, (uint32_t)((size_t)a.nb * D * BLK));
+        const size_t vrow = FP4V ? BLK / 2 : BLK;  // bytes per channel row of a V block
+        rv = make_rsrc(a.v8 + (size_t)bh * a.nb * D * vrow, (uint32_t)((size_t)a.nb * D * vrow));
         if (SAGE) {
             rks = make_rsrc(a.k_scale + (size_t)bh * (Lp / 16), (uint32_t)(Lp / 16 * 4));
             vs = vm = nullptr;
@@ -212,7 +219,7 @@ struct Fp8Loader {
             vm = a.v_mean + (size_t)bh * a.nb * D;
         }
         off_k = dma_offset(w, lane, D);
-        off_v = dma_offset(w, lane, BLK);
+        off_v = dma_offset(w, lane, FP4V ? BLK / 2 : BLK);
         off_sv = (uint32_t)((lane % (2 * NC)) % NC) * 16;  // lanes past 2*NC repeat
     }
     __device__ __forceinline__ void issue(lds_u8* stage, int kb) const {
@@ -220,8 +227,9 @@ struct Fp8Loader {
         for (int i = 0; i < T::LPT; i++)
             lds_dma16(rk, stage + (i * 4 + w) * 1024, off_k, kb * T::K_TILE + i * 4096);
 #pragma unroll
-        for (int i = 0; i < T::LPT; i++)
-            lds_dma16(rv, stage + T::K_TILE + (i * 4 + w) * 1024, off_v, kb * T::V_TILE + i * 4096);
+        for (int i = 0; i < NVC; i++)
+            lds_dma16(rv, stage + T::K_TILE + (i * 4 + w) * 1024, off_v,
+                      kb * (FP4V ? T::V4_TILE : T::V_TILE) + i * 4096);
         if (!SAGE) {
             const float* src = ((lane % (2 * NC)) < NC ? vs : vm) + (size_t)kb * D;
             lds_dma16_flat(reinterpret_cast<const uint8_t*>(src) + off_sv, stage + T::SV_OFF + w * 1024);
@@ -233,7 +241,9 @@ struct Fp8Loader {
 template <int D, bool DUMP, bool SKIP, bool NAIVE, int MODE>
 struct Fp8Wave {
     using T = Fp8Tile<D>;
-    static constexpr bool SAGE = MODE != REC_VC;
+    static constexpr bool SAGE = MODE == REC_SAGE_F8 || MODE == REC_SAGE_I8;
+    static constexpr bool FP4V = MODE == REC_VC4;
+    static_assert(!FP4V || NAIVE, "4-bit probabilities come by exp-then-cast");
     const AttnArgs& a;
     int bh, w, lane, col, g, grp, q0, L, nb;
     size_t Lp;
@@ -252,6 +262,8 @@ struct Fp8Wave {
     // the coefficients of the block's eight 16-key tiles
     float sqx[2];
     float cf[2][8];
+    // 4-bit: E8M0 byte (e + 127) of each query tile's probability group
+    int sp[2];
 
     __device__ __forceinline__ Fp8Wave(const AttnArgs& args, int bh_, int qtile, int w_, int lane_)
         : a(args), bh(bh_), w(w_), lane(lane_) {
@@ -475,6 +487,58 @@ struct Fp8Wave {
         }
     }
 
+    // 4-bit probabilities: p = 2^z in fp32 (v_exp_f32), then one power-of-two
+    // scale for the lane's 32 values -- one 32-key group of the scaled FP4
+    // product, the keys (kk mod 16) div 4 = g of the block -- by the E8M0 rule
+    // on their maximum, and E2M1 codes (round to nearest even), element
+    // 4 kt + i of the lane in nibble (4 kt + i) mod 8 of dword kt / 2.
+    template <bool MASKED>
+    __device__ __forceinline__ void softmax_bytes_fp4(int kb, float c, int lim) {
+#pragma unroll
+        for (int qt = 0; qt < 2; qt++) {
+            float p[32];
+#pragma unroll
+            for (int kt = 0; kt < 8; kt++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    p[4 * kt + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[qt][kt][i], c, krow[qt]));
+                    if (MASKED && !(16 * kt + i < lim)) p[4 * kt + i] = 0.f;  // keys past L: code 0
+                }
+            // plain fmaxf, not the inline-asm max3: these are transcendental
+            // results, whose read-after-write wait state the compiler only
+            // inserts before instructions it can see
+            float m0 = fmaxf(p[0], p[1]), m1 = fmaxf(p[2], p[3]);
+#pragma unroll
+            for (int j = 4; j < 32; j += 4) {
+                m0 = fmaxf(fmaxf(m0, p[j]), p[j + 1]);
+                m1 = fmaxf(fmaxf(m1, p[j + 2]), p[j + 3]);
+            }
+            const int ex = e8m0_exp(fmaxf(m0, m1));
+            sp[qt] = ex + 127;
+            const float sc = ldexpf(1.0f, max(ex, -126));
+#pragma unroll
+            for (int w4 = 0; w4 < 4; w4++) {
+                const float (&y)[8] = *reinterpret_cast<const float(*)[8]>(&p[8 * w4]);
+                P[qt][w4] = ex > -127 ? e2m1_pk8(y, sc) : 0u;  // a group below 2^-100: codes 0
+                P[qt][4 + w4] = 0u;
+            }
+            if (DUMP && dump) {
+                const int rl = w * QW + 16 * qt + col;
+                if (q0 + 16 * qt + col < L) {
+#pragma unroll
+                    for (int kt = 0; kt < 8; kt++)
+#pragma unroll
+                        for (int i = 0; i < 4; i++) {
+                            const int e = 4 * kt + i;
+                            const size_t o = (size_t)rl * Lp + kb * BLK + 16 * kt + 4 * g + i;
+                            a.s_dump[o] = S[qt][kt][i];
+                            a.p_dump[o] = (P[qt][e / 8] >> (4 * (e % 8))) & 0xF;
+                        }
+                }
+            }
+        }
+    }
+
     // Returns true when every row of the wave rejects the block (Skip
     // Softmax; its bytes are then all 0): the caller skips P V.  (Branching
     // around the byte conversion as well costs more than it saves.)
@@ -506,12 +570,77 @@ struct Fp8Wave {
         const int nvalid = L - kb * BLK;  // keys of this block that exist (>= 1)
         if (nvalid < BLK) {
             softmax_max<true>(cb, nvalid - 4 * g);
-            softmax_bytes<true>(kb, cscale, nvalid - 4 * g);
+            if (FP4V)
+                softmax_bytes_fp4<true>(kb, cscale, nvalid - 4 * g);
+            else
+                softmax_bytes<true>(kb, cscale, nvalid - 4 * g);
         } else {
             softmax_max<false>(cb, 0);
-            softmax_bytes<false>(kb, cscale, 0);
+            if (FP4V)
+                softmax_bytes_fp4<false>(kb, cscale, 0);
+            else
+                softmax_bytes<false>(kb, cscale, 0);
         }
         return SKIP && !DUMP && __all(reject[0] && reject[1]);
+    }
+
+    // 4-bit P V: row sums (ones(16x128) P^T with the probability scale) and
+    // V4^T P^T on the scaled FP4 matrix cores -- the V operand is 16 bytes of
+    // E2M1 codes per lane (channel 16 ct + col, slots 32 g .. 32 g + 31) with
+    // that (channel, group)'s E8M0 byte, the P operand the lane's codes with
+    // its own; O += l_b mean_b + acc on the vector ALU.
+    __device__ __forceinline__ void slot_pv_fp4(const lds_u8* st) {
+        const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
+        v8i ones;  // E2M1 1.0 in every element, scale 2^0
+        int one4;
+        asm volatile("v_mov_b32 %0, 0x22222222" : "=v"(one4));
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            ones[i] = one4;
+            ones[4 + i] = 0;
+        }
+        v8i pv[2];
+        float ell[2];
+#pragma unroll
+        for (int qt = 0; qt < 2; qt++) {
+#pragma unroll
+            for (int kt = 0; kt < 8; kt++) pv[qt][kt] = (int)P[qt][kt];
+            const v4f r = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, pv[qt], zero4, 4, 4, 0, 127, 0,
+                                                                            sp[qt]);
+            ell[qt] = r[0];
+        }
+        const lds_u8* sV = st + T::K_TILE;
+        const VC_LDS float* sS = reinterpret_cast<const VC_LDS float*>(st + T::SV_OFF);
+        const lds_u8* sE = st + T::SV_OFF;  // E8M0 bytes [D][4]
+#pragma unroll
+        for (int ct = 0; ct < T::NCT; ct++) {
+            const int r = 16 * ct + col;
+            const u32x4 c4 = *reinterpret_cast<const VC_LDS u32x4*>(sV + r * (BLK / 2) +
+                                                                   ((g ^ chunk_swizzle(r, 4)) << 4));
+            v8i vop;
+            vop[0] = c4[0]; vop[1] = c4[1]; vop[2] = c4[2]; vop[3] = c4[3];
+            vop[4] = 0; vop[5] = 0; vop[6] = 0; vop[7] = 0;
+            const int sv = sE[4 * r + g];
+            const f32x4 mu = *reinterpret_cast<const VC_LDS f32x4*>(sS + D + 16 * ct + 4 * g);
+#pragma unroll
+            for (int qt = 0; qt < 2; qt++) {
+                const v4f acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(vop, pv[qt], zero4, 4, 4, 0, sv, 0,
+                                                                                  sp[qt]);
+#pragma unroll
+                for (int i = 0; i < 4; i++)
+                    O[qt][ct][i] = __fadd_rn(__builtin_fmaf(ell[qt], mu[i], O[qt][ct][i]), acc[i]);
+            }
+        }
+#pragma unroll
+        for (int qt = 0; qt < 2; qt++) l[qt] = __builtin_fmaf(alpha[qt], l[qt], ell[qt]);
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // DS read: tiles 0, 1 (operand, scale, mean)
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA: row sums
+#pragma unroll
+        for (int ct = 0; ct < T::NCT; ct++) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA: tile ct
+            if (ct + 2 < T::NCT) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+            if (ct > 0) __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);  // VALU: tile ct-1
+        }
     }
 
     // Row sums (ones(16x128) * P^T, exact), V8^T P^T on the matrix
@@ -590,7 +719,7 @@ struct Fp8Wave {
     // has four stages: block kb + 2 is copied, after barrier kb, into the
     // stage of block kb - 2, which both groups left before that barrier.
     template <bool LOADER, bool LAG>
-    __device__ __forceinline__ void block(const Fp8Loader<D, SAGE>& ld, int kb, const lds_u8* cur,
+    __device__ __forceinline__ void block(const Fp8Loader<D, MODE>& ld, int kb, const lds_u8* cur,
                                           lds_u8* ahead) {
         slot_qk(cur);
         if (LAG) block_barrier();
@@ -603,18 +732,23 @@ struct Fp8Wave {
 #pragma unroll
                 for (int ct = 0; ct < T::NCT; ct++) O[qt][ct] *= alpha[qt];
             }
-        if (__builtin_expect(!rejected, 1)) slot_pv(cur);
+        if (__builtin_expect(!rejected, 1)) {
+            if (FP4V)
+                slot_pv_fp4(cur);
+            else
+                slot_pv(cur);
+        }
         if (LOADER) {
             if (DUMP)
                 wait_vmcnt<0>();
             else
-                wait_vmcnt<Fp8Loader<D, SAGE>::NLD>();
+                wait_vmcnt<Fp8Loader<D, MODE>::NLD>();
         }
         if (!LAG) block_barrier();
     }
 
     template <bool LOADER, bool LAG>
-    __device__ __forceinline__ void run(const Fp8Loader<D, SAGE>& ld, lds_u8* const (&st)[4]) {
+    __device__ __forceinline__ void run(const Fp8Loader<D, MODE>& ld, lds_u8* const (&st)[4]) {
         for (int kb = 0; kb < nb; kb += 4) {
             block<LOADER, LAG>(ld, kb, st[0], st[2]);
             if (kb + 1 < nb) block<LOADER, LAG>(ld, kb + 1, st[1], st[3]);
@@ -626,7 +760,7 @@ struct Fp8Wave {
 
 template <int D, bool OUT_BF16, bool DUMP, bool SKIP, bool NAIVE, int MODE>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fp8_kernel(AttnArgs a) {
-    constexpr bool SAGE = MODE != REC_VC;
+    constexpr bool SAGE = MODE == REC_SAGE_F8 || MODE == REC_SAGE_I8;
     using T = Fp8Tile<D>;
     __shared__ __attribute__((aligned(16))) uint8_t st0_[T::STAGE];
     __shared__ __attribute__((aligned(16))) uint8_t st1_[T::STAGE];
@@ -639,7 +773,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fp8_kernel(AttnArgs a) {
     // wave index as a scalar (uniform) value
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     Fp8Wave<D, DUMP, SKIP, NAIVE, MODE> s(a, bh, qtile, w, lane);
-    const Fp8Loader<D, SAGE> ld(a, bh, w, lane);
+    const Fp8Loader<D, MODE> ld(a, bh, w, lane);
     const int nb = a.nb;
 
     // Blocks 0 and 1 are in flight before the loop; block 0 is published by
@@ -648,7 +782,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fp8_kernel(AttnArgs a) {
     if (s.grp == 0) {
         ld.issue(st[0], 0);
         ld.issue(st[1], min(1, nb - 1));
-        wait_vmcnt<Fp8Loader<D, SAGE>::NLD>();
+        wait_vmcnt<Fp8Loader<D, MODE>::NLD>();
     }
     block_barrier();
     if (s.grp == 0) {

@@ -48,6 +48,25 @@ __device__ __forceinline__ uint32_t e4m3_pk4(float x0, float x1, float x2, float
     return e4m3_pk2<true>(x2, x3, e4m3_pk2<false>(x0, x1, 0u));
 }
 
+// Eight values -> one dword of E2M1 (OCP MX FP4) codes, element j in nibble j
+// (low nibble first): v_cvt_scalef32_pk_fp4_f32 rounds x / sc to the nearest
+// E2M1 value, ties to even, saturating at +-6 (measured on gfx950); with sc a
+// power of two the division is exact.
+__device__ __forceinline__ uint32_t e2m1_pk8(const float (&y)[8], float sc) {
+    uint32_t r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y[0], y[1], sc, 0);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[2], y[3], sc, 1);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[4], y[5], sc, 2);
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y[6], y[7], sc, 3);
+}
+
+// E8M0 exponent of an FP4 group with amax A: the least e with A <= 6 * 2^e
+// (6 = 0.75 * 2^3, A = f * 2^E with f in [0.5, 1)); -127 for A < 2^-100.
+__device__ __forceinline__ int e8m0_exp(float A) {
+    int E;
+    const float f = frexpf(A, &E);
+    return A >= 0x1p-100f ? E - 3 + (f > 0.75f ? 1 : 0) : -127;
+}
+
 // ExpCast-FP8: y = fma(S, c8, krow), then v_cvt_pk_u8_f32, which rounds to
 // the nearest integer (ties to even) and saturates to [0, 255], into byte
 // `sel` of `acc`.  Callers keep y below 126.5.

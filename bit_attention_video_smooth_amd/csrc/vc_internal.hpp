@@ -11,6 +11,7 @@ namespace vc {
 struct PrepareArgs {
     int B, H, L, d, nb;
     int smooth_k, v_mode;
+    int v_format;         // 0 E4M3 residual, fp32 scales; 1 E2M1 residual, E8M0 scales per 32-key group
     const void *q, *k, *v;
     const int32_t* perm;  // [B,H,L]
     uint8_t *q8, *k8, *v8;
@@ -92,6 +93,8 @@ constexpr int SAGE_VCHUNK = 1024;  // tokens per partial channel amax
 hipError_t launch_sage_prepare(const SageArgs& a, hipStream_t st);
 hipError_t launch_kmeans(const KmeansArgs& a, hipStream_t st);
 hipError_t launch_attn_fp8(const AttnArgs& a, int d, int out_bf16, bool dump, hipStream_t st);
+// 4-bit V-Smooth: v8 [BH, nb, d, 64] E2M1 codes, v_scale read as [BH, nb, d, 4] E8M0 bytes
+hipError_t launch_attn_fp4v(const AttnArgs& a, int d, int out_bf16, bool dump, hipStream_t st);
 // SAGE recipe: q_scale [BH, Lp], k_scale [BH, Lp/16], v_scale [BH, d]; v_mean unused
 hipError_t launch_attn_sage(const AttnArgs& a, int d, int out_bf16, bool dump, bool qk_int8, hipStream_t st);
 hipError_t launch_attn_bf16(const AttnBf16Args& a, int d, int out_bf16, hipStream_t st);

@@ -74,7 +74,11 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // max(a, b, c) in one instruction; written out so that the compiler keeps
-// the chains it is given instead of re-associating them into a tree.
+// the chains it is given instead of re-associating them into a tree.  Inline
+// assembly is invisible to the compiler's hazard pass: the wait states that a
+// read of a transcendental or matrix-core result needs are not inserted
+// before it, so use it only on values whose producers lie far behind (the
+// scores, read after the whole S^T region), never on v_exp results.
 __device__ __forceinline__ float vmax3(float a, float b, float c) {
     float r;
     asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));

@@ -247,6 +247,102 @@ __global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict
     }
 }
 
+// ------------------------------------------------------------------------
+// 4-bit V-Smooth residual: the same exact block mean, then E2M1 codes with
+// one power-of-two (E8M0) scale per (channel, key group), the group of key kk
+// being (kk mod 16) div 4 -- slots 32 g .. 32 g + 31 of the P V slot order,
+// the 32-element k-blocks of the scaled matrix-core product.  Scale 2^e with
+// e the least integer such that amax <= 6 * 2^e (no element clips); amax <
+// 2^-100: codes 0.  Codes: v_cvt_scalef32_pk_fp4_f32 (round to nearest even
+// of x / 2^e, exact scaling).  Output: codes [bh][nb][D][64] bytes, slot 2 t
+// in the low nibble of byte t; scales [bh][nb][D][4] bytes e + 127.  The
+// loads, the mean and the wave/key layout are those of quant_v_kernel; each
+// wave holds 8 keys of every group (keys 4 g .. 4 g + 3 and 16 + 4 g ..
+// 16 + 4 g + 3 of its 32), so group maxima are combined over the waves in LDS.
+// ------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void quant_v4_kernel(const uint16_t* __restrict__ v,
+                                                       const int32_t* __restrict__ perm,
+                                                       uint8_t* __restrict__ codes,
+                                                       uint32_t* __restrict__ vexp,
+                                                       float* __restrict__ vmean, int L, int nb) {
+    constexpr int CPL = D / 64;
+    constexpr int KW = BLK / 4;
+    __shared__ double psum[4][D];
+    __shared__ float pmax[4][D][4];
+    const int b = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63;
+    const int i0 = b * BLK;
+    const int n = min(BLK, L - i0);
+    const uint16_t* vb = v + (size_t)bh * L * D + CPL * lane;
+    const int32_t* pb = perm + (size_t)bh * L + i0 + KW * w;
+    const int nw = min(KW, max(0, n - KW * w));
+    float x[KW][CPL];
+#pragma unroll
+    for (int i = 0; i < KW; i++) {
+        if (i < nw) {
+            const int src = pb[i];
+            if (CPL == 2) {
+                const uint32_t u = *reinterpret_cast<const uint32_t*>(vb + (size_t)src * D);
+                x[i][0] = bf16_to_f32(u & 0xFFFFu);
+                x[i][CPL - 1] = bf16_to_f32(u >> 16);
+            } else {
+                x[i][0] = bf16_to_f32(vb[(size_t)src * D]);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < CPL; e++) x[i][e] = 0.0f;
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < CPL; e++) {
+        double s4[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+        for (int i = 0; i < KW; i++) s4[i % 4] += (double)x[i][e];
+        psum[w][CPL * lane + e] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+    }
+    __syncthreads();
+    float mu[CPL];
+#pragma unroll
+    for (int e = 0; e < CPL; e++) {
+        const int c = CPL * lane + e;
+        mu[e] = (float)((((psum[0][c] + psum[1][c]) + psum[2][c]) + psum[3][c]) / (double)n);
+#pragma unroll
+        for (int i = 0; i < KW; i++) x[i][e] = i < nw ? __fsub_rn(x[i][e], mu[e]) : 0.0f;  // residual
+#pragma unroll
+        for (int g = 0; g < 4; g++) {
+            float am = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; j++) am = fmaxf(am, fabsf(x[16 * (j / 4) + 4 * g + j % 4][e]));
+            pmax[w][c][g] = am;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < CPL; e++) {
+        const int c = CPL * lane + e;
+        const size_t gi = ((size_t)bh * nb + b) * D + c;
+        uint32_t ebytes = 0;
+        uint8_t* out = codes + gi * (BLK / 2);
+#pragma unroll
+        for (int g = 0; g < 4; g++) {
+            const float A = fmaxf(fmaxf(pmax[0][c][g], pmax[1][c][g]), fmaxf(pmax[2][c][g], pmax[3][c][g]));
+            const int ex = e8m0_exp(A);
+            ebytes |= (uint32_t)(ex + 127) << (8 * g);
+            // slots 32 g + 8 w + j hold keys 32 w + 16 (j / 4) + 4 g + j % 4
+            float y[8];
+#pragma unroll
+            for (int j = 0; j < 8; j++) y[j] = x[16 * (j / 4) + 4 * g + j % 4][e];
+            const uint32_t pk = ex > -127 ? e2m1_pk8(y, ldexpf(1.0f, ex)) : 0u;  // zero group: codes 0
+            *reinterpret_cast<uint32_t*>(out + 16 * g + 4 * w) = pk;
+        }
+        if (w == 0) {
+            vmean[gi] = mu[e];
+            vexp[gi] = ebytes;
+        }
+    }
+}
+
 // src may equal dst (a permutation kept from an earlier call): each element
 // is read and written by the same thread.
 __global__ void copy_perm_kernel(const int32_t* src, int32_t* dst, size_t n,
@@ -304,9 +400,13 @@ static hipError_t launch_prepare_quant_t(const PrepareArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((quant_qk_kernel<D, true>), dim3(a.nb, BH), dim3(256), 0, st,
                        (const uint16_t*)a.k, a.perm, (const float*)a.kbar, a.k8, a.k_scale, a.L,
                        a.nb);
-    hipLaunchKernelGGL((quant_v_kernel<D>), dim3(a.nb, BH), dim3(256), 0, st,
-                       (const uint16_t*)a.v, a.perm, a.v8, a.v_scale, a.v_mean, a.L, a.nb,
-                       a.v_mode);
+    if (a.v_format == 1)
+        hipLaunchKernelGGL((quant_v4_kernel<D>), dim3(a.nb, BH), dim3(256), 0, st, (const uint16_t*)a.v, a.perm,
+                           a.v8, reinterpret_cast<uint32_t*>(a.v_scale), a.v_mean, a.L, a.nb);
+    else
+        hipLaunchKernelGGL((quant_v_kernel<D>), dim3(a.nb, BH), dim3(256), 0, st,
+                           (const uint16_t*)a.v, a.perm, a.v8, a.v_scale, a.v_mean, a.L, a.nb,
+                           a.v_mode);
     return hipGetLastError();
 }
 

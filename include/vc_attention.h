@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define VC_ATTENTION_VERSION 1
+#define VC_ATTENTION_VERSION 2
 
 enum {
     VC_OK = 0,
@@ -72,8 +72,17 @@ typedef struct vsmooth_params {
                              softmax is unchanged by it); 0: off */
     int32_t v_scale_mode; /* residual scale per (block, channel):
                              0: s = fp32(amax / 448);
-                             1: s = 2^e, the least power of two with amax <= 448 s */
-    int32_t reserved;     /* must be 0 */
+                             1: s = 2^e, the least power of two with amax <= 448 s;
+                             must be 0 with v_format 1 */
+    int32_t v_format;     /* residual format: 0 E4M3 (the 8-bit kernel); 1 E2M1
+                             (4-bit V-Smooth, MarkTechPost abstract): one
+                             power-of-two scale 2^e per (block, channel, key
+                             group), the group of key kk being (kk % 16) / 4,
+                             e the least integer with amax <= 6 * 2^e (amax <
+                             2^-100: codes 0); then v8 holds [B,H,nb,d,64]
+                             bytes (slot 2t in the low nibble of byte t, slots
+                             as below) and v_scale holds [B,H,nb,d,4] bytes
+                             e + 127 in place of fp32 scales */
     uint64_t seed;        /* seeds the k-means initial centroids (SplitMix64) */
 } vsmooth_params;
 
@@ -150,6 +159,14 @@ typedef struct vc_attn_params {
                           (MarkTechPost abstract): z = fma(S, c_b,
                           z_off - m'), p = 2^z in fp32, E4M3 round to
                           nearest even.  Other values: -1 */
+    int32_t v_format;  /* format of the prepared V residual (vsmooth_params):
+                          0 E4M3; 1 E2M1, and then P is E2M1 too: p = 2^z as
+                          for prob_cast 1 (required, since ExpCast has no
+                          4-bit form), one power-of-two scale per (query,
+                          key group) by the rule of v_format, E2M1 codes
+                          (round to nearest even), and both products on
+                          the scaled FP4 matrix cores.  skip_lambda must be
+                          0 with v_format 1.  Other values: -1 */
 } vc_attn_params;
 
 /* Fused VC-Attention forward (agihunt ExpCast-FP8 bullet; MarkTechPost

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version(lib):
-    assert _lib.vc_version() == 1
+    assert _lib.vc_version() == 2
 
 
 def test_prepared_sizes(lib):
@@ -70,7 +70,7 @@ def test_bad_params_rejected(lib):
         _lib.vsmooth_workspace_bytes(s, p)
     assert e.value.code == _lib.VC_ERR_UNSUPPORTED
     for field, val in [("kmeans_iters", -1), ("v_scale_mode", 2), ("smooth_k", 3), ("kmeans_k", 257),
-                       ("reserved", 1)]:
+                       ("v_format", 2)]:
         p = _lib.make_params()
         setattr(p, field, val)
         with pytest.raises(_lib.VCError) as e:
@@ -207,3 +207,23 @@ def test_sage_rejects_bad_arguments(lib):
         _lib.vc_sage_attention_fwd_dump(s, p, _lib.vc_attn_params(8, 0, 0.0, 1), _sprep(), FAKE, 2, 0, FAKE,
                                         FAKE, 0)
     assert e.value.code == _lib.VC_ERR_INVALID
+
+
+def test_fp4_v_format_rules(lib):
+    s = _lib.shape_of(1, 1, 256, 64)
+    p = _lib.make_params(v_scale_mode=1, v_format=1)   # FP4 scales are powers of two already
+    with pytest.raises(_lib.VCError) as e:
+        _lib.vsmooth_workspace_bytes(s, p)
+    assert e.value.code == _lib.VC_ERR_INVALID
+    assert _lib.vsmooth_workspace_bytes(s, _lib.make_params(v_format=1)) > 0
+    for pc, lam, code in [(0, 0.0, _lib.VC_ERR_UNSUPPORTED), (1, 0.5, _lib.VC_ERR_UNSUPPORTED)]:
+        with pytest.raises(_lib.VCError) as e:
+            _lib.vc_attention_fwd(s, _lib.vc_attn_params(8, 0, lam, pc, 1), _prep(), FAKE, 0)
+        assert e.value.code == code
+    with pytest.raises(_lib.VCError) as e:
+        _lib.vc_attention_fwd(s, _lib.vc_attn_params(8, 0, 0.0, 1, 2), _prep(), FAKE, 0)
+    assert e.value.code == _lib.VC_ERR_INVALID
+    with pytest.raises(_lib.VCError) as e:
+        _lib.vc_sage_attention_fwd(s, _lib.make_sage_params(), _lib.vc_attn_params(8, 0, 0.0, 1, 1), _sprep(),
+                                   FAKE, 0)
+    assert e.value.code == _lib.VC_ERR_UNSUPPORTED

@@ -128,3 +128,33 @@ def test_full_size_sage_sampled(api, cfg_idx, qk):
             ma = float(np.abs(got - ref).max() / np.abs(ref).max())
             print("sage %s %s bh=%d rows %d-%d: rel-L2 %.3g max-abs/max %.3g" % (qk, cfg.name, bh, r0, r1, rel, ma))
             assert rel <= bar[0] and ma <= bar[1]
+
+
+def test_full_size_fp4v_sampled(api):
+    """4-bit V-Smooth at Wan 720p in the benchmark's launch configuration:
+    sampled heads bit-exact (E2M1 codes, E8M0 scales, means), sampled query
+    tiles (first and ragged last) against the oracle."""
+    cfg_idx = 2
+    cfg = synth.CONFIGS[cfg_idx]
+    B, H, L, d = cfg.B, cfg.H, cfg.L, cfg.d
+    q, k, v = synth.make_inputs(cfg, cfg_idx)
+    perm = synth.random_perms(B, H, L, 400)
+    P = api.prepare(dev_bf16(q), dev_bf16(k), dev_bf16(v), perm_in=torch.from_numpy(perm).cuda(), v_format=1)
+    out = api.attention(P)
+    codes, exps = api.v4_codes_natural(P)
+    torch.cuda.synchronize()
+    last_tile = ((L - 1) // 256) * 256
+    for bh in (0, B * H - 1):
+        b, h = divmod(bh, H)
+        o = oracle.prepare_head_fp4v(q[b, h], k[b, h], v[b, h], perm[b, h])
+        assert np.array_equal(codes[b, h].cpu().numpy(), o["v4"])
+        assert np.array_equal(exps[b, h].cpu().numpy(), o["v_exp"])
+        assert np.array_equal(P.v_mean[b, h].cpu().numpy(), o["v_mean"])
+        for r0 in (0, last_tile):
+            r1 = min(L, r0 + 256)
+            ref = oracle.attention_head_fp4v(o, L, rows=(r0, r1))
+            got = out[b, h, r0:r1].cpu().numpy()
+            rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+            ma = float(np.abs(got - ref).max() / np.abs(ref).max())
+            print("fp4 P V wan720p bh=%d rows %d-%d: rel-L2 %.3g max-abs/max %.3g" % (bh, r0, r1, rel, ma))
+            assert rel <= 2e-3 and ma <= 2e-2

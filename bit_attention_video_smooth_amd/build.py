@@ -36,9 +36,8 @@ def flags():
 
 # NaN inputs are outside the library's contract; without NaN semantics the
 # compiler drops the quieting moves it otherwise puts around every max.
-EXTRA = {"vc_attn_fp8.hip": ["-fno-honor-nans"], "vc_attn_sage.hip": ["-fno-honor-nans"], "vc_attn_fp4.hip": ["-fno-honor-nans"],
-         "vc_attn_bf16.hip": ["-fno-honor-nans"],
-         "vc_kmeans.hip": ["-fno-honor-nans"]}
+EXTRA = {src: ["-fno-honor-nans"] for src in
+         ("vc_attn_fp8.hip", "vc_attn_sage.hip", "vc_attn_fp4.hip", "vc_attn_bf16.hip", "vc_kmeans.hip")}
 
 
 def _compile(src: str) -> str:

@@ -3,8 +3,10 @@
 // block-mean restore; and, on the same scaffold, the SAGE-style quantised
 // attention of the TensorRT-LLM blog ("Quantized Attention": one Q scale per
 // query token, one K scale per 16 keys, INT8 or FP8 QK^T, FP8 PV with one V
-// scale per channel).  The template is instantiated by vc_attn_fp8.hip
-// (V-Smooth) and vc_attn_sage.hip (SAGE), compiled side by side.
+// scale per channel); and 4-bit V-Smooth (E2M1 V residual and probabilities
+// with power-of-two scales per 32-key group, on the scaled FP4 matrix
+// cores).  The template is instantiated by vc_attn_fp8.hip (V-Smooth),
+// vc_attn_sage.hip (SAGE) and vc_attn_fp4.hip (4-bit), compiled side by side.
 //
 // Method: agihunt summary (ExpCast-FP8 bullet: E4M3 probability codes from
 // log-domain scores with one fused multiply-add; V-Smooth bullet: the mean

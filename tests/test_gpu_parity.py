@@ -454,3 +454,31 @@ def test_kmeans_permutation_attention_in_band(api):
     for h in range(cfg.H):
         ref = oracle.attention_f64(f(q[0, h]), f(k[0, h]), f(v[0, h]))
         assert rel_l2(out[0, h], ref) < 6e-2
+
+
+# ------------------------------------------- dump instance = plain instance --
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_dump_instances_compute_what_plain_ones_do(api, d):
+    """Every recipe's dumping kernel instance (a separate template instance,
+    scheduled differently) writes the same output as the plain instance, bit
+    for bit: V-Smooth with ExpCast, exp-then-cast and Skip Softmax, SAGE with
+    INT8 and FP8 QK^T, and 4-bit V-Smooth."""
+    B, H, L = 1, 2, 700
+    q, k, v = _inputs(B, H, L, d, 77, None)
+    perm = synth.random_perms(B, H, L, 78)
+    qd, kd, vd, pd = dev_bf16(q), dev_bf16(k), dev_bf16(v), torch.from_numpy(perm).cuda()
+    P = api.prepare(qd, kd, vd, perm_in=pd)
+    P4 = api.prepare(qd, kd, vd, perm_in=pd, v_format=1)
+    cases = {"expcast": (lambda: api.attention(P), lambda: api.attention_dump(P, 1, 2)),
+             "exp-then-cast": (lambda: api.attention(P, prob_cast=1), lambda: api.attention_dump(P, 1, 2, prob_cast=1)),
+             "skip": (lambda: api.attention(P, skip_lambda=0.3), lambda: api.attention_dump(P, 1, 2, skip_lambda=0.3)),
+             "fp4": (lambda: api.attention(P4), lambda: api.attention_dump(P4, 1, 2))}
+    for qk in ("int8", "fp8"):
+        S = api.sage_prepare(qd, kd, vd, qk_dtype=qk)
+        cases["sage " + qk] = (lambda S=S: api.sage_attention(S), lambda S=S: api.sage_attention_dump(S, 1, 2))
+    for name, (plain, dump) in cases.items():
+        a = plain()
+        b = dump()[0]
+        torch.cuda.synchronize()
+        assert torch.equal(a, b), name

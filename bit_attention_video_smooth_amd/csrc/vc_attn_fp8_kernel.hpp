@@ -506,9 +506,8 @@ struct Fp8Wave {
                     p[4 * kt + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[qt][kt][i], c, krow[qt]));
                     if (MASKED && !(16 * kt + i < lim)) p[4 * kt + i] = 0.f;  // keys past L: code 0
                 }
-            // plain fmaxf, not the inline-asm max3: these are transcendental
-            // results, whose read-after-write wait state the compiler only
-            // inserts before instructions it can see
+            // compiler-visible maxima: these read transcendental results, whose
+            // wait states the compiler inserts only before code it can see
             float m0 = fmaxf(p[0], p[1]), m1 = fmaxf(p[2], p[3]);
 #pragma unroll
             for (int j = 4; j < 32; j += 4) {

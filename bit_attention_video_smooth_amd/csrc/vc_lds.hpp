@@ -73,16 +73,13 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// max(a, b, c) in one instruction; written out so that the compiler keeps
-// the chains it is given instead of re-associating them into a tree.  Inline
-// assembly is invisible to the compiler's hazard pass: the wait states that a
-// read of a transcendental or matrix-core result needs are not inserted
-// before it, so use it only on values whose producers lie far behind (the
-// scores, read after the whole S^T region), never on v_exp results.
+// max(a, b, c): the compiler forms v_max3_f32 from the two fmaxf (NaN inputs
+// are outside the library's contract and the attention sources are built
+// with -fno-honor-nans) and inserts the wait states its inputs need, which it
+// would not do for inline assembly reading a transcendental or matrix-core
+// result (measured: same instruction mix and timing as an asm version).
 __device__ __forceinline__ float vmax3(float a, float b, float c) {
-    float r;
-    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-    return r;
+    return fmaxf(fmaxf(a, b), c);
 }
 
 }  // namespace vc

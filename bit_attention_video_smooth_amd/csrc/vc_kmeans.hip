@@ -30,7 +30,8 @@ namespace {
 
 constexpr int KT = 64;       // centroids per LDS tile of the assign kernel
 constexpr int CHUNK = 1024;  // tokens per chunk of the counting sort
-constexpr int ATOK = 512;    // tokens per assign workgroup (8 waves x 64)
+constexpr int ANTT = 8;      // 16-token tiles per wave of the assign kernel
+constexpr int ATOK = 8 * 16 * ANTT;  // tokens per assign workgroup (8 waves)
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -118,7 +119,7 @@ __device__ __forceinline__ int cent_chunk(int r, int lc) {
     return lc ^ ((r & 7) ^ ((r >> 3) & 1));                 // 128-byte rows, 8 chunks
 }
 
-// Grid (ceil(L/512), B*H), 512 threads: 8 waves x 64 tokens.  The output
+// Grid (ceil(L/ATOK), B*H), 512 threads: 8 waves x 16 ANTT tokens.  The output
 // tile of the matrix core is (16 centroids) x (16 tokens): a lane scans 4
 // centroids of one token per tile and the four lanes of a token merge at the
 // end.  Centroid tiles of 64 rows are double-buffered in LDS.  The product
@@ -133,7 +134,7 @@ __global__ __launch_bounds__(512) void km_assign(const uint16_t* __restrict__ v,
                                                  int32_t* __restrict__ assign, int L, int k, int kpad) {
     constexpr int NU = D / 32;          // 32-element steps of the bf16 product
     constexpr int RB = D * 2;           // bytes per centroid row
-    constexpr int NTT = 4;              // 16-token tiles per wave
+    constexpr int NTT = ANTT;           // 16-token tiles per wave
     constexpr int NCH = KT * RB / 16;   // 16-byte chunks per centroid tile
     constexpr int CPT = NCH / 512;      // chunks staged per thread
     constexpr int CPR = RB / 16;        // chunks per row
@@ -142,7 +143,7 @@ __global__ __launch_bounds__(512) void km_assign(const uint16_t* __restrict__ v,
     __shared__ __attribute__((aligned(16))) float sn[2][KT];  // -||c||^2 / 2
     const int bh = blockIdx.y;
     const int t = threadIdx.x, w = t >> 6, lane = t & 63, col = lane & 15, g = lane >> 4;
-    const int tok0 = blockIdx.x * ATOK + w * 64;
+    const int tok0 = blockIdx.x * ATOK + w * 16 * NTT;
     v8bf xop[NTT][NU];
 #pragma unroll
     for (int tt = 0; tt < NTT; tt++) {

@@ -31,8 +31,8 @@ HBM_PEAK_GBS = 8000.0
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=10)
-    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--config", type=int, default=2, help="workload index (0 tiny .. 4 cfg)")
     p.add_argument("--cpu-rows", type=int, default=-1, help="query rows of the CPU oracle sample (-1: auto)")
     p.add_argument("--no-cpu", action="store_true")
@@ -161,14 +161,20 @@ def main():
     if args.v_scale_mode not in (0, 1):
         sys.exit("--v-scale-mode must be 0 or 1")
 
-    # prepare without k-means (permutation reused, as across adjacent steps)
+    # prepare without k-means (permutation reused, as across adjacent steps),
+    # each repetition after a 512 MiB write that flushes the last-level cache
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    ev[0].record(stream)
-    for _ in range(args.steps):
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    qev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        flush.fill_(i & 0xFF)
+        qev[i][0].record(stream)
         api.prepare(q, k, v, perm_in=P.perm, out=P, ws=ws, v_scale_mode=args.v_scale_mode)
-    ev[1].record(stream)
+        qev[i][1].record(stream)
     torch.cuda.synchronize()
-    quant_ms = ev[0].elapsed_time(ev[1]) / args.steps
+    quant_each = [e[0].elapsed_time(e[1]) for e in qev]
+    quant_ms = float(np.mean(quant_each))
+    del flush
     E = B * H * L * d
     nb = api.nblocks(L)
     quant_bytes = 3 * E * 2 + 3 * E * 1 + B * H * nb * d * 8 + B * H * L * 4
@@ -345,6 +351,8 @@ def main():
         ablation["sage_per_channel"] = {"v_rel_err": float(sage_value_stats(SP, v)["v_rel_err"].mean())}
         del SP
 
+    clock = clock_under_load(lambda: api.attention(P, out=out), stream)
+
     attn_tflops = flop / attn_ms / 1e9
     res = {
         "metric": "FP8 attention TFLOP/s (4*B*H*L^2*d) & % FP8 MFMA peak, Wan2.2-shaped L=75,600",
@@ -366,11 +374,15 @@ def main():
         "attention": {"ms": attn_ms, "tflops": attn_tflops, "frac_fp8_peak": attn_tflops / FP8_PEAK_TFLOPS,
                       "ms_median": float(np.median(attn_each)), "ms_min": float(np.min(attn_each))},
         "device": {"name": torch.cuda.get_device_name(0),
-                   "compute_units": torch.cuda.get_device_properties(0).multi_processor_count},
+                   "compute_units": torch.cuda.get_device_properties(0).multi_processor_count, **clock},
+        "frac_fp8_peak_at_measured_clock": (attn_tflops / (FP8_PEAK_TFLOPS * clock["sclk_mhz"] / 2400.0)
+                                            if clock.get("sclk_mhz") else None),
         "attention_other_v_scale_mode": {"v_scale_mode": 1 - args.v_scale_mode, "ms": other_ms,
                                          "tflops": flop / other_ms / 1e9,
                                          "frac_fp8_peak": flop / other_ms / 1e9 / FP8_PEAK_TFLOPS},
         "prepare": {"ms_with_kmeans": prep_ms, "ms_without_kmeans": quant_ms,
+                    "ms_without_kmeans_median": float(np.median(quant_each)),
+                    "ms_without_kmeans_min": float(np.min(quant_each)),
                     "quant_algorithmic_bytes": quant_bytes,
                     "quant_gbs": quant_bytes / quant_ms / 1e6},
         "bf16_attention": bf16,
@@ -388,6 +400,32 @@ def main():
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(cfg, qn, kn, vn, args.cpu_rows)
     print(json.dumps(res))
+
+
+def clock_under_load(launch, stream, n=20):
+    """Shader clock and power cap read by rocm-smi while n attention launches
+    keep the GPU busy (queued first, so the reading falls inside them);
+    fields it could not read are None."""
+    import re
+    import subprocess
+
+    import torch
+    for _ in range(n):
+        launch()
+    info = {"sclk_mhz": None, "power_cap_w": None, "clock_source": "rocm-smi during %d attention launches" % n}
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--showmaxpower"], capture_output=True, text=True, timeout=30)
+        txt = r.stdout
+        m = re.search(r"sclk clock level:\s*\w+:\s*\((\d+)\s*Mhz\)", txt, re.I)
+        if m:
+            info["sclk_mhz"] = float(m.group(1))
+        m = re.search(r"Max Graphics Package Power \(W\):\s*([\d.]+)", txt, re.I)
+        if m:
+            info["power_cap_w"] = float(m.group(1))
+    except (OSError, subprocess.SubprocessError):
+        pass
+    torch.cuda.synchronize()
+    return info
 
 
 def grouping_schedule(prep_ms, quant_ms, attn_ms, num_steps=40):

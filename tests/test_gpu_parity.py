@@ -59,24 +59,31 @@ def test_e4m3_encoder_bit_exact(api):
 
 
 def test_expcast_bit_exact(api):
-    rng = np.random.default_rng(2)
-    n = 1 << 21
-    S = (rng.normal(0, 3000, n)).astype(np.float32)
-    c8 = (8 * rng.uniform(1e-4, 1e-2, n)).astype(np.float32)
-    m = (S * c8 / 8).astype(np.float32)  # a running max around the score
-    krow = (np.float32(119.65) - np.float32(8) * (m + rng.uniform(0, 20, n).astype(np.float32))).astype(np.float32)
-    # exact ties y = k + 0.5 and the clamp at zero
-    k = np.arange(-20, 127)
-    S[:k.size] = 0.0
-    krow[:k.size] = (k + 0.5).astype(np.float32)
-    S[k.size:2 * k.size] = 1.0
-    c8[k.size:2 * k.size] = 1.0
-    krow[k.size:2 * k.size] = (k - 0.5).astype(np.float32)
-    got = api.expcast(torch.from_numpy(S).cuda(), torch.from_numpy(c8).cuda(),
-                      torch.from_numpy(krow).cuda()).cpu().numpy()
-    ref = oracle.expcast(S, c8, krow)
-    bad = np.nonzero(got != ref)[0]
-    assert bad.size == 0, (S[bad[:5]], c8[bad[:5]], krow[bad[:5]], got[bad[:5]], ref[bad[:5]])
+    """The kernel's ExpCast device function against the oracle on 8 x 2^24
+    (1.3e8) fp32 inputs, exact .5 ties and the clamp at zero included."""
+    n = 1 << 24
+    total = 0
+    for chunk in range(8):
+        rng = np.random.default_rng(2 + chunk)
+        S = (rng.normal(0, 3000, n)).astype(np.float32)
+        c8 = (8 * rng.uniform(1e-4, 1e-2, n)).astype(np.float32)
+        m = (S * c8 / 8).astype(np.float32)  # a running max around the score
+        krow = (np.float32(119.65) - np.float32(8) * (m + rng.uniform(0, 20, n).astype(np.float32))).astype(np.float32)
+        if chunk == 0:
+            # exact ties y = k + 0.5 and the clamp at zero
+            k = np.arange(-20, 127)
+            S[:k.size] = 0.0
+            krow[:k.size] = (k + 0.5).astype(np.float32)
+            S[k.size:2 * k.size] = 1.0
+            c8[k.size:2 * k.size] = 1.0
+            krow[k.size:2 * k.size] = (k - 0.5).astype(np.float32)
+        got = api.expcast(torch.from_numpy(S).cuda(), torch.from_numpy(c8).cuda(),
+                          torch.from_numpy(krow).cuda()).cpu().numpy()
+        ref = oracle.expcast(S, c8, krow)
+        bad = np.nonzero(got != ref)[0]
+        assert bad.size == 0, (chunk, S[bad[:5]], c8[bad[:5]], krow[bad[:5]], got[bad[:5]], ref[bad[:5]])
+        total += n
+    assert total >= 10 ** 8
 
 
 # Measured on MI355X: the FP8 matrix-core 128-term dot product is exact when

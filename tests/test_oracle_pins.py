@@ -605,3 +605,31 @@ def test_kmeans_warm_start_composes(oracle_mod):
     # warm-starting from converged centroids does not raise the objective
     _, _, hist = oracle_mod.kmeans_warm(vh, C8, 4, history=True)
     assert np.all(np.diff(hist) <= 1e-9 * hist[0]) and hist[-1] <= J8 * (1 + 1e-12)
+
+
+def test_v_smooth_beats_plain_quantisation(oracle_mod):
+    """Direction check on the value term (agihunt V-Smooth bullet: only the
+    residual after the block mean is quantised): with the same permutation
+    and the same per-(block, channel) amax/448 scale rule, mean + E4M3
+    residual reconstructs V better than E4M3 of V itself, on every head of
+    the tiny workload, in k-means and in sequence order."""
+    cfg = synth.CONFIGS[0]
+    _, _, v = synth.make_inputs(cfg, 0)
+    q = k = v  # Q and K do not enter the value reconstruction
+    L, d = cfg.L, cfg.d
+    for h in range(cfg.H):
+        x = oracle_mod.bf16_to_f32(v[0, h]).astype(np.float64)
+        a, _, _ = oracle_mod.kmeans(v[0, h], 8, 8, oracle_mod.head_seed(0, 0, h, cfg.H))
+        for perm in (oracle_mod.stable_perm(a, 8), np.arange(L, dtype=np.int32)):
+            P = oracle_mod.prepare_head(q[0, h], k[0, h], v[0, h], perm)
+            xp = x[perm].reshape(L // 128, 128, d)                          # permuted blocks
+            dec = oracle_mod.e4m3_decode(P["v8"]).transpose(0, 2, 1)           # [nb,128,d]
+            smooth = P["v_mean"][:, None, :] + P["v_scale"][:, None, :].astype(np.float64) * dec
+            amax = np.abs(xp.astype(np.float32)).max(axis=1)                   # [nb,d]
+            s = (amax / np.float32(448)).astype(np.float32)
+            inv = (np.float32(448) / amax).astype(np.float32)
+            plain = s[:, None, :].astype(np.float64) * oracle_mod.e4m3_decode(
+                oracle_mod.e4m3_encode((xp.astype(np.float32) * inv[:, None, :]).astype(np.float32)))
+            e_s = np.linalg.norm(smooth - xp) / np.linalg.norm(xp)
+            e_p = np.linalg.norm(plain - xp) / np.linalg.norm(xp)
+            assert e_s < e_p, (h, e_s, e_p)

@@ -489,3 +489,69 @@ def test_dump_instances_compute_what_plain_ones_do(api, d):
         b = dump()[0]
         torch.cuda.synchronize()
         assert torch.equal(a, b), name
+
+
+# ------------------------------------------------------- extreme inputs --
+
+def _extreme_inputs(case, L=700, d=128, seed=91):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((1, 2, L, d))
+    k = rng.standard_normal((1, 2, L, d)) + 0.5
+    v = rng.standard_normal((1, 2, L, d))
+    if case == "peaked":          # scores x64: nearly one-hot rows, most bytes clamp to 0
+        q *= 8.0
+        k *= 8.0
+    elif case == "flat":          # nearly uniform attention
+        q *= 1e-6
+    elif case == "large_v_zeros":  # large values, a zero channel, a zero 128-token block
+        v *= 1e4
+        v[:, :, :, 5] = 0.0
+        v[:, :, 128:256, :] = 0.0
+    return tuple(synth.f32_to_bf16_bits(a.astype(np.float32)) for a in (q, k, v))
+
+
+@pytest.mark.parametrize("case", ["peaked", "flat", "large_v_zeros"])
+def test_attention_extreme_inputs(api, case):
+    """V-Smooth (ExpCast and exp-then-cast), SAGE INT8 and 4-bit V-Smooth on
+    inputs the synthetic workloads do not produce, against the oracle: given
+    the kernel's scores within the given-S bar, end to end within twice the
+    output bar (these rows are as short as the small cases)."""
+    q, k, v = _extreme_inputs(case)
+    B, H, L, d = q.shape
+    perm = synth.random_perms(B, H, L, 92)
+    qd, kd, vd = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    P = api.prepare(qd, kd, vd, perm_in=torch.from_numpy(perm).cuda())
+    for pc in (0, 1):
+        out = api.attention(P, prob_cast=pc).cpu().numpy()
+        assert np.all(np.isfinite(out)), (case, pc)
+        ref = _oracle_out(q, k, v, perm, prob_cast=pc)
+        S = np.zeros((B, H, 3 * 256, 768), np.float32)
+        for bh in range(B * H):
+            for qt in range(3):
+                S[0, bh, qt * 256:(qt + 1) * 256] = api.attention_dump(P, bh, qt, prob_cast=pc)[1].cpu().numpy()
+        refS = _oracle_out(q, k, v, perm, prob_cast=pc, scores=S[:, :, :L])
+        rs = rel_l2(out, refS)
+        r = rel_l2(out, ref)
+        print("extreme %s prob_cast=%d: given-S rel-L2 %.3g, end-to-end %.3g" % (case, pc, rs, r))
+        assert rs <= GIVEN_S_REL and r <= 2 * REL_L2
+    S8 = api.sage_prepare(qd, kd, vd, qk_dtype="int8")
+    outs = api.sage_attention(S8).cpu().numpy()
+    refs = np.stack([[oracle.sage_attention_head(oracle.sage_prepare_head(q[0, h], k[0, h], v[0, h], "int8"),
+                                                 L, "int8") for h in range(H)]])
+    print("extreme %s SAGE int8: rel-L2 %.3g" % (case, rel_l2(outs, refs)))
+    assert rel_l2(outs, refs) <= GIVEN_S_REL  # INT8 scores are exact
+    P4 = api.prepare(qd, kd, vd, perm_in=torch.from_numpy(perm).cuda(), v_format=1)
+    out4 = api.attention(P4).cpu().numpy()
+    ref4 = np.stack([[oracle.attention_head_fp4v(oracle.prepare_head_fp4v(q[0, h], k[0, h], v[0, h], perm[0, h]), L)
+                      for h in range(H)]])
+    print("extreme %s 4-bit: end-to-end rel-L2 %.3g" % (case, rel_l2(out4, ref4)))
+    assert np.all(np.isfinite(out4)) and rel_l2(out4, ref4) <= 4e-3
+
+
+def test_attention_single_partial_block(api):
+    """L = 127: one block with one padded key, against the oracle."""
+    B, H, L, d = 1, 2, 127, 64
+    q, k, v = _inputs(B, H, L, d, 93, None)
+    perm = synth.random_perms(B, H, L, 94)
+    P = api.prepare(dev_bf16(q), dev_bf16(k), dev_bf16(v), perm_in=torch.from_numpy(perm).cuda())
+    _check_attention(api, P, q, k, v, perm, 8, 0, "attention L=127")

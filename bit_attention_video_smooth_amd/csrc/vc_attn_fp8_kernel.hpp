@@ -266,6 +266,12 @@ struct Fp8Wave {
     float cf[2][8];
     // 4-bit: E8M0 byte (e + 127) of each query tile's probability group
     int sp[2];
+    // E4M3 1.0 in every byte: the A operand of the 8-bit row sums. Kept
+    // resident where registers allow (rebuilding it each block costs more
+    // than its 8 registers); the INT8 SAGE instance, whose score products
+    // need more registers, rebuilds it per block instead of spilling.
+    static constexpr bool ONES_RESIDENT = MODE != REC_SAGE_I8;
+    v8i ones8;
 
     __device__ __forceinline__ Fp8Wave(const AttnArgs& args, int bh_, int qtile, int w_, int lane_)
         : a(args), bh(bh_), w(w_), lane(lane_) {
@@ -303,6 +309,7 @@ struct Fp8Wave {
             const int qblk = min(q0 / BLK, nb - 1);
             sq = a.q_scale[(size_t)bh * nb + qblk];
         }
+        if (ONES_RESIDENT) ones8 = e4m3_ones();
         // the Q operands and scale are in registers before any block copy is
         // issued, so no later wait on them can drain the copy pipeline
         __builtin_amdgcn_s_waitcnt(0);
@@ -644,16 +651,21 @@ struct Fp8Wave {
         }
     }
 
+    __device__ __forceinline__ static v8i e4m3_ones() {
+        int one4;
+        asm volatile("v_mov_b32 %0, 0x38383838" : "=v"(one4));
+        v8i r;
+#pragma unroll
+        for (int i = 0; i < 8; i++) r[i] = one4;
+        return r;
+    }
+
     // Row sums (ones(16x128) * P^T, exact), V8^T P^T on the matrix
     // cores, and O += s_v (.) acc + l_b mean_b on the vector ALU, one channel
     // tile behind the products.
     __device__ __forceinline__ void slot_pv(const lds_u8* st) {
         const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
-        v8i ones;  // E4M3 1.0, made here so it takes no register across the block
-        int one4;
-        asm volatile("v_mov_b32 %0, 0x38383838" : "=v"(one4));
-#pragma unroll
-        for (int i = 0; i < 8; i++) ones[i] = one4;
+        const v8i ones = ONES_RESIDENT ? ones8 : e4m3_ones();
         v8i pv[2];
         float ell[2];
 #pragma unroll

@@ -414,7 +414,15 @@ def clock_under_load(launch, stream, n=20):
         launch()
     info = {"sclk_mhz": None, "power_cap_w": None, "clock_source": "rocm-smi during %d attention launches" % n}
     try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--showmaxpower"], capture_output=True, text=True, timeout=30)
+        # rocm-smi is a Python script: run it with this interpreter, not
+        # through its "env python3" line, so no process in between replaces
+        # itself (under a profiler that preloads into every process, such an
+        # exec would come after that process had opened the GPU)
+        import shutil
+        import sys
+        smi = shutil.which("rocm-smi") or "/opt/rocm/bin/rocm-smi"
+        r = subprocess.run([sys.executable, smi, "--showclocks", "--showmaxpower"], capture_output=True, text=True,
+                           timeout=30)
         txt = r.stdout
         m = re.search(r"sclk clock level:\s*\w+:\s*\((\d+)\s*Mhz\)", txt, re.I)
         if m:

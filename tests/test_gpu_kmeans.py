@@ -43,20 +43,27 @@ def dev_bf16(u16):
     return torch.from_numpy(np.ascontiguousarray(u16)).view(torch.bfloat16).cuda()
 
 
-def _candidates(v_head, C):
+def _candidates(v_head, C, chunk=2048):
     """Exact scores and, per token, the centroids within the error bound of
     the best one (a dict token -> sorted candidates, only where there are
-    several) and the best centroid (lowest index among exact ties)."""
-    x = oracle.bf16_to_f32(v_head).astype(np.float64)
+    several) and the best centroid (lowest index among exact ties); tokens
+    in chunks so that large k stays within host memory."""
+    x_all = oracle.bf16_to_f32(v_head).astype(np.float64)
     C = C.astype(np.float64)
     half = 0.5 * (C * C).sum(axis=1)
-    S = x @ C.T - half[None, :]
-    E = 2.0 ** -14 * (np.abs(x) @ np.abs(C).T + half[None, :])
-    best = np.argmax(S, axis=1)
-    rows = np.arange(x.shape[0])
-    near = (S[rows, best][:, None] - S) <= (E[rows, best][:, None] + E)
-    cnt = near.sum(axis=1)
-    ties = {int(t): tuple(np.nonzero(near[t])[0].tolist()) for t in np.nonzero(cnt > 1)[0]}
+    aC = np.abs(C).T
+    best = np.empty(x_all.shape[0], np.int64)
+    ties = {}
+    for t0 in range(0, x_all.shape[0], chunk):
+        x = x_all[t0:t0 + chunk]
+        S = x @ C.T - half[None, :]
+        E = 2.0 ** -14 * (np.abs(x) @ aC + half[None, :])
+        b = np.argmax(S, axis=1)
+        rows = np.arange(x.shape[0])
+        near = (S[rows, b][:, None] - S) <= (E[rows, b][:, None] + E)
+        best[t0:t0 + x.shape[0]] = b
+        for t in np.nonzero(near.sum(axis=1) > 1)[0]:
+            ties[int(t0 + t)] = tuple(np.nonzero(near[t])[0].tolist())
     return best, ties
 
 
@@ -117,7 +124,14 @@ CASES = [  # B, H, L, d, k, grid, outlier settings
     (2, 1, 3000, 64, 24, None, {}),
     (1, 2, 9000, 128, 71, (9, 25, 40), {"outlier_frac": 0.005, "outlier_factor": 30.0}),  # a 7-centroid last tile
     (1, 1, 700, 128, 6, None, {}),
+    (1, 1, 500, 128, 1, None, {}),           # one cluster: the identity permutation
+    (1, 1, 300, 64, 300, None, {}),          # k = L, the largest k a shape allows
 ]
+
+# k in the thousands and the library's largest k (16384); centroids are
+# tokens with a small seeded jitter (a k-means round on the CPU would
+# dominate the test's time)
+LARGE_K = [(1, 1, 5000, 64, 4096), (1, 1, 16500, 64, 16384), (1, 1, 3000, 128, 1500)]
 
 
 @pytest.mark.parametrize("case", CASES)
@@ -137,6 +151,24 @@ def test_kmeans_steps_match_oracle(api, case, rounds):
         for h in range(H):
             _check_head(api, v[b, h], C[b, h], perm[b, h], Cout[b, h] if rounds == 1 else None,
                         "%s rounds=%d b=%d h=%d" % ((B, H, L, d, k), rounds, b, h))
+
+
+@pytest.mark.parametrize("case", LARGE_K)
+def test_kmeans_steps_large_k(api, case):
+    """One round: the permutation checks the assignment, the centroids the
+    update."""
+    rounds = 1
+    B, H, L, d, k = case
+    q, kk, v = synth.make_inputs(synth.custom(B, H, L, d), 70 + k)
+    rng = np.random.default_rng(k)
+    pick = np.sort(rng.choice(L, size=k, replace=False))
+    x = oracle.bf16_to_f32(v[0, 0])
+    C = (x[pick] + 0.05 * rng.standard_normal((k, d))).astype(np.float32)[None, None]
+    Cout = torch.empty((B, H, k, d), dtype=torch.float32, device="cuda")
+    P = api.prepare(dev_bf16(q), dev_bf16(kk), dev_bf16(v), kmeans_k=k, kmeans_iters=rounds,
+                    centroids_in=torch.from_numpy(C).cuda(), centroids_out=Cout)
+    _check_head(api, v[0, 0], C[0, 0], P.perm.cpu().numpy()[0, 0], Cout.cpu().numpy()[0, 0] if rounds == 1 else None,
+                "%s rounds=%d" % ((B, H, L, d, k), rounds))
 
 
 def test_kmeans_steps_full_size(api):

@@ -174,8 +174,10 @@ __global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict
                                                       int mode) {
     constexpr int CPL = D / 64;  // channels per lane
     constexpr int KW = BLK / 4;  // keys per wave
+    constexpr int PITCH = BLK + 16;  // LDS row of one channel's codes, padded against bank conflicts
     __shared__ double psum[4][D];
     __shared__ float pmax[4][D];
+    __shared__ __attribute__((aligned(16))) uint8_t tile[D * PITCH];
     const int b = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63;
     const int i0 = b * BLK;
@@ -231,7 +233,7 @@ __global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict
             vmean[gi] = mu[e];
             vscale[gi] = s;
         }
-        uint8_t* out = codes + gi * BLK + 8 * w;
+        uint8_t* out = tile + c * PITCH + 8 * w;
 #pragma unroll
         for (int bb = 0; bb < 4; bb++) {
             // slots 32 bb + 8 w + j hold keys 32 w + 16 (j / 4) + 4 bb + j % 4
@@ -244,6 +246,14 @@ __global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict
             *reinterpret_cast<uint2*>(out + 32 * bb) =
                 make_uint2(e4m3_pk4(y[0], y[1], y[2], y[3]), e4m3_pk4(y[4], y[5], y[6], y[7]));
         }
+    }
+    // the block's D x 128 codes are contiguous in HBM: 16 bytes per lane
+    __syncthreads();
+    uint8_t* dst = codes + ((size_t)bh * nb + b) * D * BLK;
+#pragma unroll
+    for (int i = 0; i < D * BLK / (16 * 256); i++) {
+        const int q = t + 256 * i, row = q / (BLK / 16), ch = q % (BLK / 16);
+        *reinterpret_cast<uint4*>(dst + 16 * q) = *reinterpret_cast<const uint4*>(tile + row * PITCH + 16 * ch);
     }
 }
 

@@ -278,8 +278,11 @@ __global__ __launch_bounds__(256) void quant_v4_kernel(const uint16_t* __restric
                                                        float* __restrict__ vmean, int L, int nb) {
     constexpr int CPL = D / 64;
     constexpr int KW = BLK / 4;
+    constexpr int RB = BLK / 2;      // code bytes per channel row
+    constexpr int PITCH = RB + 16;   // LDS row, padded against bank conflicts
     __shared__ double psum[4][D];
     __shared__ float pmax[4][D][4];
+    __shared__ __attribute__((aligned(16))) uint8_t tile[D * PITCH];
     const int b = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63;
     const int i0 = b * BLK;
@@ -333,7 +336,7 @@ __global__ __launch_bounds__(256) void quant_v4_kernel(const uint16_t* __restric
         const int c = CPL * lane + e;
         const size_t gi = ((size_t)bh * nb + b) * D + c;
         uint32_t ebytes = 0;
-        uint8_t* out = codes + gi * (BLK / 2);
+        uint8_t* out = tile + c * PITCH;
 #pragma unroll
         for (int g = 0; g < 4; g++) {
             const float A = fmaxf(fmaxf(pmax[0][c][g], pmax[1][c][g]), fmaxf(pmax[2][c][g], pmax[3][c][g]));
@@ -350,6 +353,14 @@ __global__ __launch_bounds__(256) void quant_v4_kernel(const uint16_t* __restric
             vmean[gi] = mu[e];
             vexp[gi] = ebytes;
         }
+    }
+    // the block's D x 64 code bytes are contiguous in HBM: 16 bytes per lane
+    __syncthreads();
+    uint8_t* dst = codes + ((size_t)bh * nb + b) * D * RB;
+#pragma unroll
+    for (int i = 0; i < D * RB / (16 * 256); i++) {
+        const int q = t + 256 * i, row = q / (RB / 16), ch = q % (RB / 16);
+        *reinterpret_cast<uint4*>(dst + 16 * q) = *reinterpret_cast<const uint4*>(tile + row * PITCH + 16 * ch);
     }
 }
 

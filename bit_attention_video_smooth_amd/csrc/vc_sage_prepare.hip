@@ -179,6 +179,8 @@ __global__ __launch_bounds__(256) void sage_quant_v_kernel(const uint16_t* __res
                                                            uint8_t* __restrict__ codes, int L, int nb) {
     constexpr int CPL = D / 64;
     constexpr int KW = BLK / 4;
+    constexpr int PITCH = BLK + 16;  // LDS row of one channel's codes, padded against bank conflicts
+    __shared__ __attribute__((aligned(16))) uint8_t tile[D * PITCH];
     const int b = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63;
     const int i0 = b * BLK + KW * w;
@@ -204,7 +206,7 @@ __global__ __launch_bounds__(256) void sage_quant_v_kernel(const uint16_t* __res
     for (int e = 0; e < CPL; e++) {
         const int c = CPL * lane + e;
         const float inv = vinv[(size_t)bh * D + c];
-        uint8_t* out = codes + (((size_t)bh * nb + b) * D + c) * BLK + 8 * w;
+        uint8_t* out = tile + c * PITCH + 8 * w;
 #pragma unroll
         for (int bb = 0; bb < 4; bb++) {
             float y[8];
@@ -216,6 +218,14 @@ __global__ __launch_bounds__(256) void sage_quant_v_kernel(const uint16_t* __res
             *reinterpret_cast<uint2*>(out + 32 * bb) =
                 make_uint2(e4m3_pk4(y[0], y[1], y[2], y[3]), e4m3_pk4(y[4], y[5], y[6], y[7]));
         }
+    }
+    // the block's D x 128 codes are contiguous in HBM: 16 bytes per lane
+    __syncthreads();
+    uint8_t* dst = codes + ((size_t)bh * nb + b) * D * BLK;
+#pragma unroll
+    for (int i = 0; i < D * BLK / (16 * 256); i++) {
+        const int q = t + 256 * i, row = q / (BLK / 16), ch = q % (BLK / 16);
+        *reinterpret_cast<uint4*>(dst + 16 * q) = *reinterpret_cast<const uint4*>(tile + row * PITCH + 16 * ch);
     }
 }
 

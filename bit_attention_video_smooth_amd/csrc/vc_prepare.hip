@@ -18,7 +18,8 @@
 namespace vc {
 
 // ------------------------------------------------------------------------
-// a1: per-channel K mean, split over token chunks.  partial[bh][split][D].
+// QK smoothing, K side: per-channel K mean, split over token chunks.
+// partial[bh][split][D].
 // ------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void k_colsum_partial(const uint16_t* __restrict__ k,
@@ -96,7 +97,7 @@ __device__ __forceinline__ float block_max_256(float v, float* red4) {
 }
 
 // ------------------------------------------------------------------------
-// a7 / a8: per-block scalar-scale FP8 of Q (original order, GATHER=false) or
+// Per-block scalar-scale FP8 of Q (original order, GATHER=false) or
 // of K - kbar (permuted order, GATHER=true).  Grid (nb, B*H), 256 threads.
 // ------------------------------------------------------------------------
 template <int D, bool GATHER>
@@ -156,15 +157,16 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(const uint16_t* __restric
 }
 
 // ------------------------------------------------------------------------
-// a6: V-Smooth residual quantisation of one permuted 128-token block.
+// V-Smooth residual quantisation of one permuted 128-token block.
 // Wave w holds keys 32 w .. 32 w + 31 of the block (slots in permuted order)
 // and lane l holds channels CPL l .. CPL l + CPL - 1 (CPL = D / 64), so each
 // key's row is one coalesced load across the wave and the values stay in
 // registers: per-channel fp64 sums (exact for bf16 inputs, so the order does
-// not matter) and maxima are combined over the four waves through LDS; the
-// codes are written channel-major in the slot order of the attention
-// kernel's P V operand, where the 32 keys of wave w fill slots
-// 32 b + 8 w .. 32 b + 8 w + 7 of every channel row (b = 0..3).
+// not matter) and maxima are combined over the four waves through LDS.  The
+// codes are channel-major in the slot order of the attention kernel's P V
+// operand, where the 32 keys of wave w fill slots 32 b + 8 w .. 32 b + 8 w +
+// 7 of every channel row (b = 0..3); they are assembled in an LDS tile and
+// the block's D x 128 bytes, contiguous in HBM, leave as 16-byte stores.
 template <int D>
 __global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict__ v,
                                                       const int32_t* __restrict__ perm,

@@ -262,7 +262,7 @@ def expcast_z(z, z_off: int = 8) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
-# Blockwise attention (steps a9-a14).
+# Blockwise attention.
 # --------------------------------------------------------------------------
 
 def skip_threshold(skip_lambda: float) -> np.float32:

@@ -209,7 +209,7 @@ static inline float vco_bf16(uint16_t u)
 }
 
 /* ------------------------------------------------------------------------ */
-/* Step a1 (QK smoothing, K half): per-channel mean of K over all L tokens.  */
+/* QK smoothing, K side: per-channel mean of K over all L tokens.           */
 /* The pages measure with QK smoothing applied; subtracting one vector from  */
 /* every key adds a per-query constant to each score row, which softmax     */
 /* ignores.                                                                  */
@@ -225,7 +225,7 @@ void vco_k_mean(const uint16_t* k, int L, int d, float* kbar)
 }
 
 /* ------------------------------------------------------------------------ */
-/* Steps a2-a4: Lloyd k-means on x_j = fp32(V_j) of one head.                 */
+/* Lloyd k-means on x_j = fp32(V_j) of one head.                            */
 /*  assign: argmin_c sum_ch (x - C_c)^2 in double, ties -> lowest c;          */
 /*  update: C_c = fp32(double sum / n_c); an empty cluster keeps C_c.         */
 /* J_hist (iters+1 entries, may be NULL): J_hist[0] is the objective of the   */
@@ -330,7 +330,7 @@ double vco_kmeans_warm(const uint16_t* v, int L, int d, int k, int iters, const 
     return J;
 }
 
-/* Step a5: stable argsort of the assignment.  perm[i] = original token that
+/* The permutation: stable argsort of the assignment.  perm[i] = original token that
  * lands in permuted slot i; slots are ordered by cluster id, then token id. */
 void vco_stable_perm(const int32_t* a, int L, int k, int32_t* perm)
 {
@@ -372,7 +372,8 @@ static inline uint8_t vco_quant(float x, float inv)
 }
 
 /* ------------------------------------------------------------------------ */
-/* Steps a6-a8 for one head, given the permutation.                           */
+/* Q/K codes, block means, residual scales and codes for one head, given the */
+/* permutation.                                                             */
 /*  q,k,v : bf16 bits [L, d] of this head                                     */
 /*  perm  : [L]                                                               */
 /*  q8,k8 : [Lp, d] codes (Q in original order, K' = K - kbar in perm order)  */
@@ -524,7 +525,7 @@ float vco_kb(int z_off) { return (float)(56.0 - 0.35 + 8.0 * (double)z_off); }
 float vco_c0(int d) { return (float)(1.4426950408889634074 / sqrt((double)d)); }
 
 /* ------------------------------------------------------------------------ */
-/* Steps a9-a14: blockwise attention for query rows [r0, r1) of one head.    */
+/* Blockwise attention for query rows [r0, r1) of one head.                 */
 /*                                                                          */
 /* mode 0 (quantised, the method):                                          */
 /*   S_j   = fp32(exact sum_c qhat_c khat_jc)                                */

@@ -384,7 +384,15 @@ def main():
                     "ms_without_kmeans_median": float(np.median(quant_each)),
                     "ms_without_kmeans_min": float(np.min(quant_each)),
                     "quant_algorithmic_bytes": quant_bytes,
-                    "quant_gbs": quant_bytes / quant_ms / 1e6},
+                    "quant_gbs": quant_bytes / quant_ms / 1e6,
+                    "gbs_with_kmeans": quant_bytes / prep_ms / 1e6,
+                    # k-means = prepare with minus without; its assign steps
+                    # do 2*B*H*L*k*d FLOP per round (k = nb centroids)
+                    "kmeans": {"ms": prep_ms - quant_ms, "rounds": 8, "k": nb,
+                               "assign_tflop": 2.0 * B * H * L * nb * d * 8 / 1e12,
+                               "assign_tflops_over_kmeans_time": 2.0 * B * H * L * nb * d * 8 / (prep_ms - quant_ms) / 1e9,
+                               "frac_bf16_peak": 2.0 * B * H * L * nb * d * 8 / (prep_ms - quant_ms) / 1e9
+                               / BF16_PEAK_TFLOPS}},
         "bf16_attention": bf16,
         "exp_then_cast_attention": exp_then_cast,
         "sage_baseline": sage,
@@ -474,7 +482,14 @@ def cpu_baseline(cfg, qn, kn, vn, rows):
     oracle.attention_head(P, L, 8, rows=(0, rows))
     t_attn = time.time() - t0
     fl = 4.0 * rows * L * d
-    return {"value": fl / t_attn / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+    cpu = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
+    return {"value": fl / t_attn / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "cpu_model": cpu,
+            "kind": "oracle",
             "sample": "head (0,0) of %s: oracle prepare (identity permutation, %.2fs) then blockwise "
                       "ExpCast attention for %d query rows x %d keys (%.2fs); k-means not included"
                       % (cfg.name, t_prep, rows, L, t_attn)}

@@ -106,7 +106,7 @@ def copy_probe(mib):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: this library has no multi-GPU path "
               "(the workload shards by (batch, head) with no exchange between GPUs)", file=sys.stderr)
         sys.exit(2)
     if args.copy_probe:

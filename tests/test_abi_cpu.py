@@ -227,3 +227,32 @@ def test_fp4_v_format_rules(lib):
         _lib.vc_sage_attention_fwd(s, _lib.make_sage_params(), _lib.vc_attn_params(8, 0, 0.0, 1, 1), _sprep(),
                                    FAKE, 0)
     assert e.value.code == _lib.VC_ERR_UNSUPPORTED
+
+
+def test_error_text_is_per_thread(lib):
+    """vc_last_error() is thread-local: an error raised on one thread is not
+    seen by another, and a fresh thread starts with an empty text."""
+    import threading
+    s = _lib.shape_of(1, 1, 256, 64)
+    seen = {}
+
+    def failing():
+        with pytest.raises(_lib.VCError):
+            _lib.vc_attention_fwd(s, _lib.vc_attn_params(9, 0), _prep(), FAKE, 0)
+        seen["failing"] = _lib.vc_last_error()
+        barrier.wait()  # stay alive while the other thread looks
+        barrier.wait()
+
+    def clean():
+        barrier.wait()
+        seen["clean"] = _lib.vc_last_error()
+        barrier.wait()
+
+    barrier = threading.Barrier(2, timeout=30)
+    ts = [threading.Thread(target=failing, daemon=True), threading.Thread(target=clean, daemon=True)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join(timeout=60)
+    assert seen["failing"] != ""
+    assert seen["clean"] == ""

@@ -264,8 +264,10 @@ struct Fp8Wave {
     // the coefficients of the block's eight 16-key tiles
     float sqx[2];
     float cf[2][8];
-    // 4-bit: E8M0 byte (e + 127) of each query tile's probability group
+    // 4-bit: E8M0 byte (e + 127) of each query tile's probability group, and
+    // the lane's largest valid score of the block (its group's 32 keys)
     int sp[2];
+    float lmx[2];
     // E4M3 1.0 in every byte: the A operand of the 8-bit row sums. Kept
     // resident where registers allow (rebuilding it each block costs more
     // than its 8 registers); the INT8 SAGE instance, whose score products
@@ -419,6 +421,10 @@ struct Fp8Wave {
                     for (int i = 0; i < 4; i++) mx[qt] = fmaxf(mx[qt], (16 * kt + i < lim) ? S[qt][kt][i] : -INFINITY);
             }
         }
+        if (FP4V) {
+            lmx[0] = mx[0];
+            lmx[1] = mx[1];
+        }
         max_over_groups2(mx[0], mx[1]);
 #pragma unroll
         for (int qt = 0; qt < 2; qt++) {
@@ -513,15 +519,11 @@ struct Fp8Wave {
                     p[4 * kt + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[qt][kt][i], c, krow[qt]));
                     if (MASKED && !(16 * kt + i < lim)) p[4 * kt + i] = 0.f;  // keys past L: code 0
                 }
-            // compiler-visible maxima: these read transcendental results, whose
-            // wait states the compiler inserts only before code it can see
-            float m0 = fmaxf(p[0], p[1]), m1 = fmaxf(p[2], p[3]);
-#pragma unroll
-            for (int j = 4; j < 32; j += 4) {
-                m0 = fmaxf(fmaxf(m0, p[j]), p[j + 1]);
-                m1 = fmaxf(fmaxf(m1, p[j + 2]), p[j + 3]);
-            }
-            const int ex = e8m0_exp(fmaxf(m0, m1));
+            // the group's largest probability from its largest score: the FMA
+            // is monotone in S for c >= 0, and so is 2^z; a group with no
+            // valid key has largest probability 0
+            const float zg = lmx[qt] == -INFINITY ? -INFINITY : __builtin_fmaf(lmx[qt], c, krow[qt]);
+            const int ex = e8m0_exp(__builtin_amdgcn_exp2f(zg));
             sp[qt] = ex + 127;
             const float sc = ldexpf(1.0f, max(ex, -126));
 #pragma unroll

@@ -41,7 +41,12 @@ __device__ __forceinline__ uint32_t lds_addr(const lds_u8* p) {
 // compiler neither waits on them nor counts them: every wait on these copies
 // is explicit (wait_vmcnt) and every LDS hand-over goes through a barrier.
 // They have no register outputs; M0 (the wave's LDS base) is set in the same
-// block, one wait state before the load.
+// block, one wait state before the load.  M0 is declared clobbered; clang
+// warns that it is a reserved register, which it does not save around the
+// asm.  The kernels that include this header leave M0 to these blocks alone
+// (the compiled code has no other M0 access), so the warning is silenced here.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void lds_dma16(const v4si& r, const lds_u8* lds_wave_base, uint32_t voff,
                                           uint32_t soff) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
@@ -64,6 +69,8 @@ __device__ __forceinline__ void lds_dma16_flat(const void* g, const lds_u8* lds_
                     "v"(reinterpret_cast<uint64_t>(g))
                  : "memory", "m0");
 }
+
+#pragma clang diagnostic pop
 
 // s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
 // 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).

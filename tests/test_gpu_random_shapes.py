@@ -1,0 +1,78 @@
+"""GPU parity over seeded random shapes (B, H, L, d and the permutation all
+drawn; L includes values next to block boundaries), through the C ABI.
+Per case: Q/K/V codes, scales and means bit-exact against the oracle, and,
+given the kernel's own scores, the output within the given-S bar (rel-L2
+1e-4, max-abs 1e-3 of max).  End to end, against the oracle's exactly
+rounded scores, the median over the cases is held to the output bar and the
+worst case to twice it (single cases have a tail from the matrix core's
+inexact 128-term score sums, as the seed sweep of the tiny workload shows)."""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_attention_video_smooth_amd import synth
+
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+from test_gpu_parity import (GIVEN_S_MAXABS, GIVEN_S_REL, _end_to_end_bar, _kernel_scores,  # noqa: E402
+                             _oracle_out, dev_bf16, rel_l2)
+
+pytestmark = pytest.mark.gpu
+
+
+def _shapes(n=10, seed=2026):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        d = int(rng.choice([64, 128]))
+        B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+        if i % 3 == 0:
+            L = int(128 * rng.integers(1, 20) + rng.choice([-1, 0, 1]))  # next to a block boundary
+        else:
+            L = int(rng.integers(1, 3000))
+        L = max(L, 1)
+        out.append((B, H, L, d, int(rng.integers(1 << 30))))
+    out.append((1, 1, 5000, 128, 7))
+    return out
+
+
+SHAPES = _shapes()
+
+
+@pytest.fixture(scope="module")
+def api():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    from bit_attention_video_smooth_amd import api as a
+    a._lib.load()
+    return a
+
+
+def test_random_shapes_match_oracle(api):
+    ends = []
+    for B, H, L, d, seed in SHAPES:
+        q, k, v = synth.make_inputs(synth.custom(B, H, L, d), seed % 100000)
+        perm = synth.random_perms(B, H, L, seed % 1000)
+        P = api.prepare(dev_bf16(q), dev_bf16(k), dev_bf16(v), perm_in=torch.from_numpy(perm).cuda())
+        g = {n: getattr(P, n).cpu().numpy() for n in ("q8", "k8", "q_scale", "k_scale", "v_scale", "v_mean")}
+        g["v8"] = api.v_codes_natural(P.v8).cpu().numpy()
+        for b in range(B):
+            for h in range(H):
+                o = oracle.prepare_head(q[b, h], k[b, h], v[b, h], perm[b, h])
+                for n in ("q8", "k8", "v8", "q_scale", "k_scale", "v_scale", "v_mean"):
+                    assert np.array_equal(g[n][b, h].view(np.uint8), o[n].view(np.uint8)), ((B, H, L, d), n)
+        out = api.attention(P).cpu().numpy()
+        ref = _oracle_out(q, k, v, perm)
+        refS = _oracle_out(q, k, v, perm, scores=_kernel_scores(api, P))
+        rs, mas = rel_l2(out, refS), float(np.abs(out - refS).max() / np.abs(refS).max())
+        r = rel_l2(out, ref)
+        print("random shape %s: given kernel S rel-L2 %.3g max-abs/max %.3g | end-to-end rel-L2 %.3g"
+              % ((B, H, L, d), rs, mas, r))
+        assert rs <= GIVEN_S_REL and mas <= GIVEN_S_MAXABS, (B, H, L, d)
+        ends.append(r / _end_to_end_bar(d)[0])
+    ends = np.array(ends)
+    print("end-to-end error / bar over %d shapes: median %.3g max %.3g" % (len(ends), np.median(ends), ends.max()))
+    assert np.median(ends) <= 1.0 and ends.max() <= 2.0

@@ -76,3 +76,60 @@ def test_random_shapes_match_oracle(api):
     ends = np.array(ends)
     print("end-to-end error / bar over %d shapes: median %.3g max %.3g" % (len(ends), np.median(ends), ends.max()))
     assert np.median(ends) <= 1.0 and ends.max() <= 2.0
+
+
+@pytest.mark.parametrize("qk", ["int8", "fp8"])
+def test_random_shapes_sage_match_oracle(api, qk):
+    """The SAGE-style baseline over the same shapes: codes and scales
+    bit-exact, given-S bar per case, end-to-end bar over the set."""
+    import test_gpu_sage as ts
+    ends = []
+    for B, H, L, d, seed in SHAPES[:6]:
+        q, k, v = synth.make_inputs(synth.custom(B, H, L, d), seed % 100000)
+        P = api.sage_prepare(dev_bf16(q), dev_bf16(k), dev_bf16(v), qk_dtype=qk)
+        g = {n: getattr(P, n).cpu().numpy() for n in ("q8", "k8", "q_scale", "k_scale", "v_scale")}
+        g["v8"] = api.v_codes_natural(P.v8).cpu().numpy()
+        for b in range(B):
+            for h in range(H):
+                o = oracle.sage_prepare_head(q[b, h], k[b, h], v[b, h], qk, 1)
+                for n in ("q8", "k8", "v8", "q_scale", "k_scale", "v_scale"):
+                    assert np.array_equal(g[n][b, h].view(np.uint8), o[n].view(np.uint8)), ((B, H, L, d), qk, n)
+        out = api.sage_attention(P).cpu().numpy()
+        ref = ts._oracle_out(q, k, v, qk)
+        refS = ts._oracle_out(q, k, v, qk, scores=ts._kernel_scores(api, P, 1))
+        rs, mas = rel_l2(out, refS), float(np.abs(out - refS).max() / np.abs(refS).max())
+        r = rel_l2(out, ref)
+        print("random shape sage %s %s: given kernel S rel-L2 %.3g max-abs/max %.3g | end-to-end rel-L2 %.3g"
+              % (qk, (B, H, L, d), rs, mas, r))
+        assert rs <= GIVEN_S_REL and mas <= GIVEN_S_MAXABS, (B, H, L, d)
+        ends.append(r / ts._end_to_end_bar(d)[0])
+    ends = np.array(ends)
+    assert np.median(ends) <= 1.0 and ends.max() <= 2.0
+
+
+def test_random_shapes_fp4_match_oracle(api):
+    """4-bit V-Smooth over the same shapes: codes, means and E8M0 scales
+    bit-exact, given-S bar per case, end-to-end bar (twice the 8-bit one)
+    over the set."""
+    import test_gpu_fp4v as tf
+    ends = []
+    for B, H, L, d, seed in SHAPES[:6]:
+        q, k, v = synth.make_inputs(synth.custom(B, H, L, d), seed % 100000)
+        perm = synth.random_perms(B, H, L, seed % 1000)
+        P = api.prepare(dev_bf16(q), dev_bf16(k), dev_bf16(v), perm_in=torch.from_numpy(perm).cuda(), v_format=1)
+        codes, exps = (t.cpu().numpy() for t in api.v4_codes_natural(P))
+        for b in range(B):
+            for h in range(H):
+                o = oracle.prepare_head_fp4v(q[b, h], k[b, h], v[b, h], perm[b, h])
+                assert np.array_equal(codes[b, h], o["v4"]) and np.array_equal(exps[b, h], o["v_exp"]), (B, H, L, d)
+        out = api.attention(P).cpu().numpy()
+        ref = tf._oracle_out(q, k, v, perm)
+        refS = tf._oracle_out(q, k, v, perm, scores=_kernel_scores(api, P))
+        rs, mas = rel_l2(out, refS), float(np.abs(out - refS).max() / np.abs(refS).max())
+        r = rel_l2(out, ref)
+        print("random shape fp4 %s: given kernel S rel-L2 %.3g max-abs/max %.3g | end-to-end rel-L2 %.3g"
+              % ((B, H, L, d), rs, mas, r))
+        assert rs <= GIVEN_S_REL and mas <= GIVEN_S_MAXABS, (B, H, L, d)
+        ends.append(r / tf._end_to_end_bar(d)[0])
+    ends = np.array(ends)
+    assert np.median(ends) <= 1.0 and ends.max() <= 2.0

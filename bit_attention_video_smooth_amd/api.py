@@ -15,6 +15,29 @@ def nblocks(L: int) -> int:
     return (L + BLK - 1) // BLK
 
 
+def _require(cond, msg):
+    """Argument check that survives python -O (the C ABI cannot see tensor
+    sizes, so a mis-sized buffer must be caught here)."""
+    if not cond:
+        raise ValueError(msg)
+
+
+def _check_bf16_inputs(q, k, v):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _require(t.dtype == torch.bfloat16, "%s must be bfloat16, got %s" % (name, t.dtype))
+        _require(t.is_contiguous(), "%s must be contiguous" % name)
+        _require(t.dim() == 4 and t.shape == q.shape,
+                 "%s must be [B,H,L,d]%s, got %s" % (name, "" if name == "q" else " like q", tuple(t.shape)))
+        _require(t.device == q.device, "%s is on %s, q on %s" % (name, t.device, q.device))
+
+
+def _check_out(out, shape, device):
+    _require(out.dtype in (torch.float32, torch.bfloat16), "out must be float32 or bfloat16, got %s" % out.dtype)
+    _require(out.is_contiguous(), "out must be contiguous")
+    _require(tuple(out.shape) == tuple(shape), "out must be %s, got %s" % (tuple(shape), tuple(out.shape)))
+    _require(out.device == device, "out is on %s, the inputs on %s" % (out.device, device))
+
+
 @dataclasses.dataclass
 class Prepared:
     shape: tuple
@@ -63,11 +86,11 @@ def prepare(q, k, v, *, perm_in=None, kmeans_k=0, kmeans_iters=8, seed=0, smooth
     and/or centroids_out (fp32 [B,H,k,d]) vsmooth_prepare_warm, whose k-means
     starts from centroids_in (None: the seeded init) and leaves its final
     centroids in centroids_out (may be the same tensor)."""
+    _check_bf16_inputs(q, k, v)
     B, H, L, d = q.shape
-    for t in (q, k, v):
-        assert t.dtype == torch.bfloat16 and t.is_contiguous() and t.shape == q.shape
     if perm_in is not None:
-        assert perm_in.dtype == torch.int32 and perm_in.is_contiguous() and tuple(perm_in.shape) == (B, H, L)
+        _require(perm_in.dtype == torch.int32 and perm_in.is_contiguous() and tuple(perm_in.shape) == (B, H, L)
+                 and perm_in.device == q.device, "perm_in must be contiguous int32 [B,H,L] on the inputs' device")
     warm = centroids_in is not None or centroids_out is not None
     if warm:
         if perm_in is not None:
@@ -75,7 +98,8 @@ def prepare(q, k, v, *, perm_in=None, kmeans_k=0, kmeans_iters=8, seed=0, smooth
         kk = kmeans_k if kmeans_k > 0 else nblocks(L)
         for t in (centroids_in, centroids_out):
             if t is not None:
-                assert t.dtype == torch.float32 and t.is_contiguous() and tuple(t.shape) == (B, H, kk, d)
+                _require(t.dtype == torch.float32 and t.is_contiguous() and tuple(t.shape) == (B, H, kk, d)
+                         and t.device == q.device, "centroids must be contiguous float32 [B,H,%d,%d]" % (kk, d))
     shape = _lib.shape_of(B, H, L, d)
     params = _lib.make_params(kmeans_k, kmeans_iters, seed, smooth_k, v_scale_mode, v_format)
     out = out if out is not None else alloc_prepared(B, H, L, d, q.device)
@@ -102,6 +126,7 @@ def attention(prep: Prepared, *, z_off=8, out_dtype=torch.float32, out=None, ski
     B, H, L, d = prep.shape
     if out is None:
         out = torch.empty((B, H, L, d), dtype=out_dtype, device=prep.q8.device)
+    _check_out(out, (B, H, L, d), prep.q8.device)
     od = 1 if out.dtype == torch.bfloat16 else 0
     params = _lib.vc_attn_params(z_off, od, skip_lambda, _prob_cast(prep, prob_cast), prep.v_format)
     _lib.vc_attention_fwd(_lib.shape_of(B, H, L, d), params, prep.c(), out, stream)
@@ -151,9 +176,8 @@ def sage_prepare(q, k, v, *, qk_dtype="int8", smooth_k=1, out: SagePrepared | No
                  ws: torch.Tensor | None = None, stream=None) -> SagePrepared:
     """vc_sage_prepare on bf16 [B,H,L,d] device tensors (qk_dtype "int8" or
     "fp8"; q/k/v block sizes 1/16/1, V in FP8 E4M3)."""
+    _check_bf16_inputs(q, k, v)
     B, H, L, d = q.shape
-    for t in (q, k, v):
-        assert t.dtype == torch.bfloat16 and t.is_contiguous() and t.shape == q.shape
     if qk_dtype not in SAGE_QK:
         raise ValueError("qk_dtype must be 'int8' or 'fp8'")
     shape = _lib.shape_of(B, H, L, d)
@@ -180,6 +204,7 @@ def sage_attention(prep: SagePrepared, *, z_off=8, prob_cast=1, out_dtype=torch.
     B, H, L, d = prep.shape
     if out is None:
         out = torch.empty((B, H, L, d), dtype=out_dtype, device=prep.q8.device)
+    _check_out(out, (B, H, L, d), prep.q8.device)
     od = 1 if out.dtype == torch.bfloat16 else 0
     params = _lib.vc_attn_params(z_off, od, 0.0, prob_cast)
     _lib.vc_sage_attention_fwd(_lib.shape_of(B, H, L, d), prep.params(), params, prep.c(), out, stream)
@@ -202,11 +227,11 @@ def sage_attention_dump(prep: SagePrepared, bh: int, q_tile: int, *, z_off=8, pr
 
 def attention_bf16(q, k, v, *, out_dtype=torch.float32, out=None, stream=None):
     """vc_attention_fwd_bf16 on bf16 [B,H,L,d] device tensors."""
+    _check_bf16_inputs(q, k, v)
     B, H, L, d = q.shape
-    for t in (q, k, v):
-        assert t.dtype == torch.bfloat16 and t.is_contiguous() and t.shape == q.shape
     if out is None:
         out = torch.empty((B, H, L, d), dtype=out_dtype, device=q.device)
+    _check_out(out, (B, H, L, d), q.device)
     od = 1 if out.dtype == torch.bfloat16 else 0
     _lib.vc_attention_fwd_bf16(_lib.shape_of(B, H, L, d), q, k, v, out, od, stream)
     return out

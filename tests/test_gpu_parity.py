@@ -295,7 +295,12 @@ def test_attention_scores_and_bytes(api, shape):
         diff = Pb[:n].astype(int) - rby.astype(int)
         bad = diff != 0
         frac = float(bad.mean())
-        dist = np.abs(ry.astype(np.float64) - (np.floor(ry.astype(np.float64)) + 0.5))
+        # distance of the oracle's unrounded byte to the nearest rounding midpoint
+        # (padded keys are -inf there and never mismatch: both sides give 0)
+        ry64 = ry.astype(np.float64)
+        fin = np.isfinite(ry64)
+        dist = np.full(ry64.shape, np.inf)
+        dist[fin] = np.abs(ry64[fin] - (np.floor(ry64[fin]) + 0.5))
         print("dump bh=%d qt=%d: S max |dS|/tol %.3f, byte mismatch %.2e (max |d| %d)"
               % (bh, qt, float((np.abs(S[:n] - rS) / (tolS + 1e-30)).max()), frac, np.abs(diff).max()))
         assert np.abs(diff).max() <= 1

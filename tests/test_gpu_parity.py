@@ -45,6 +45,17 @@ SHAPES = [(1, 2, 1024, 64, (4, 16, 16)), (1, 3, 300, 128, None), (2, 2, 129, 64,
 # ----------------------------------------------------------- primitives ----
 
 def test_e4m3_encoder_bit_exact(api):
+    """The device encoder against the oracle's, over every class of fp32
+    inputs up to 448 in magnitude.  For |x| <= 448 the saturating
+    round-to-nearest-even E4M3 code depends only on the sign, the exponent
+    and the top 7 mantissa bits (the upper 16 bits of x) and on whether the
+    low 16 bits are zero: the rounding position is at most 3 mantissa bits
+    down for normal codes and moves right by at most 4 more positions
+    through the subnormal codes, staying inside the upper 16 bits, so the low
+    16 bits only act as the sticky bit.  Every upper-16 pattern from 0 to
+    448, both signs, is taken with low halves zero and nonzero (ties,
+    just-above and just-below included), plus random values, 448, 464,
+    +-1e30 and +-0."""
     hi16 = np.arange(0, 0x43E0 + 1, dtype=np.uint32)
     lows = np.array([0, 1, 0x7FFF, 0x8000, 0x8001, 0xFFFF, 0x4000, 0xC000], np.uint32)
     u = (hi16[:, None] << 16 | lows[None, :]).ravel()

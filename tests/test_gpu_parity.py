@@ -49,10 +49,10 @@ def test_e4m3_encoder_bit_exact(api):
     inputs up to 448 in magnitude.  For |x| <= 448 the saturating
     round-to-nearest-even E4M3 code depends only on the sign, the exponent
     and the top 7 mantissa bits (the upper 16 bits of x) and on whether the
-    low 16 bits are zero: the rounding position is at most 3 mantissa bits
-    down for normal codes and moves right by at most 4 more positions
-    through the subnormal codes, staying inside the upper 16 bits, so the low
-    16 bits only act as the sticky bit.  Every upper-16 pattern from 0 to
+    low 16 bits are zero: the rounding position lies after the third
+    mantissa bit for normal codes and moves toward the leading bit (by up to
+    four positions) through the subnormal codes, so it is always inside the
+    upper 16 bits and the low 16 bits only act as the sticky bit.  Every upper-16 pattern from 0 to
     448, both signs, is taken with low halves zero and nonzero (ties,
     just-above and just-below included), plus random values, 448, 464,
     +-1e30 and +-0."""

@@ -50,6 +50,12 @@ int check_shape(const vc_shape* s) {
         return fail(VC_ERR_INVALID, "shape too large");
     if ((int64_t)s->B * s->H * ((s->L + vc::ATTN_BM - 1) / vc::ATTN_BM) > 0x7FFFFFFF)
         return fail(VC_ERR_INVALID, "shape too large for one launch");
+    // The attention kernels address one head's K and V (codes, or bf16 rows)
+    // through buffer descriptors with 32-bit byte counts and offsets: keep
+    // 2 * Lp * d (the bf16 bytes of a padded head) below 2^31.
+    if (nb * 128 * s->d * 2 > 0x7FFFFFFF)
+        return fail(VC_ERR_INVALID, "L=%d too long for d=%d: one head's padded K/V must stay below 2^31 bytes in bf16 "
+                    "(L <= %lld)", s->L, s->d, (long long)(((int64_t)1 << 30) / s->d - 128));
     return VC_OK;
 }
 

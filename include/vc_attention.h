@@ -27,7 +27,10 @@
  *   - Inputs holding NaN or infinities give undefined results.
  *
  * Sizes: d is 64 or 128; L >= 1; blocks are 128 tokens; nb = ceil(L/128);
- * Lp = 128*nb (the length padded to whole blocks).
+ * Lp = 128*nb (the length padded to whole blocks).  The kernels address one
+ * head's K and V through 32-bit byte offsets, so 2*Lp*d must stay below 2^31
+ * (L <= 8,388,480 at d = 128, L <= 16,777,088 at d = 64); B*H <= 2^20 and
+ * B*H*Lp*d <= 2^40.  Larger shapes are rejected with -1.
  */
 #ifndef VC_ATTENTION_H
 #define VC_ATTENTION_H

@@ -256,3 +256,19 @@ def test_error_text_is_per_thread(lib):
         t.join(timeout=60)
     assert seen["failing"] != ""
     assert seen["clean"] == ""
+
+
+@pytest.mark.parametrize("L,d", [(8388480 + 1, 128), (16777088 + 1, 64), (2 ** 31 - 1, 128)])
+def test_head_beyond_32bit_offsets_rejected(lib, L, d):
+    # one head's padded K/V in bf16 (2 Lp d bytes) must stay below 2^31
+    with pytest.raises(_lib.VCError) as e:
+        _lib.vc_prepared_sizes(_lib.shape_of(1, 1, L, d))
+    assert e.value.code == _lib.VC_ERR_INVALID
+    assert "2^31" in str(e.value) or "too large" in str(e.value)
+
+
+@pytest.mark.parametrize("L,d", [(8388480, 128), (16777088, 64)])
+def test_longest_head_accepted(lib, L, d):
+    b = _lib.vc_prepared_sizes(_lib.shape_of(1, 1, L, d))
+    assert b[0] == ((L + 127) // 128) * 128 * d
+

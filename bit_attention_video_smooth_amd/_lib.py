@@ -22,7 +22,8 @@ VC_ERR_WORKSPACE = -3
 VC_ERR_HIP = -4
 
 EXPORTS = ["vc_version", "vc_last_error", "vc_prepared_sizes", "vsmooth_workspace_bytes",
-           "vsmooth_prepare", "vsmooth_prepare_warm", "vc_attention_fwd", "vc_attention_fwd_dump",
+           "vsmooth_prepare", "vsmooth_prepare_warm", "vsmooth_prepare_noalloc", "vc_attention_fwd",
+           "vc_attention_fwd_dump",
            "vc_attention_fwd_bf16", "vc_sage_prepared_sizes", "vc_sage_workspace_bytes",
            "vc_sage_prepare", "vc_sage_attention_fwd", "vc_sage_attention_fwd_dump",
            "vc_debug_expcast", "vc_debug_e4m3_encode", "vc_debug_mfma_fp8"]
@@ -94,6 +95,7 @@ def load():
         L.vsmooth_workspace_bytes.argtypes = [S, VP, ctypes.POINTER(sz)]
         L.vsmooth_prepare.argtypes = [S, VP, P, P, P, P, PR, P, sz, P]
         L.vsmooth_prepare_warm.argtypes = [S, VP, P, P, P, P, P, PR, P, sz, P]
+        L.vsmooth_prepare_noalloc.argtypes = [S, VP, P, P, P, P, PR, P]
         L.vc_attention_fwd.argtypes = [S, AP, PR, P, P]
         L.vc_attention_fwd_dump.argtypes = [S, AP, PR, P, i32, i32, P, P, P]
         L.vc_attention_fwd_bf16.argtypes = [S, P, P, P, P, i32, P]
@@ -167,6 +169,11 @@ def vsmooth_workspace_bytes(shape: vc_shape, params: vsmooth_params) -> int:
 def vsmooth_prepare(shape, params, q, k, v, perm_in, out: vc_prepared, ws, ws_bytes, stream=None):
     _check(load().vsmooth_prepare(ctypes.byref(shape), ctypes.byref(params), _ptr(q), _ptr(k), _ptr(v),
                                   _ptr(perm_in), ctypes.byref(out), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def vsmooth_prepare_noalloc(shape, params, q, k, v, perm_in, out: vc_prepared, stream=None):
+    _check(load().vsmooth_prepare_noalloc(ctypes.byref(shape), ctypes.byref(params), _ptr(q), _ptr(k), _ptr(v),
+                                          _ptr(perm_in), ctypes.byref(out), _stream(stream)))
 
 
 def vsmooth_prepare_warm(shape, params, q, k, v, centroids_in, centroids_out, out: vc_prepared, ws, ws_bytes,

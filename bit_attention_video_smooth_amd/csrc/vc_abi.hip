@@ -6,10 +6,19 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "vc_attention.h"
 #include "vc_internal.hpp"
+
+// Device memory for vsmooth_prepare_noalloc: the prepare workspace (k-means
+// centroids, assignment, sort counts, K column partials) lives here instead
+// of in a caller buffer.  Every GPU the library runs on holds its own copy
+// until the process ends.  In host code `scratch` names a host-side stand-in,
+// not the device array: its device address comes from hipGetSymbolAddress,
+// taken once per device (scratch_ptr below).
+static __device__ __align__(256) uint8_t scratch[VC_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -292,6 +301,32 @@ int prepare_common(const vc_shape* shape, const vsmooth_params* params, const vo
 }
 
 
+// Device address of `scratch` on the current device, looked up on the first
+// call per device (with that device current) and kept; nullptr on failure,
+// with the HIP error in *err.
+constexpr int MAX_DEVICES = 64;
+std::once_flag g_scratch_once[MAX_DEVICES];
+void* g_scratch_ptr[MAX_DEVICES];
+hipError_t g_scratch_err[MAX_DEVICES];
+
+void* scratch_ptr(int* dev_out, hipError_t* err) {
+    int dev = -1;
+    *err = hipGetDevice(&dev);
+    if (*err != hipSuccess) return nullptr;
+    *dev_out = dev;
+    if (dev < 0 || dev >= MAX_DEVICES) {
+        *err = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    std::call_once(g_scratch_once[dev], [dev] {
+        void* p = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+    });
+    *err = g_scratch_err[dev];
+    return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -330,6 +365,24 @@ int vsmooth_prepare(const vc_shape* shape, const vsmooth_params* params, const v
                     const void* v, const int32_t* perm_in, const vc_prepared* out, void* ws,
                     size_t ws_bytes, hipStream_t stream) {
     return prepare_common(shape, params, q, k, v, perm_in, nullptr, nullptr, out, ws, ws_bytes, stream);
+}
+
+int vsmooth_prepare_noalloc(const vc_shape* shape, const vsmooth_params* params, const void* q, const void* k,
+                            const void* v, const int32_t* perm_in, const vc_prepared* out, hipStream_t stream) {
+    int r, kk;
+    if ((r = check_shape(shape))) return r;
+    if ((r = check_params(shape, params, &kk))) return r;
+    const size_t need = prepare_ws(shape, perm_in == nullptr, kk);
+    if (need > VC_NOALLOC_SCRATCH_BYTES)
+        return fail(VC_ERR_WORKSPACE, "vsmooth_prepare_noalloc: this shape needs %zu bytes of workspace, more than the "
+                    "library's fixed %zu-byte scratch (use vsmooth_prepare with a caller workspace)", need,
+                    (size_t)VC_NOALLOC_SCRATCH_BYTES);
+    int dev = -1;
+    hipError_t e;
+    void* ws = scratch_ptr(&dev, &e);
+    if (ws == nullptr) return hip_status(e, "vsmooth_prepare_noalloc: scratch address");
+    return prepare_common(shape, params, q, k, v, perm_in, nullptr, nullptr, out, ws, VC_NOALLOC_SCRATCH_BYTES,
+                          stream);
 }
 
 int vsmooth_prepare_warm(const vc_shape* shape, const vsmooth_params* params, const void* q, const void* k,

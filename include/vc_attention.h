@@ -17,7 +17,8 @@
  *   - All tensors are device pointers to contiguous, row-major memory owned
  *     by the caller.  The library allocates nothing, frees nothing and keeps
  *     no state between calls; the workspace of vsmooth_prepare is caller
- *     memory too.
+ *     memory too.  (vsmooth_prepare_noalloc alone takes its workspace from
+ *     a fixed scratch array of the library, see there.)
  *   - Every pointer the kernels read or write must be 16-byte aligned.
  *   - Work is enqueued on `stream` and the call returns without waiting.
  *     Concurrent calls on different streams are independent.
@@ -148,6 +149,30 @@ int vsmooth_prepare_warm(const vc_shape* shape, const vsmooth_params* params, co
                          const void* k, const void* v, const float* centroids_in,
                          float* centroids_out, const vc_prepared* out, void* ws, size_t ws_bytes,
                          hipStream_t stream);
+
+/* Size of the fixed device scratch behind vsmooth_prepare_noalloc (64 MiB;
+ * enough for every shape up to B*H = 40 heads of L = 75,600 at d = 128 with
+ * k-means). */
+#define VC_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* vsmooth_prepare for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same steps, arguments and results, with the workspace taken from a
+ * fixed scratch array inside the library (VC_NOALLOC_SCRATCH_BYTES per
+ * device, held by every GPU the library runs on until the process ends)
+ * instead of a caller buffer.  The call itself allocates nothing.
+ * The scratch address of a device is looked up on the first call made with
+ * that device current; the current device must be the one that owns `stream`
+ * and the buffers.  Errors: -3 when vsmooth_workspace_bytes() for this shape
+ * and parameters exceeds VC_NOALLOC_SCRATCH_BYTES; -4 when the scratch
+ * address cannot be obtained; otherwise as vsmooth_prepare.
+ * All calls on one GPU share its scratch: calls that overlap in time on one
+ * GPU (on different streams, or from different threads without ordering)
+ * race and give undefined results.  The scratch keeps whatever the last call
+ * left; nothing in it needs to start at zero. */
+int vsmooth_prepare_noalloc(const vc_shape* shape, const vsmooth_params* params, const void* q,
+                            const void* k, const void* v, const int32_t* perm_in,
+                            const vc_prepared* out, hipStream_t stream);
 
 /* Attention parameters. */
 typedef struct vc_attn_params {

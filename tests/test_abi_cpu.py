@@ -272,3 +272,21 @@ def test_longest_head_accepted(lib, L, d):
     b = _lib.vc_prepared_sizes(_lib.shape_of(1, 1, L, d))
     assert b[0] == ((L + 127) // 128) * 128 * d
 
+
+def test_noalloc_rejects_shape_beyond_scratch(lib):
+    # the long workload (24 heads of L = 245,952) needs ~114 MiB of workspace
+    # with k-means, more than the fixed 64 MiB scratch; the check comes before
+    # any pointer is looked at or any device call is made
+    s = _lib.shape_of(1, 24, 245952, 128)
+    p = _lib.make_params()
+    need = _lib.vsmooth_workspace_bytes(s, p)
+    assert need > 64 << 20
+    with pytest.raises(_lib.VCError) as e:
+        _lib.vsmooth_prepare_noalloc(s, p, None, None, None, None, _lib.vc_prepared(), stream=0)
+    assert e.value.code == _lib.VC_ERR_WORKSPACE
+    assert "scratch" in str(e.value)
+
+
+def test_noalloc_fits_the_benchmark_workload(lib):
+    s = _lib.shape_of(1, 40, 75600, 128)
+    assert _lib.vsmooth_workspace_bytes(s, _lib.make_params()) <= 64 << 20

@@ -4,12 +4,18 @@ oracle then checks sampled heads (codes, scales, means bit-exact), sampled
 query tiles of the output (4 heads x 8 tiles for the method, always the
 first and the ragged last tile; 2 x 2 for the variants), and the k-means
 objective of one head."""
+import os
+import sys
+
 import numpy as np
 import pytest
 import torch
 
 import oracle
 from bit_attention_video_smooth_amd import synth
+
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+from parity_util import MAXABS, REL_L2, check_explained, explain_vsmooth_rows  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
@@ -30,14 +36,13 @@ def dev_bf16(u16):
 @pytest.mark.parametrize("cfg_idx", [1, 2, 3, 4])
 def test_full_size_sampled(api, cfg_idx):
     """Sampled heads bit-exact; sampled query tiles against the oracle.  The
-    output tolerance (rel-L2 <= 1e-3, max-abs <= 1e-2 max|O_ref|) is stated
-    for the output, and is applied to all sampled rows together; per-tile
-    figures are printed.  A tile's end-to-end error has a tail because the
-    FP8 matrix core does not round its 128-term score sums exactly (bounded
-    in test_fp8_matrix_core_sum_error_bound), so a byte next to a rounding
-    boundary can come out one code apart.  Given the kernel's own scores
-    (dumped for the first and last tile of the first and last head), every
-    byte is bit-exact and the output is within rel-L2 1e-4, max-abs 1e-3."""
+    output bar (rel-L2 <= 1e-3, max-abs <= 1e-2 max|O_ref|) is asserted on
+    all sampled rows together; per-tile figures are printed.  For the first
+    and last tile of the first and last head the kernel's scores and bytes
+    are dumped: bytes bit-exact given those scores, output within rel-L2
+    1e-4, max-abs 1e-3 of them, and the tile's end-to-end deviation beyond
+    that accounted for by one-code byte flips of the matrix core's inexact
+    score sums (parity_util)."""
     cfg = synth.CONFIGS[cfg_idx]
     B, H, L, d = cfg.B, cfg.H, cfg.L, cfg.d
     q, k, v = synth.make_inputs(cfg, cfg_idx)
@@ -70,21 +75,18 @@ def test_full_size_sampled(api, cfg_idx):
             gots.append(got)
             refs.append(ref)
             if bh in (heads[0], heads[-1]) and t in (tiles[0], tiles[-1]):
+                # bytes bit-exact given the kernel's scores, the given-S bar,
+                # and the tile's own end-to-end deviation accounted for
                 _, S, Pb = api.attention_dump(P, bh, t)
                 S, Pb = S.cpu().numpy()[:r1 - r0], Pb.cpu().numpy()[:r1 - r0]
-                gs, gby, _, _ = oracle.attention_head(o, L, 8, rows=(r0, r1), want_bytes=True,
-                                                      scores=np.ascontiguousarray(S))
-                assert np.array_equal(Pb, gby), "bytes given the kernel's scores"
-                rs = float(np.linalg.norm(got - gs) / np.linalg.norm(gs))
-                mas = float(np.abs(got - gs).max() / np.abs(gs).max())
-                print("   given the kernel's scores: bytes bit-exact, rel-L2 %.3g max-abs/max %.3g" % (rs, mas))
-                assert rs <= 1e-4 and mas <= 1e-3
+                ref2, refS, delta, flips = explain_vsmooth_rows(o, L, (r0, r1), S, Pb)
+                check_explained("   %s bh=%d tile %d" % (cfg.name, bh, t), got, ref2, refS, delta, flips)
     g, r = np.concatenate(gots), np.concatenate(refs)
     rel = float(np.linalg.norm(g - r) / np.linalg.norm(r))
     ma = float(np.abs(g - r).max() / np.abs(r).max())
     print("%s sampled rows (%d heads x %d tiles): rel-L2 %.3g max-abs/max %.3g; worst tile %.3g / %.3g"
           % (cfg.name, len(heads), len(tiles), rel, ma, worst[0], worst[1]))
-    assert rel <= 1e-3 and ma <= 1e-2
+    assert rel <= REL_L2 and ma <= MAXABS
     assert nb == P.q_scale.shape[-1]
 
 

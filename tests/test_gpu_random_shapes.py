@@ -3,9 +3,9 @@ drawn; L includes values next to block boundaries), through the C ABI.
 Per case: Q/K/V codes, scales and means bit-exact against the oracle, and,
 given the kernel's own scores, the output within the given-S bar (rel-L2
 1e-4, max-abs 1e-3 of max).  End to end, against the oracle's exactly
-rounded scores, the median over the cases is held to the output bar and the
-worst case to twice it (single cases have a tail from the matrix core's
-inexact 128-term score sums, as the seed sweep of the tiny workload shows)."""
+rounded scores, every case as in test_gpu_parity (the output bar, or the
+excess over it accounted for by one-code byte flips of the matrix core's
+inexact score sums), and the median over the cases within the output bar."""
 import os
 import sys
 
@@ -17,8 +17,8 @@ import oracle
 from bit_attention_video_smooth_amd import synth
 
 sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
-from test_gpu_parity import (GIVEN_S_MAXABS, GIVEN_S_REL, _end_to_end_bar, _kernel_scores,  # noqa: E402
-                             _oracle_out, dev_bf16, rel_l2)
+from parity_util import GIVEN_S_MAXABS, GIVEN_S_REL, REL_L2, rel_l2  # noqa: E402
+from test_gpu_parity import _explain, _kernel_scores, _oracle_out, dev_bf16  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
@@ -65,23 +65,19 @@ def test_random_shapes_match_oracle(api):
                 for n in ("q8", "k8", "v8", "q_scale", "k_scale", "v_scale", "v_mean"):
                     assert np.array_equal(g[n][b, h].view(np.uint8), o[n].view(np.uint8)), ((B, H, L, d), n)
         out = api.attention(P).cpu().numpy()
-        ref = _oracle_out(q, k, v, perm)
-        refS = _oracle_out(q, k, v, perm, scores=_kernel_scores(api, P))
-        rs, mas = rel_l2(out, refS), float(np.abs(out - refS).max() / np.abs(refS).max())
-        r = rel_l2(out, ref)
-        print("random shape %s: given kernel S rel-L2 %.3g max-abs/max %.3g | end-to-end rel-L2 %.3g"
-              % ((B, H, L, d), rs, mas, r))
-        assert rs <= GIVEN_S_REL and mas <= GIVEN_S_MAXABS, (B, H, L, d)
-        ends.append(r / _end_to_end_bar(d)[0])
+        r, _, _ = _explain("random shape", api, P, q, k, v, perm, out)
+        ends.append(r)
     ends = np.array(ends)
-    print("end-to-end error / bar over %d shapes: median %.3g max %.3g" % (len(ends), np.median(ends), ends.max()))
-    assert np.median(ends) <= 1.0 and ends.max() <= 2.0
+    print("end-to-end rel-L2 over %d shapes: median %.3g max %.3g" % (len(ends), np.median(ends), ends.max()))
+    assert np.median(ends) <= REL_L2
 
 
 @pytest.mark.parametrize("qk", ["int8", "fp8"])
 def test_random_shapes_sage_match_oracle(api, qk):
     """The SAGE-style baseline over the same shapes: codes and scales
-    bit-exact, given-S bar per case, end-to-end bar over the set."""
+    bit-exact; per case the given-S bar and the end-to-end check of
+    test_gpu_sage (INT8: the output bar itself); the median within the
+    output bar."""
     import test_gpu_sage as ts
     ends = []
     for B, H, L, d, seed in SHAPES[:6]:
@@ -95,16 +91,12 @@ def test_random_shapes_sage_match_oracle(api, qk):
                 for n in ("q8", "k8", "v8", "q_scale", "k_scale", "v_scale"):
                     assert np.array_equal(g[n][b, h].view(np.uint8), o[n].view(np.uint8)), ((B, H, L, d), qk, n)
         out = api.sage_attention(P).cpu().numpy()
-        ref = ts._oracle_out(q, k, v, qk)
-        refS = ts._oracle_out(q, k, v, qk, scores=ts._kernel_scores(api, P, 1))
-        rs, mas = rel_l2(out, refS), float(np.abs(out - refS).max() / np.abs(refS).max())
-        r = rel_l2(out, ref)
-        print("random shape sage %s %s: given kernel S rel-L2 %.3g max-abs/max %.3g | end-to-end rel-L2 %.3g"
-              % (qk, (B, H, L, d), rs, mas, r))
-        assert rs <= GIVEN_S_REL and mas <= GIVEN_S_MAXABS, (B, H, L, d)
-        ends.append(r / ts._end_to_end_bar(d)[0])
+        r, _, within = ts._explain("random shape sage %s" % qk, api, P, q, k, v, qk, out, 1)
+        if qk == "int8":
+            assert within
+        ends.append(r)
     ends = np.array(ends)
-    assert np.median(ends) <= 1.0 and ends.max() <= 2.0
+    assert np.median(ends) <= REL_L2
 
 
 def test_random_shapes_fp4_match_oracle(api):

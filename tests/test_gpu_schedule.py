@@ -2,13 +2,20 @@
 run k-means on that step's V, the other steps reuse the latest permutation
 (passed back into the library as perm_in = the layer's own perm buffer),
 and every step's output equals a direct prepare + attention with that
-permutation; one reuse step is checked against the oracle."""
+permutation; one reuse step is checked against the oracle (bytes given the
+kernel's scores, given-S bar, end to end as in test_gpu_parity)."""
+import os
+import sys
+
 import numpy as np
 import pytest
 import torch
 
 import oracle
 from bit_attention_video_smooth_amd import synth
+
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+from parity_util import check_explained, explain_vsmooth_rows  # noqa: E402
 from bit_attention_video_smooth_amd.schedule import GroupingSchedule, VCAttentionLayer
 
 pytestmark = pytest.mark.gpu
@@ -53,15 +60,17 @@ def test_session_regroups_on_schedule_and_reuses_permutation(api):
         ref = api.attention(ref_P)
         torch.cuda.synchronize()
         assert torch.equal(out, ref), step
-        if step == 5:  # a reuse step against the oracle
+        if step == 5:  # a reuse step against the oracle, every query tile
             pn = perm.cpu().numpy()
             for h in range(H):
                 o = oracle.prepare_head(q[0, h], k[0, h], vs[0, h], pn[0, h])
-                r = oracle.attention_head(o, L)
-                got = out[0, h].cpu().numpy()
-                rel = float(np.linalg.norm(got - r) / np.linalg.norm(r))
-                print("schedule step 5 head %d: rel-L2 %.3g" % (h, rel))
-                assert rel <= 2e-3
+                for qt in range((L + 255) // 256):
+                    r0, r1 = 256 * qt, min(L, 256 * qt + 256)
+                    _, S, Pb = api.attention_dump(layer.prepared, h, qt)
+                    ref, refS, delta, flips = explain_vsmooth_rows(o, L, (r0, r1), S.cpu().numpy()[:r1 - r0],
+                                                                   Pb.cpu().numpy()[:r1 - r0])
+                    check_explained("schedule step 5 head %d tile %d" % (h, qt), out[0, h, r0:r1].cpu().numpy(),
+                                    ref, refS, delta, flips)
     assert layer.grouped_at == 2
 
 

@@ -454,12 +454,16 @@ void vco_prepare_head(const uint16_t* q, const uint16_t* k, const uint16_t* v, i
 /* ExpCast has no 4-bit form).  Readings: Q and K as the 8-bit path (per-    */
 /* block FP8); the same exact block mean; the residual r = fp32(v - mean)   */
 /* quantised to E2M1 with one power-of-two scale per (block, channel, key   */
-/* group), the group of key kk in its block being (kk mod 16) div 4 -- the  */
-/* 32-key blocks along k of the matrix-core product that consumes it.       */
+/* group), the group of key kk in its block being kk div 32: 32 consecutive */
+/* slots of the permuted block (the pages do not define the groups; this is */
+/* the plain reading, and the slots of a block hold same-cluster tokens).   */
 /* Outputs as vco_prepare_head, except v4 [nb, d, 128] (one E2M1 code per    */
 /* byte, natural key order, 0 for padded keys) and v_exp [nb, d, 4] (e +     */
 /* 127 of each group's scale 2^e) in place of v8 / v_scale.                 */
 /* ------------------------------------------------------------------------ */
+
+/* the 4-bit key group of in-block slot j: 32 consecutive slots */
+static int vco_fp4_group(int j) { return j / 32; }
 
 void vco_prepare_head_fp4v(const uint16_t* q, const uint16_t* k, const uint16_t* v, int L, int d,
                            int smooth_k, const int32_t* perm, uint8_t* q8, uint8_t* k8, uint8_t* v4,
@@ -484,11 +488,11 @@ void vco_prepare_head_fp4v(const uint16_t* q, const uint16_t* k, const uint16_t*
             for (int g = 0; g < 4; g++) {
                 double A = 0.0;
                 for (int j = 0; j < n; j++)
-                    if ((j % 16) / 4 == g && fabs((double)r[j]) > A) A = fabs((double)r[j]);
+                    if (vco_fp4_group(j) == g && fabs((double)r[j]) > A) A = fabs((double)r[j]);
                 int e = vco_e8m0_exp(A);
                 v_exp[((int64_t)b * d + c) * 4 + g] = (uint8_t)(e + 127);
                 for (int j = 0; j < VCO_BLK; j++)
-                    if ((j % 16) / 4 == g)
+                    if (vco_fp4_group(j) == g)
                         v4[((int64_t)b * d + c) * VCO_BLK + j] =
                             (j < n && e > -127) ? vco_e2m1_encode(ldexp((double)r[j], -e)) : 0;
             }
@@ -543,7 +547,7 @@ float vco_c0(int d) { return (float)(1.4426950408889634074 / sqrt((double)d)); }
 /*   casting it to FP8).                                                    */
 /* mode 3 (4-bit P V, with vco_prepare_head_fp4v inputs): p_j as mode 2     */
 /*   before the cast, fp32(2^z_j); per key group G of the block (key j in   */
-/*   group (j mod 16) div 4), e_G = the E8M0 rule on max_{j in G} p_j and     */
+/*   group j div 32), e_G = the E8M0 rule on max_{j in G} p_j and           */
 /*   phat_j = 2^e_G E2M1(p_j / 2^e_G); l_b = sum phat_j; acc_c = fp32(sum_j  */
 /*   phat_j rhat_jc), rhat_jc = 2^(v_exp - 127) E2M1 code value; O = alpha O */
 /*   + acc + l_b mu_b (no separate V scale).  bytes_out holds the E2M1 codes */
@@ -646,10 +650,10 @@ void vco_attention_rows(int mode, int L, int d, int z_off,
                     for (int g = 0; g < 4; g++) {
                         double A = 0.0;
                         for (int j = 0; j < n; j++)
-                            if ((j % 16) / 4 == g && p4[j] > A) A = p4[j];
+                            if (vco_fp4_group(j) == g && p4[j] > A) A = p4[j];
                         int e = vco_e8m0_exp(A);
                         for (int j = 0; j < VCO_BLK; j++) {
-                            if ((j % 16) / 4 != g) continue;
+                            if (vco_fp4_group(j) != g) continue;
                             uint8_t code = (j < n && e > -127) ? vco_e2m1_encode(ldexp(p4[j], -e)) : 0;
                             double ph = vco_e2m1_decode(code) * ldexp(1.0, e);
                             int64_t o = (int64_t)(i - r0) * Lp + b * VCO_BLK + j;
@@ -688,7 +692,7 @@ void vco_attention_rows(int mode, int L, int d, int z_off,
                 for (int j = 0; j < n; j++) {
                     double rv;
                     if (mode == 3)
-                        rv = vco_e2m1_decode(v8[vr + j]) * ldexp(1.0, (int)v_exp[((int64_t)b * d + c) * 4 + (j % 16) / 4] - 127);
+                        rv = vco_e2m1_decode(v8[vr + j]) * ldexp(1.0, (int)v_exp[((int64_t)b * d + c) * 4 + vco_fp4_group(j)] - 127);
                     else
                         rv = (mode != 1) ? dec[v8[vr + j]] : rf[vr + j];
                     acc += p[j] * rv;

@@ -7,8 +7,11 @@ outside the oracle:
   * the encoder against NumPy's round-half-even at one mantissa bit (a
     different algorithm from the oracle's nearest-code search);
   * the E8M0 rule by its defining inequality;
-  * the residual codes within half a step, every interleaved key group
-    reaching the top codes (a contiguous grouping would not);
+  * the residual codes within half a step, every key group (32 consecutive
+    slots of the permuted block) reaching the top codes;
+  * a block whose first 32 slots are large and the rest small keeps the
+    small values at their own fine scale (an interleaved grouping, which
+    mixes slots of every quarter into each group, would zero them);
   * P codes against dequantised float64 scores with a running maximum;
   * a closed form: uniform attention on inputs built so that every
     quantisation is exact gives the plain mean of V, and the 8-bit
@@ -65,7 +68,36 @@ def test_e8m0_rule(oracle_mod):
 
 
 def _group(j):
-    return (j % 16) // 4
+    """Key group of in-block slot j: 32 consecutive slots (the plain reading;
+    the pages name 4-bit V-Smooth but not its groups)."""
+    return j // 32
+
+
+def test_fp4v_groups_are_contiguous_slots(oracle_mod):
+    """Residual values 4 in every channel of slots 0..31 of the block and
+    values in [0.1, 0.4] in slots 32..127: with groups of 32 consecutive
+    slots, groups 1..3 take the scale 2^-4 and keep every small value within
+    half an E2M1 step of it (the E8M0 rule puts 0.4 <= 6 * 2^-4); a grouping
+    that puts any of slots 0..31 into those groups gives them scale 2^0, at
+    which values below 0.25 encode to 0."""
+    L, d = 128, 64
+    rng = np.random.default_rng(7)
+    x = rng.uniform(0.1, 0.4, (48, d)) * rng.choice([-1.0, 1.0], (48, d))
+    small = np.concatenate([x, -x])                  # (x, -x) pairs: mean exactly 0
+    big = 4.0 * np.concatenate([np.ones((16, d)), -np.ones((16, d))])
+    res = np.concatenate([big, small])
+    v = _bf16(res)                                   # bf16 keeps the pairs exact negatives
+    q = _bf16(rng.standard_normal((L, d)))
+    k = _bf16(rng.standard_normal((L, d)))
+    perm = np.arange(L, dtype=np.int32)
+    P4 = oracle_mod.prepare_head_fp4v(q, k, v, perm)
+    e = P4["v_exp"][0].astype(int) - 127             # [d, 4]
+    assert np.all(e[:, 0] >= 0) and np.all(e[:, 1:] <= -3)
+    r = (oracle_mod.bf16_to_f32(v).astype(np.float32) - P4["v_mean"][0][None, :]).astype(np.float64)
+    yh = oracle_mod.e2m1_decode(P4["v4"][0]).T * (2.0 ** e[:, np.arange(128) // 32]).T  # [128, d]
+    tail = r[32:]
+    assert np.all(np.abs(yh[32:] - tail) <= 2.0 ** e[:, 1:].max() * 0.5 + 1e-12)
+    assert np.count_nonzero(yh[32:]) >= 0.95 * tail.size
 
 
 def test_fp4v_prepare(oracle_mod):
@@ -117,7 +149,7 @@ def test_fp4v_bytes_follow_dequantised_scores(oracle_mod):
     run = np.maximum.accumulate(z.reshape(L, nb, 128).max(axis=2), axis=1)
     p = np.exp2(z - np.repeat(run, 128, axis=1) + z_off)
     ref = np.zeros_like(p)
-    g = _group(np.arange(Lp))
+    g = _group(np.arange(Lp) % 128)
     for b in range(nb):
         for gg in range(4):
             cols = np.nonzero((np.arange(Lp) // 128 == b) & (g == gg))[0]
@@ -140,7 +172,8 @@ def _uniform_inputs(L, d, seed):
     """Identical Q rows and identical K rows (every score equal, so P is
     exact: 2^z_off at every key), and V = block constant mu_b plus a residual
     whose values are E2M1 values times 2^-4, in (x, -x) pairs inside each key
-    group (block means exactly mu_b) with every group reaching 6 * 2^-4."""
+    group of 32 consecutive slots (block means exactly mu_b) with every group
+    reaching 6 * 2^-4."""
     rng = np.random.default_rng(seed)
     q = np.tile(rng.standard_normal(d), (L, 1))
     k = np.tile(rng.standard_normal(d), (L, 1))
@@ -153,7 +186,7 @@ def _uniform_inputs(L, d, seed):
         for a in range(0, n, 32):                 # keys a .. a+31: two 16-key rows
             vals = rng.choice(MAGS, size=(16, d)) * rng.choice([-1.0, 1.0], size=(16, d))
             vals[0] = 6.0
-            res[a:a + 16] = vals                  # key a + t and a + 16 + t share the group (t % 16) // 4
+            res[a:a + 16] = vals                  # keys a + t and a + 16 + t share the group a // 32
             res[a + 16:a + 32] = -vals
         v[b0:b0 + n] = mu[None, :] + res * 2.0 ** -4
     return _bf16(q), _bf16(k), _bf16(v), v

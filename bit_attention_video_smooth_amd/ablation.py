@@ -89,7 +89,7 @@ def fp4_value_stats(P: api.Prepared, v: torch.Tensor) -> dict:
     codes, exps = api.v4_codes_natural(P)                   # [B,H,nb,d,128], [B,H,nb,d,4]
     table = torch.tensor([0, 0.5, 1, 1.5, 2, 3, 4, 6, -0.0, -0.5, -1, -1.5, -2, -3, -4, -6],
                          dtype=torch.float64, device=v.device)
-    group = (torch.arange(api.BLK, device=v.device) % 16) // 4  # key group of each in-block key
+    group = torch.arange(api.BLK, device=v.device) // 32      # key group of each in-block key
     err = np.empty((B, H))
     for b in range(B):
         for h in range(H):

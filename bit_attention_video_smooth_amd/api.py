@@ -267,13 +267,15 @@ def key_of_slot():
 
 def v4_codes_natural(prep: Prepared):
     """The E2M1 residual of a 4-bit prepare: (codes [B,H,nb,d,128] one code
-    per byte in natural key order, E8M0 bytes [B,H,nb,d,4])."""
+    per byte in natural key order, E8M0 bytes [B,H,nb,d,4]).  The 4-bit
+    layout keeps keys in slot order already (slot 2t in the low nibble of
+    byte t), so this only unpacks the nibbles."""
     B, H, L, d = prep.shape
     nb = nblocks(L)
     packed = prep.v8.reshape(-1)[:B * H * nb * d * BLK // 2].view(B, H, nb, d, BLK // 2)
-    slots = torch.stack([packed & 0xF, packed >> 4], dim=-1).reshape(B, H, nb, d, BLK)
+    codes = torch.stack([packed & 0xF, packed >> 4], dim=-1).reshape(B, H, nb, d, BLK)
     exps = prep.v_scale.view(torch.uint8).view(B, H, nb, d, 4)
-    return v_codes_natural(slots), exps
+    return codes, exps
 
 
 def v_codes_natural(v8):

@@ -206,6 +206,14 @@ struct Fp8Loader {
     v4si rk, rv, rks;
     const float *vs, *vm;
     uint32_t off_k, off_v, off_sv;
+    // 4-bit V-Smooth: K rows enter LDS reordered so that the S^T products
+    // give lane group g the keys 32 g .. 32 g + 31 of the block (one 32-key
+    // group, the k-block of the lane's scaled FP4 operand): LDS row
+    // 16 kt + 4 g + i holds key 32 g + 4 kt + i.  A 4 KiB K slice s holds
+    // LDS rows s R .. s R + R - 1 (R = 4096 / D), whose keys are those of
+    // slice 0's rows plus 8 s (D = 128) or 16 s (D = 64) -- 1024 s bytes
+    // either way -- so one in-block offset (slice 0) serves every slice.
+    uint32_t off_k4;
     int w, lane;
     __device__ __forceinline__ Fp8Loader(const AttnArgs& a, int bh, int w_, int lane_) : w(w_), lane(lane_) {
         const size_t Lp = (size_t)a.nb * BLK;
@@ -221,13 +229,24 @@ struct Fp8Loader {
             vm = a.v_mean + (size_t)bh * a.nb * D;
         }
         off_k = dma_offset(w, lane, D);
+        {
+            const int cpr = D / 16;                     // 16-byte chunks per K row
+            const int p = w * 64 + lane;
+            const int r = p / cpr, cp = p % cpr;        // LDS row (slice 0) and chunk position
+            const int key = 32 * ((r % 16) / 4) + 4 * (r / 16) + r % 4;
+            off_k4 = (uint32_t)(key * D + ((cp ^ chunk_swizzle(r, cpr)) << 4));
+        }
         off_v = dma_offset(w, lane, FP4V ? BLK / 2 : BLK);
         off_sv = (uint32_t)((lane % (2 * NC)) % NC) * 16;  // lanes past 2*NC repeat
     }
     __device__ __forceinline__ void issue(lds_u8* stage, int kb) const {
 #pragma unroll
-        for (int i = 0; i < T::LPT; i++)
-            lds_dma16(rk, stage + (i * 4 + w) * 1024, off_k, kb * T::K_TILE + i * 4096);
+        for (int i = 0; i < T::LPT; i++) {
+            if (FP4V)
+                lds_dma16(rk, stage + (i * 4 + w) * 1024, off_k4, kb * T::K_TILE + i * 1024);
+            else
+                lds_dma16(rk, stage + (i * 4 + w) * 1024, off_k, kb * T::K_TILE + i * 4096);
+        }
 #pragma unroll
         for (int i = 0; i < NVC; i++)
             lds_dma16(rv, stage + T::K_TILE + (i * 4 + w) * 1024, off_v,
@@ -274,6 +293,17 @@ struct Fp8Wave {
     // need more registers, rebuilds it per block instead of spilling.
     static constexpr bool ONES_RESIDENT = MODE != REC_SAGE_I8;
     v8i ones8;
+
+    // In-block key of score (kt, i) of this lane: 16 kt + 4 g + i, or for
+    // 4-bit V-Smooth (K rows reordered in LDS, see Fp8Loader) 32 g + 4 kt + i.
+    __device__ __forceinline__ int key_of(int kt, int i) const {
+        return FP4V ? 32 * g + 4 * kt + i : 16 * kt + 4 * g + i;
+    }
+    // with lim = nvalid - key_of(0, 0) (the block's valid keys past the
+    // lane's first), score (kt, i) belongs to a key that exists
+    __device__ __forceinline__ static bool key_ok(int kt, int i, int lim) {
+        return (FP4V ? 4 * kt + i : 16 * kt + i) < lim;
+    }
 
     __device__ __forceinline__ Fp8Wave(const AttnArgs& args, int bh_, int qtile, int w_, int lane_)
         : a(args), bh(bh_), w(w_), lane(lane_) {
@@ -379,7 +409,7 @@ struct Fp8Wave {
                         mk = -INFINITY;
 #pragma unroll
                         for (int i = 0; i < 4; i++)
-                            if (16 * kt + i < lim) mk = fmaxf(mk, S[qt][kt][i]);
+                            if (key_ok(kt, i, lim)) mk = fmaxf(mk, S[qt][kt][i]);
                     }
                     // a tile with no valid key keeps -inf (coefficients are >= 0,
                     // and a zero coefficient only occurs with zero scores)
@@ -414,11 +444,10 @@ struct Fp8Wave {
 #pragma unroll
             for (int qt = 0; qt < 2; qt++) {
                 mx[qt] = -INFINITY;
-                // key 16 kt + 4 g + i exists iff 16 kt + i < lim
 #pragma unroll
                 for (int kt = 0; kt < 8; kt++)
 #pragma unroll
-                    for (int i = 0; i < 4; i++) mx[qt] = fmaxf(mx[qt], (16 * kt + i < lim) ? S[qt][kt][i] : -INFINITY);
+                    for (int i = 0; i < 4; i++) mx[qt] = fmaxf(mx[qt], key_ok(kt, i, lim) ? S[qt][kt][i] : -INFINITY);
             }
         }
         if (FP4V) {
@@ -459,7 +488,7 @@ struct Fp8Wave {
 #pragma unroll
                     for (int i = 0; i < 4; i++) {
                         p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[qt][kt][i], SAGE ? cf[qt][kt] : c8, krow[qt]));
-                        if (MASKED && !(16 * kt + i < lim)) p[i] = 0.f;  // keys past L keep byte 0
+                        if (MASKED && !key_ok(kt, i, lim)) p[i] = 0.f;  // keys past L keep byte 0
                     }
                     const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
                     P[qt][kt] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], lo, true);
@@ -481,7 +510,7 @@ struct Fp8Wave {
                     uint32_t pk = 0;
 #pragma unroll
                     for (int i = 0; i < 4; i++)
-                        if (16 * kt + i < lim)  // keys past L keep byte 0
+                        if (key_ok(kt, i, lim))  // keys past L keep byte 0
                             pk = expcast_byte_into(S[qt][kt][i], SAGE ? cf[qt][kt] : c8, krow[qt], i, pk);
                     P[qt][kt] = pk;
                 }
@@ -493,7 +522,7 @@ struct Fp8Wave {
                     for (int kt = 0; kt < 8; kt++)
 #pragma unroll
                         for (int i = 0; i < 4; i++) {
-                            const size_t o = (size_t)rl * Lp + kb * BLK + 16 * kt + 4 * g + i;
+                            const size_t o = (size_t)rl * Lp + kb * BLK + key_of(kt, i);
                             a.s_dump[o] = S[qt][kt][i];
                             a.p_dump[o] = (P[qt][kt] >> (8 * i)) & 0xFF;
                         }
@@ -503,10 +532,11 @@ struct Fp8Wave {
     }
 
     // 4-bit probabilities: p = 2^z in fp32 (v_exp_f32), then one power-of-two
-    // scale for the lane's 32 values -- one 32-key group of the scaled FP4
-    // product, the keys (kk mod 16) div 4 = g of the block -- by the E8M0 rule
-    // on their maximum, and E2M1 codes (round to nearest even), element
-    // 4 kt + i of the lane in nibble (4 kt + i) mod 8 of dword kt / 2.
+    // scale for the lane's 32 values -- keys 32 g .. 32 g + 31 of the block,
+    // one 32-key group and the lane's k-block of the scaled FP4 product -- by
+    // the E8M0 rule on their maximum, and E2M1 codes (round to nearest even),
+    // element 4 kt + i (key 32 g + 4 kt + i) in nibble (4 kt + i) mod 8 of
+    // dword kt / 2.
     template <bool MASKED>
     __device__ __forceinline__ void softmax_bytes_fp4(int kb, float c, int lim) {
 #pragma unroll
@@ -517,7 +547,7 @@ struct Fp8Wave {
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
                     p[4 * kt + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[qt][kt][i], c, krow[qt]));
-                    if (MASKED && !(16 * kt + i < lim)) p[4 * kt + i] = 0.f;  // keys past L: code 0
+                    if (MASKED && !key_ok(kt, i, lim)) p[4 * kt + i] = 0.f;  // keys past L: code 0
                 }
             // the group's largest probability from its largest score: the FMA
             // is monotone in S for c >= 0, and so is 2^z; a group with no
@@ -540,7 +570,7 @@ struct Fp8Wave {
 #pragma unroll
                         for (int i = 0; i < 4; i++) {
                             const int e = 4 * kt + i;
-                            const size_t o = (size_t)rl * Lp + kb * BLK + 16 * kt + 4 * g + i;
+                            const size_t o = (size_t)rl * Lp + kb * BLK + key_of(kt, i);
                             a.s_dump[o] = S[qt][kt][i];
                             a.p_dump[o] = (P[qt][e / 8] >> (4 * (e % 8))) & 0xF;
                         }
@@ -579,11 +609,12 @@ struct Fp8Wave {
         }
         const int nvalid = L - kb * BLK;  // keys of this block that exist (>= 1)
         if (nvalid < BLK) {
-            softmax_max<true>(cb, nvalid - 4 * g);
+            const int lim = nvalid - key_of(0, 0);
+            softmax_max<true>(cb, lim);
             if (FP4V)
-                softmax_bytes_fp4<true>(kb, cscale, nvalid - 4 * g);
+                softmax_bytes_fp4<true>(kb, cscale, lim);
             else
-                softmax_bytes<true>(kb, cscale, nvalid - 4 * g);
+                softmax_bytes<true>(kb, cscale, lim);
         } else {
             softmax_max<false>(cb, 0);
             if (FP4V)

@@ -262,15 +262,16 @@ __global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict
 // ------------------------------------------------------------------------
 // 4-bit V-Smooth residual: the same exact block mean, then E2M1 codes with
 // one power-of-two (E8M0) scale per (channel, key group), the group of key kk
-// being (kk mod 16) div 4 -- slots 32 g .. 32 g + 31 of the P V slot order,
-// the 32-element k-blocks of the scaled matrix-core product.  Scale 2^e with
-// e the least integer such that amax <= 6 * 2^e (no element clips); amax <
-// 2^-100: codes 0.  Codes: v_cvt_scalef32_pk_fp4_f32 (round to nearest even
-// of x / 2^e, exact scaling).  Output: codes [bh][nb][D][64] bytes, slot 2 t
-// in the low nibble of byte t; scales [bh][nb][D][4] bytes e + 127.  The
-// loads, the mean and the wave/key layout are those of quant_v_kernel; each
-// wave holds 8 keys of every group (keys 4 g .. 4 g + 3 and 16 + 4 g ..
-// 16 + 4 g + 3 of its 32), so group maxima are combined over the waves in LDS.
+// being kk div 32 (32 consecutive slots of the permuted block; the attention
+// kernel's loader orders K so that these are the 32-element k-blocks of its
+// scaled matrix-core product).  Scale 2^e with e the least integer such that
+// amax <= 6 * 2^e (no element clips); amax < 2^-100: codes 0.  Codes:
+// v_cvt_scalef32_pk_fp4_f32 (round to nearest even of x / 2^e, exact
+// scaling).  Output: codes [bh][nb][D][64] bytes, key kk of the block in
+// slot kk, slot 2 t in the low nibble of byte t; scales [bh][nb][D][4] bytes
+// e + 127.  The loads, the mean and the wave/key layout are those of
+// quant_v_kernel: wave w holds keys 32 w .. 32 w + 31, i.e. group w, so each
+// group's maximum stays inside one wave.
 // ------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void quant_v4_kernel(const uint16_t* __restrict__ v,
@@ -283,7 +284,7 @@ __global__ __launch_bounds__(256) void quant_v4_kernel(const uint16_t* __restric
     constexpr int RB = BLK / 2;      // code bytes per channel row
     constexpr int PITCH = RB + 16;   // LDS row, padded against bank conflicts
     __shared__ double psum[4][D];
-    __shared__ float pmax[4][D][4];
+    __shared__ uint32_t pexp[D];  // E8M0 byte of group g (wave g) in byte g
     __shared__ __attribute__((aligned(16))) uint8_t tile[D * PITCH];
     const int b = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63;
@@ -324,36 +325,31 @@ __global__ __launch_bounds__(256) void quant_v4_kernel(const uint16_t* __restric
         mu[e] = (float)((((psum[0][c] + psum[1][c]) + psum[2][c]) + psum[3][c]) / (double)n);
 #pragma unroll
         for (int i = 0; i < KW; i++) x[i][e] = i < nw ? __fsub_rn(x[i][e], mu[e]) : 0.0f;  // residual
+        // the wave's 32 keys are the key group w: its scale from their amax,
+        // then the codes in slot order, slot 2t in the low nibble of byte t
+        float am = 0.0f;
 #pragma unroll
-        for (int g = 0; g < 4; g++) {
-            float am = 0.0f;
+        for (int i = 0; i < KW; i++) am = fmaxf(am, fabsf(x[i][e]));
+        const int ex = e8m0_exp(am);
+        uint8_t* out = tile + c * PITCH + 16 * w;
 #pragma unroll
-            for (int j = 0; j < 8; j++) am = fmaxf(am, fabsf(x[16 * (j / 4) + 4 * g + j % 4][e]));
-            pmax[w][c][g] = am;
-        }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < CPL; e++) {
-        const int c = CPL * lane + e;
-        const size_t gi = ((size_t)bh * nb + b) * D + c;
-        uint32_t ebytes = 0;
-        uint8_t* out = tile + c * PITCH;
-#pragma unroll
-        for (int g = 0; g < 4; g++) {
-            const float A = fmaxf(fmaxf(pmax[0][c][g], pmax[1][c][g]), fmaxf(pmax[2][c][g], pmax[3][c][g]));
-            const int ex = e8m0_exp(A);
-            ebytes |= (uint32_t)(ex + 127) << (8 * g);
-            // slots 32 g + 8 w + j hold keys 32 w + 16 (j / 4) + 4 g + j % 4
+        for (int j4 = 0; j4 < KW / 8; j4++) {
             float y[8];
 #pragma unroll
-            for (int j = 0; j < 8; j++) y[j] = x[16 * (j / 4) + 4 * g + j % 4][e];
+            for (int j = 0; j < 8; j++) y[j] = x[8 * j4 + j][e];
             const uint32_t pk = ex > -127 ? e2m1_pk8(y, ldexpf(1.0f, ex)) : 0u;  // zero group: codes 0
-            *reinterpret_cast<uint32_t*>(out + 16 * g + 4 * w) = pk;
+            *reinterpret_cast<uint32_t*>(out + 4 * j4) = pk;
         }
-        if (w == 0) {
+        reinterpret_cast<uint8_t*>(pexp + c)[w] = (uint8_t)(ex + 127);
+    }
+    __syncthreads();
+    if (w == 0) {
+#pragma unroll
+        for (int e = 0; e < CPL; e++) {
+            const int c = CPL * lane + e;
+            const size_t gi = ((size_t)bh * nb + b) * D + c;
             vmean[gi] = mu[e];
-            vexp[gi] = ebytes;
+            vexp[gi] = pexp[c];
         }
     }
     // the block's D x 64 code bytes are contiguous in HBM: 16 bytes per lane

@@ -81,12 +81,14 @@ typedef struct vsmooth_params {
     int32_t v_format;     /* residual format: 0 E4M3 (the 8-bit kernel); 1 E2M1
                              (4-bit V-Smooth, MarkTechPost abstract): one
                              power-of-two scale 2^e per (block, channel, key
-                             group), the group of key kk being (kk % 16) / 4,
-                             e the least integer with amax <= 6 * 2^e (amax <
-                             2^-100: codes 0); then v8 holds [B,H,nb,d,64]
-                             bytes (slot 2t in the low nibble of byte t, slots
-                             as below) and v_scale holds [B,H,nb,d,4] bytes
-                             e + 127 in place of fp32 scales */
+                             group), the group of in-block key kk being
+                             kk / 32 (32 consecutive slots), e the least
+                             integer with amax <= 6 * 2^e (amax < 2^-100:
+                             codes 0); then v8 holds [B,H,nb,d,64] bytes, key
+                             kk of the block in slot kk, slot 2t in the low
+                             nibble of byte t, and v_scale holds
+                             [B,H,nb,d,4] bytes e + 127 in place of fp32
+                             scales */
     uint64_t seed;        /* seeds the k-means initial centroids (SplitMix64) */
 } vsmooth_params;
 
@@ -95,7 +97,8 @@ typedef struct vsmooth_params {
  * c, v8[((bh*nb + b)*d + c)*128 + pos] holds the code of the key in slot
  * k = 128 b + kk of the permuted order, where
  *     pos = 32*((kk % 16) / 4) + 4*(kk / 16) + (kk % 4),
- * the order in which the PV matrix-core step consumes keys. */
+ * the order in which the PV matrix-core step consumes keys (E4M3 residual;
+ * the 4-bit layout of v_format 1 is described there). */
 typedef struct vc_prepared {
     uint8_t* q8;        /* [B,H,Lp,d] E4M3 codes of Q, original token order */
     uint8_t* k8;        /* [B,H,Lp,d] E4M3 codes of K - kbar, permuted order */

@@ -59,20 +59,26 @@ def _block_running_max(S, coef, L):
     return np.maximum.accumulate(t.reshape(n, nb, 128).max(axis=2), axis=1)
 
 
-def _weights(S, by, coef, L):
+def _weights(S, p, coef, L):
+    """w_j = p_j 2^(m_b(j) - m_final): p the decoded probability values
+    (relative to the running maximum of their block) [n, Lp]."""
     m = _block_running_max(S, coef, L).astype(np.float64)
     scale = np.exp2(m - m[:, -1:])                        # [n, nb]
-    return oracle.e4m3_decode(by).astype(np.float64) * np.repeat(scale, 128, axis=1)
+    return p.astype(np.float64) * np.repeat(scale, 128, axis=1)
 
 
-def flip_attribution(S_K, by_K, S_E, by_E, coef, vhat, L):
+def flip_attribution(S_K, by_K, S_E, by_E, coef, vhat, L, p_K=None, p_E=None):
     """Flip term of the end-to-end deviation for rows with kernel scores/bytes
     (S_K, by_K) and exact-score oracle scores/bytes (S_E, by_E), each
     [n, Lp]; coef [n, Lp] the fp32 score coefficient of every (row, key);
-    vhat [Lp, d] the dequantised values in key order (float64).  Returns
-    (delta [n, d], flips [n, Lp] int byte differences)."""
+    vhat [Lp, d] the dequantised values in key order (float64).  The
+    probability values are the E4M3 decodes of the bytes unless given
+    (p_K, p_E: 4-bit values with their group scales).  Returns (delta [n, d],
+    flips [n, Lp] int code differences)."""
     flips = by_K.astype(np.int32) - by_E.astype(np.int32)
-    wK, wE = _weights(S_K, by_K, coef, L), _weights(S_E, by_E, coef, L)
+    if p_K is None:
+        p_K, p_E = oracle.e4m3_decode(by_K), oracle.e4m3_decode(by_E)
+    wK, wE = _weights(S_K, p_K, coef, L), _weights(S_E, p_E, coef, L)
     lE, lK = wE.sum(axis=1), wK.sum(axis=1)
     OE = (wE @ vhat) / lE[:, None]
     dw = wK - wE
@@ -110,6 +116,38 @@ def sage_vhat(o):
     nb, d, _ = o["v8"].shape
     r = oracle.e4m3_decode(o["v8"]).astype(np.float64).transpose(0, 2, 1).reshape(nb * 128, d)
     return r * o["v_scale"][None, :].astype(np.float64)
+
+
+def fp4_vhat(o):
+    """Dequantised 4-bit values mean + 2^e E2M1(code) [Lp, d] in key order
+    (group of in-block key kk: kk div 32)."""
+    nb, d, _ = o["v4"].shape
+    e = o["v_exp"].astype(np.int64)[..., np.arange(128) // 32] - 127          # [nb, d, 128]
+    vh = o["v_mean"][:, :, None].astype(np.float64) + oracle.e2m1_decode(o["v4"]) * np.exp2(e)
+    return vh.transpose(0, 2, 1).reshape(nb * 128, d)
+
+
+def explain_fp4_rows(o, L, rows, S_K, codes_K):
+    """Oracle side of the end-to-end check for 4-bit V-Smooth rows of one head
+    (oracle.prepare_head_fp4v output `o`), given the kernel's dumped scores
+    and E2M1 probability codes [n, Lp]: the kernel's codes equal the
+    oracle's given the kernel's scores (one-code differences where
+    v_exp_f32's last bit straddles a rounding midpoint, rate below 1e-4).
+    The flip term uses the probability values with their group scales: a
+    score error can move a group's largest probability across a power of
+    two and so change the group's scale and all its codes at once, which
+    the values account for.  Returns (ref, refS, delta, flips); the flips
+    are left at zero (no one-code rule for 4-bit groups)."""
+    d = o["q8"].shape[1]
+    S_K = np.ascontiguousarray(S_K)
+    ref, c_E, S_E, p_E = oracle.attention_head_fp4v(o, L, rows=rows, want_bytes=True)
+    refS, c_S, _, p_S = oracle.attention_head_fp4v(o, L, rows=rows, want_bytes=True, scores=S_K)
+    dd = c_S.astype(np.int32) - codes_K.astype(np.int32)
+    assert (dd != 0).mean() <= 1e-4, "codes given the kernel's scores"
+    n_changed = int((c_S != c_E).sum())
+    delta, _ = flip_attribution(S_K, c_S, S_E, c_E, vsmooth_coef(o, rows, d), fp4_vhat(o), L, p_K=p_S, p_E=p_E)
+    print("   4-bit: %d probability codes differ from the exact-score ones" % n_changed)
+    return ref, refS, delta, np.zeros(c_S.shape, np.int32)
 
 
 def check_explained(tag, got, ref, refS, delta, flips):

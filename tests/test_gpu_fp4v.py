@@ -7,10 +7,14 @@ the kernel's own scores, the dumped E2M1 probability codes equal the
 oracle's (one-code differences allowed at a rate below 1e-4, where
 v_exp_f32's last-bit error could straddle a rounding midpoint) and the output
 is within rel-L2 1e-4, max-abs 1e-3 of max; end to end, against the oracle's
-exactly rounded scores, within twice the 8-bit output bar: one E2M1 step
-moves a probability about five times further than one E4M3 step, at a
-fourfold lower rate of score errors crossing a rounding boundary, so the
-per-row error is burstier."""
+exactly rounded scores, the deviation beyond that accounted for by the
+probability values the matrix core's inexact score sums change (codes one
+step apart, or a group's power-of-two scale moved when its largest
+probability crosses a power of two; parity_util.explain_fp4_rows).  The key
+group of in-block key kk is kk div 32."""
+import os
+import sys
+
 import numpy as np
 import pytest
 import torch
@@ -18,9 +22,10 @@ import torch
 import oracle
 from bit_attention_video_smooth_amd import synth
 
-pytestmark = pytest.mark.gpu
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+from parity_util import check_explained, explain_fp4_rows  # noqa: E402
 
-GIVEN_S_REL, GIVEN_S_MAXABS = 1e-4, 1e-3
+pytestmark = pytest.mark.gpu
 
 SHAPES = [(1, 2, 1024, 64, (4, 16, 16)), (1, 3, 300, 128, None), (2, 2, 129, 64, None),
           (1, 1, 1, 128, None), (1, 2, 4000, 128, None), (1, 1, 520, 64, None),
@@ -46,10 +51,6 @@ def rel_l2(a, b):
 
 def _inputs(B, H, L, d, seed, grid=None):
     return synth.make_inputs(synth.custom(B, H, L, d, grid=grid), seed)
-
-
-def _end_to_end_bar(d):
-    return (2e-3, 2e-2) if d == 128 else (4e-3, 4e-2)
 
 
 @pytest.mark.parametrize("shape", SHAPES)
@@ -92,10 +93,14 @@ def test_fp4v_attention_matches_oracle(api, shape):
     perm = synth.random_perms(B, H, L, 19)
     P = api.prepare(dev_bf16(q), dev_bf16(k), dev_bf16(v), perm_in=torch.from_numpy(perm).cuda(), v_format=1)
     out = api.attention(P).cpu().numpy()
+    _explain_fp4("fp4 P V", api, P, q, k, v, perm, out)
+
+
+def _explain_fp4(tag, api, P, q, k, v, perm, out):
+    """Whole-output end-to-end check of the 4-bit path, every query tile."""
+    B, H, L, d = q.shape
     nqt = (L + 255) // 256
-    Lp = ((L + 127) // 128) * 128
-    S = np.zeros((B, H, nqt * 256, Lp), np.float32)
-    worst = 0.0
+    refs, refSs, deltas, flips = [], [], [], []
     for bh in range(B * H):
         b, h = divmod(bh, H)
         o = oracle.prepare_head_fp4v(q[b, h], k[b, h], v[b, h], perm[b, h])
@@ -103,22 +108,16 @@ def test_fp4v_attention_matches_oracle(api, shape):
             od, s, pb = api.attention_dump(P, bh, qt)
             if qt == 0 and bh == 0:  # the dumping instance computes what the plain one does
                 assert torch.equal(od, api.attention(P))
-            S[b, h, qt * 256:(qt + 1) * 256] = s.cpu().numpy()
             r0, r1 = qt * 256, min(L, qt * 256 + 256)
-            _, gby, _, _ = oracle.attention_head_fp4v(o, L, rows=(r0, r1), want_bytes=True,
-                                                      scores=np.ascontiguousarray(S[b, h, r0:r1]))
-            diff = pb.cpu().numpy()[:r1 - r0].astype(int) - gby.astype(int)
-            worst = max(worst, float((diff != 0).mean()))
-    ref = _oracle_out(q, k, v, perm)
-    refS = _oracle_out(q, k, v, perm, scores=S[:, :, :L])
-    r, ma = rel_l2(out, ref), float(np.abs(out - ref).max() / np.abs(ref).max())
-    rs, mas = rel_l2(out, refS), float(np.abs(out - refS).max() / np.abs(refS).max())
-    print("fp4 P V %s: code mismatch given S %.2e | end-to-end rel-L2 %.3g max-abs/max %.3g | given kernel S "
-          "rel-L2 %.3g max-abs/max %.3g" % ((B, H, L, d), worst, r, ma, rs, mas))
-    assert worst <= 1e-4
-    assert rs <= GIVEN_S_REL and mas <= GIVEN_S_MAXABS
-    br, bm = _end_to_end_bar(d)
-    assert r <= br and ma <= bm
+            ref, refS, delta, fl = explain_fp4_rows(o, L, (r0, r1), s.cpu().numpy()[:r1 - r0],
+                                                    pb.cpu().numpy()[:r1 - r0])
+            refs.append(ref)
+            refSs.append(refS)
+            deltas.append(delta)
+            flips.append(fl)
+    got = out.reshape(B * H, L, d)
+    return check_explained("%s %s" % (tag, (B, H, L, d)), got.reshape(-1, d), np.concatenate(refs),
+                           np.concatenate(refSs), np.concatenate(deltas), np.concatenate(flips))
 
 
 def test_fp4v_bf16_output(api):
@@ -161,7 +160,7 @@ def test_fp4_value_stats_match_oracle(api):
         for h in range(H):
             o = oracle.prepare_head_fp4v(q[b, h], k[b, h], v[b, h], perm[b, h])
             x = oracle.bf16_to_f32(v[b, h]).astype(np.float64)[perm[b, h]]
-            sc = 2.0 ** (o["v_exp"].astype(np.int64)[..., (j % 16) // 4] - 127)          # [nb,d,128]
+            sc = 2.0 ** (o["v_exp"].astype(np.int64)[..., j // 32] - 127)                # [nb,d,128]
             xh = o["v_mean"].astype(np.float64)[:, :, None] + oracle.e2m1_decode(o["v4"]) * sc
             xh = xh.transpose(0, 2, 1).reshape(-1, d)[:L]
             ref = np.sqrt(((xh - x) ** 2).sum() / (x * x).sum())

@@ -88,3 +88,23 @@ def test_skip_softmax_decision_flips_accounted(oracle_mod):
     assert np.abs(flips).max() <= 1        # and only those were exempted
     change = outK.astype(np.float64) - ref.astype(np.float64)
     assert np.linalg.norm(change - delta) / np.linalg.norm(ref) <= 2e-6
+
+
+@pytest.mark.parametrize("L,d,seed", [(700, 64, 8), (1000, 128, 9)])
+def test_fp4_flip_term_equals_oracle_change(oracle_mod, L, d, seed):
+    """The 4-bit form (probability values with their group scales): perturbed
+    scores change codes and some group scales; the flip term still equals
+    the oracle's own change of output."""
+    from parity_util import explain_fp4_rows
+    cfg = synth.custom(1, 1, L, d)
+    q, k, v = synth.make_inputs(cfg, seed)
+    perm = synth.random_perms(1, 1, L, seed)
+    o = oracle.prepare_head_fp4v(q[0, 0], k[0, 0], v[0, 0], perm[0, 0])
+    S_E = oracle.attention_head_fp4v(o, L, want_bytes=True)[2]
+    rng = np.random.default_rng(seed)
+    S_K = (S_E.astype(np.float64) * (1 + 2.0 ** -11 * rng.standard_normal(S_E.shape))).astype(np.float32)
+    outK, c_K, _, _ = oracle.attention_head_fp4v(o, L, want_bytes=True, scores=S_K)
+    ref, refS, delta, _ = explain_fp4_rows(o, L, (0, L), S_K, c_K)
+    change = outK.astype(np.float64) - ref.astype(np.float64)
+    assert np.linalg.norm(change) / np.linalg.norm(ref) > 1e-4
+    assert np.linalg.norm(change - delta) / np.linalg.norm(ref) <= 2e-6

@@ -13,7 +13,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libvcattn.so")
-SOURCES = ["vc_abi.hip", "vc_prepare.hip", "vc_sage_prepare.hip", "vc_kmeans.hip", "vc_attn_fp8.hip",
+SOURCES = ["vc_abi.hip", "vc_host.hip", "vc_prepare.hip", "vc_sage_prepare.hip", "vc_kmeans.hip", "vc_attn_fp8.hip",
            "vc_attn_sage.hip", "vc_attn_fp4.hip", "vc_attn_bf16.hip", "vc_debug.hip"]
 ARCH = os.environ.get("VC_OFFLOAD_ARCH", "gfx950")
 

@@ -57,7 +57,7 @@ int check_shape(const vc_shape* s) {
     const int64_t elems = (int64_t)s->B * s->H * nb * 128 * s->d;
     if ((int64_t)s->B * s->H > (1 << 20) || elems > ((int64_t)1 << 40))
         return fail(VC_ERR_INVALID, "shape too large");
-    if ((int64_t)s->B * s->H * ((s->L + vc::ATTN_BM - 1) / vc::ATTN_BM) > 0x7FFFFFFF)
+    if ((int64_t)s->B * s->H * (((int64_t)s->L + vc::ATTN_BM - 1) / vc::ATTN_BM) > 0x7FFFFFFF)
         return fail(VC_ERR_INVALID, "shape too large for one launch");
     // The attention kernels address one head's K and V (codes, or bf16 rows)
     // through buffer descriptors with 32-bit byte counts and offsets: keep

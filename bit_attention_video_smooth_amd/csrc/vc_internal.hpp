@@ -78,7 +78,10 @@ struct AttnBf16Args {
     float C0;
 };
 
-int k_mean_splits(int BH, int L);
+// Host-side sizes and workspace layout (vc_host.hip, no device code).
+constexpr int KMEANS_KT = 64;       // centroids per LDS tile of the k-means assign kernel
+constexpr int KMEANS_CHUNK = 1024;  // tokens per chunk of the k-means counting sort
+int k_mean_splits(int BH, int L);   // partial sums per head of the K column mean
 size_t kmeans_workspace_bytes(int B, int H, int L, int d, int k);
 void kmeans_carve(KmeansArgs& a, void* ws);
 

@@ -28,8 +28,8 @@ namespace vc {
 
 namespace {
 
-constexpr int KT = 64;       // centroids per LDS tile of the assign kernel
-constexpr int CHUNK = 1024;  // tokens per chunk of the counting sort
+constexpr int KT = KMEANS_KT;        // centroids per LDS tile of the assign kernel
+constexpr int CHUNK = KMEANS_CHUNK;  // tokens per chunk of the counting sort
 constexpr int ANTT = 8;      // 16-token tiles per wave of the assign kernel
 constexpr int ATOK = 8 * 16 * ANTT;  // tokens per assign workgroup (8 waves)
 
@@ -486,40 +486,7 @@ hipError_t launch_kmeans_t(const KmeansArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
-size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
 }  // namespace
-
-size_t kmeans_workspace_bytes(int B, int H, int L, int d, int k) {
-    const size_t BH = (size_t)B * H;
-    const size_t kpad = ((size_t)k + KT - 1) / KT * KT;
-    const size_t nchunk = ((size_t)L + CHUNK - 1) / CHUNK;
-    size_t s = 0;
-    s += align256(BH * kpad * d * 4);       // cent
-    s += 2 * align256(BH * kpad * d * 2);   // bf16 high and low parts
-    s += align256(BH * kpad * 4);           // cnorm
-    s += align256(BH * L * 4);              // assign
-    s += 2 * align256(BH * k * 4);          // counts, offsets
-    s += align256(BH * nchunk * k * 4);     // chunk counts
-    s += align256(BH * nchunk * 8);         // objective partials
-    return s;
-}
-
-void kmeans_carve(KmeansArgs& a, void* ws) {
-    const size_t BH = (size_t)a.B * a.H;
-    a.kpad = (a.k + KT - 1) / KT * KT;
-    a.nchunk = (a.L + CHUNK - 1) / CHUNK;
-    uint8_t* p = static_cast<uint8_t*>(ws);
-    a.cent = reinterpret_cast<float*>(p);          p += align256(BH * a.kpad * a.d * 4);
-    a.cent_hi = reinterpret_cast<uint16_t*>(p);    p += align256(BH * a.kpad * a.d * 2);
-    a.cent_lo = reinterpret_cast<uint16_t*>(p);    p += align256(BH * a.kpad * a.d * 2);
-    a.cnorm = reinterpret_cast<float*>(p);         p += align256(BH * a.kpad * 4);
-    a.assign = reinterpret_cast<int32_t*>(p);      p += align256(BH * a.L * 4);
-    a.counts = reinterpret_cast<int32_t*>(p);      p += align256(BH * a.k * 4);
-    a.offsets = reinterpret_cast<int32_t*>(p);     p += align256(BH * a.k * 4);
-    a.chunk_cnt = reinterpret_cast<int32_t*>(p);   p += align256(BH * a.nchunk * a.k * 4);
-    a.obj_part = reinterpret_cast<double*>(p);
-}
 
 hipError_t launch_kmeans(const KmeansArgs& a, hipStream_t st) {
     return a.d == 128 ? launch_kmeans_t<128>(a, st) : launch_kmeans_t<64>(a, st);

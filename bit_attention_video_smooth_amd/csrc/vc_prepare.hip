@@ -382,13 +382,6 @@ hipError_t launch_copy_perm(const int32_t* src, int32_t* dst, size_t n, double* 
 // ------------------------------------------------------------------------
 // Launchers.
 // ------------------------------------------------------------------------
-int k_mean_splits(int BH, int L) {
-    int by_len = (L + 1023) / 1024;
-    int want = (2048 + BH - 1) / BH;
-    int s = by_len < want ? by_len : want;
-    return s < 1 ? 1 : s;
-}
-
 template <int D>
 static void launch_k_mean_t(const void* k, double* kpartial, float* kbar, int BH, int L, int smooth,
                             hipStream_t st) {

@@ -468,10 +468,10 @@ def test_given_scores_path_reproduces_exact_path(oracle_mod):
 
 
 # ---------------------------------------------------- Skip Softmax (BLASST) --
-# [TRT] "Sparse Attention with Skip Softmax": for query row i and KV block j
-# the block is negligible when exp(m~ - m) < lambda (m~ the block's maximum
-# score, m the running maximum); rejected blocks skip the exponentials and
-# their PV accumulation.
+# [TRT] "Sparse Attention with Skip Softmax": query row i drops KV block j
+# when exp(m~ - m) falls below the threshold lambda, with m~ the largest score
+# of the block and m the running maximum; a dropped block contributes no
+# exponentials and no PV product.
 
 def _skip_brute(qf, kf_perm, v_perm, lam):
     """fp64 softmax attention over the kept blocks only, with the rejection

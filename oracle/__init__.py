@@ -309,12 +309,12 @@ def attention_head(prep: dict, L: int, z_off: int = 8, rows=None, want_bytes=Fal
     return (out, by, S, y) if want_bytes else out
 
 
-def attention_exact_blockwise(qf, kf_perm, v_perm, v_mean, skip_lambda: float = 0.0):
+def attention_exact_blockwise(qf, kf_perm, v_perm, v_mean, skip_lambda: float = 0.0, rows=None):
     """Mode 1 of the blockwise loop: no quantisation, exact exp2, in double.
     qf [L,d], kf_perm [L,d] keys in permuted order, v_perm [L,d] values in
     permuted order, v_mean [nb,d] any per-block vector (the algebra must hold
-    for any mean).  skip_lambda as in attention_head.  Returns O [L,d]
-    (fp32)."""
+    for any mean).  skip_lambda as in attention_head.  rows: (r0, r1) or None
+    for all.  Returns O [r1-r0,d] (fp32)."""
     qf = _c(qf, np.float64)
     L, d = qf.shape
     nb = nblocks(L)
@@ -328,9 +328,10 @@ def attention_exact_blockwise(qf, kf_perm, v_perm, v_mean, skip_lambda: float = 
     for b in range(nb):
         n = min(BLK, L - b * BLK)
         rf[b, :, :n] = (vp[b * BLK:b * BLK + n] - vm[b].astype(np.float64)).T
-    out = np.empty((L, d), np.float32)
+    r0, r1 = (0, L) if rows is None else rows
+    out = np.empty((r1 - r0, d), np.float32)
     lib().vco_attention_rows(1, L, d, 8, None, None, None, None, None, None, _p(vm),
-                             _p(qf), _p(kf), _p(rf), 0, L, _p(out), None, None, None, None,
+                             _p(qf), _p(kf), _p(rf), r0, r1, _p(out), None, None, None, None,
                              skip_threshold(skip_lambda), None)
     return out
 
@@ -342,6 +343,67 @@ def attention_exact_blockwise(qf, kf_perm, v_perm, v_mean, skip_lambda: float = 
 # --------------------------------------------------------------------------
 
 SAGE_QK = {"int8": 1, "fp8": 0}
+
+
+def attention_p_only(qf, kf_perm, v_perm, v_mean, z_off: int = 8, rows=None):
+    """Mode 4 of the blockwise loop: real-valued scores (double sums rounded
+    once to fp32, scale 1) and values, with only the probabilities
+    quantised, by ExpCast-FP8 against the running maximum as in the method.
+    Arguments as attention_exact_blockwise.  Returns O [L,d] (fp32)."""
+    qf = _c(qf, np.float64)
+    L, d = qf.shape
+    nb = nblocks(L)
+    Lp = nb * BLK
+    kf = np.zeros((Lp, d), np.float64)
+    kf[:L] = kf_perm
+    vp = np.zeros((Lp, d), np.float64)
+    vp[:L] = v_perm
+    vm = _c(v_mean, np.float32)
+    rf = np.zeros((nb, d, BLK), np.float64)
+    for b in range(nb):
+        n = min(BLK, L - b * BLK)
+        rf[b, :, :n] = (vp[b * BLK:b * BLK + n] - vm[b].astype(np.float64)).T
+    r0, r1 = (0, L) if rows is None else rows
+    out = np.empty((r1 - r0, d), np.float32)
+    lib().vco_attention_rows(4, L, d, z_off, None, None, None, None, None, None, _p(vm),
+                             _p(qf), _p(kf), _p(rf), r0, r1, _p(out), None, None, None, None,
+                             np.float32(-np.inf), None)
+    return out
+
+
+def attention_parts(q, k, v, perm, z_off: int = 8, smooth_k: int = 1, rows=None):
+    """The method's output for one head with each quantised quantity switched
+    on alone, for the error decomposition of the value term ([MTP] abstract:
+    after QK smoothing, the value term carries most of the output error).
+    q, k, v: bf16 bits [L,d]; perm [L]; rows (r0, r1) or None for all.
+    Returns a dict of O [r1-r0,d] fp32:
+      exact -- no quantisation (softmax(Q K^T / sqrt(d)) V, blockwise in
+               double, mode 1);
+      qk    -- Q and K replaced by their dequantised per-block FP8 codes
+               (K after its mean is subtracted), probabilities and values
+               exact;
+      p     -- scores and values exact, probabilities ExpCast-FP8 (mode 4);
+      v     -- scores and probabilities exact, V replaced by its V-Smooth
+               reconstruction mean + s_v E4M3(code) in the permuted order;
+      all   -- the method (mode 0)."""
+    o = prepare_head(q, k, v, perm, smooth_k)
+    perm = _c(perm, np.int64)
+    L, d = _c(q, np.uint16).shape
+    nb = nblocks(L)
+    qf = bf16_to_f32(q).astype(np.float64)
+    kp = bf16_to_f32(k).astype(np.float64)[perm]
+    vp = bf16_to_f32(v).astype(np.float64)[perm]
+    qb = np.minimum(np.arange(L) // BLK, nb - 1)
+    qd = e4m3_decode(o["q8"][:L]) * o["q_scale"][qb][:, None].astype(np.float64)
+    kd = e4m3_decode(o["k8"][:L]) * o["k_scale"][qb][:, None].astype(np.float64)
+    r = e4m3_decode(o["v8"]) * o["v_scale"][:, :, None].astype(np.float64)          # [nb, d, 128]
+    vd = (o["v_mean"][:, :, None].astype(np.float64) + r).transpose(0, 2, 1).reshape(nb * BLK, d)[:L]
+    mu = o["v_mean"]
+    return {"exact": attention_exact_blockwise(qf, kp, vp, mu, rows=rows),
+            "qk": attention_exact_blockwise(qd, kd, vp, mu, rows=rows),
+            "p": attention_p_only(qf, kp, vp, mu, z_off, rows=rows),
+            "v": attention_exact_blockwise(qf, kp, vd, mu, rows=rows),
+            "all": attention_head(o, L, z_off, rows=rows)}
 
 
 def sage_prepare_head(q, k, v, qk_dtype: str = "int8", smooth_k: int = 1):

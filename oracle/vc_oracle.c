@@ -552,6 +552,10 @@ float vco_c0(int d) { return (float)(1.4426950408889634074 / sqrt((double)d)); }
 /*   phat_j rhat_jc), rhat_jc = 2^(v_exp - 127) E2M1 code value; O = alpha O */
 /*   + acc + l_b mu_b (no separate V scale).  bytes_out holds the E2M1 codes */
 /*   and y_out the values phat.                                             */
+/* mode 4 (probabilities alone quantised, for the error decomposition):     */
+/*   qf, kf, rf real as in mode 1, S the double sum rounded once to fp32,   */
+/*   c_b = C0 (scales 1), ExpCast bytes and the running maximum as mode 0;  */
+/*   values exact as in mode 1.                                             */
 /* mode 1 (exact algebra, for checking the blockwise bookkeeping):          */
 /*   qhat, khat, rhat are the real values (scales 1), S is a double sum,      */
 /*   p_j = 2^(S_j C0 - m') in double; the rest as in mode 0.  With mode 1 the */
@@ -600,8 +604,9 @@ void vco_attention_rows(int mode, int L, int d, int z_off,
         double* Sd = (double*)malloc(sizeof(double) * VCO_BLK);
         float* S = (float*)malloc(sizeof(float) * VCO_BLK);
         double* p = (double*)malloc(sizeof(double) * VCO_BLK);
+        const int real_qk = (mode == 1 || mode == 4); /* real-valued q, k and residual */
         for (int c = 0; c < d; c++)
-            qrow[c] = (mode != 1) ? dec[q8[(int64_t)i * d + c]] : qf[(int64_t)i * d + c];
+            qrow[c] = real_qk ? qf[(int64_t)i * d + c] : dec[q8[(int64_t)i * d + c]];
         double* p4 = (double*)malloc(sizeof(double) * VCO_BLK);
         double m = -INFINITY, l = 0.0;
         for (int b = 0; b < nb; b++) {
@@ -609,7 +614,7 @@ void vco_attention_rows(int mode, int L, int d, int z_off,
             double m_new, ell = 0.0;
             /* scores */
             for (int j = 0; j < n; j++) {
-                if (mode != 1 && S_in) {
+                if (!real_qk && S_in) {
                     S[j] = S_in[(int64_t)(i - r0) * Lp + b * VCO_BLK + j];
                     Sd[j] = S[j];
                     continue;
@@ -617,12 +622,12 @@ void vco_attention_rows(int mode, int L, int d, int z_off,
                 int64_t kr = (int64_t)(b * VCO_BLK + j) * d;
                 double acc = 0.0;
                 for (int c = 0; c < d; c++)
-                    acc += qrow[c] * ((mode != 1) ? dec[k8[kr + c]] : kf[kr + c]);
+                    acc += qrow[c] * (real_qk ? kf[kr + c] : dec[k8[kr + c]]);
                 Sd[j] = acc;
                 S[j] = (float)acc;
             }
-            if (mode == 0 || mode == 2 || mode == 3) {
-                volatile float sqk = q_scale[i / VCO_BLK] * k_scale[b];
+            if (mode == 0 || mode == 2 || mode == 3 || mode == 4) {
+                volatile float sqk = (mode == 4) ? 1.0f : q_scale[i / VCO_BLK] * k_scale[b];
                 volatile float cb = sqk * C0;
                 float mx = -INFINITY;
                 for (int j = 0; j < n; j++) if (S[j] > mx) mx = S[j];
@@ -668,13 +673,13 @@ void vco_attention_rows(int mode, int L, int d, int z_off,
                 for (int j = 0; j < VCO_BLK && mode != 3; j++) {
                     uint8_t by = 0;
                     if (j < n)
-                        by = (mode == 0) ? vco_expcast1(S[j], c8, krow)
-                                         : vco_e4m3_encode((float)exp2((double)fmaf(S[j], cb, zrow)));
+                        by = (mode == 0 || mode == 4) ? vco_expcast1(S[j], c8, krow)
+                                                      : vco_e4m3_encode((float)exp2((double)fmaf(S[j], cb, zrow)));
                     if (bytes_out) bytes_out[(int64_t)(i - r0) * Lp + b * VCO_BLK + j] = by;
                     if (S_out) S_out[(int64_t)(i - r0) * Lp + b * VCO_BLK + j] = (j < n) ? S[j] : 0.0f;
                     if (y_out)
                         y_out[(int64_t)(i - r0) * Lp + b * VCO_BLK + j] =
-                            (j >= n) ? -INFINITY : (mode == 0) ? fmaf(S[j], c8, krow) : fmaf(S[j], cb, zrow);
+                            (j >= n) ? -INFINITY : (mode == 0 || mode == 4) ? fmaf(S[j], c8, krow) : fmaf(S[j], cb, zrow);
                     p[j] = dec[by];
                     if (j < n) ell += p[j];
                 }
@@ -694,11 +699,11 @@ void vco_attention_rows(int mode, int L, int d, int z_off,
                     if (mode == 3)
                         rv = vco_e2m1_decode(v8[vr + j]) * ldexp(1.0, (int)v_exp[((int64_t)b * d + c) * 4 + vco_fp4_group(j)] - 127);
                     else
-                        rv = (mode != 1) ? dec[v8[vr + j]] : rf[vr + j];
+                        rv = real_qk ? rf[vr + j] : dec[v8[vr + j]];
                     acc += p[j] * rv;
                 }
-                double sv = (mode == 1 || mode == 3) ? 1.0 : (double)v_scale[(int64_t)b * d + c];
-                double accr = (mode != 1) ? (double)(float)acc : acc;
+                double sv = (real_qk || mode == 3) ? 1.0 : (double)v_scale[(int64_t)b * d + c];
+                double accr = real_qk ? acc : (double)(float)acc;
                 O[c] = alpha * O[c] + sv * accr + ell * (double)v_mean[(int64_t)b * d + c];
             }
             l = alpha * l + ell;

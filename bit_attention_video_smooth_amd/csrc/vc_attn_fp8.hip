@@ -1,8 +1,8 @@
 // vc_attn_fp8.hip -- launchers of the fused VC-Attention forward (V-Smooth
-// recipe) built from the kernel template in vc_attn_fp8_kernel.hpp: one
-// instance per head dim, output type, score dump, Skip Softmax and
-// probability-byte path (ExpCast or exp-then-cast).
-#include "vc_attn_fp8_kernel.hpp"
+// recipe) on the 32x32x64 wave of vc_attn_fp8w_kernel.hpp: one instance per
+// head dim, output type, score dump, Skip Softmax and probability-byte path
+// (ExpCast or exp-then-cast).
+#include "vc_attn_fp8w_kernel.hpp"
 
 namespace vc {
 
@@ -12,10 +12,10 @@ template <int D, bool OB, bool DUMP>
 hipError_t launch_s(const AttnArgs& a, hipStream_t st) {
     const bool skip = a.skip_thr > -INFINITY;
     if (a.prob_cast == 1)
-        return skip ? launch_t<D, OB, DUMP, true, true, REC_VC>(a, st)
-                    : launch_t<D, OB, DUMP, false, true, REC_VC>(a, st);
-    return skip ? launch_t<D, OB, DUMP, true, false, REC_VC>(a, st)
-                : launch_t<D, OB, DUMP, false, false, REC_VC>(a, st);
+        return skip ? launch_w32<D, OB, DUMP, true, true>(a, st)
+                    : launch_w32<D, OB, DUMP, false, true>(a, st);
+    return skip ? launch_w32<D, OB, DUMP, true, false>(a, st)
+                : launch_w32<D, OB, DUMP, false, false>(a, st);
 }
 
 }  // namespace

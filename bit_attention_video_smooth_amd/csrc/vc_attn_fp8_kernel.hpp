@@ -79,11 +79,13 @@ struct Fp8Tile {
     static constexpr int V_TILE = D * BLK;      // bytes of one V8 block  [D][128 slots]
     static constexpr int V4_TILE = D * BLK / 2; // bytes of one E2M1 V block [D][64]
     static constexpr int LPTV = V4_TILE / 4096; // E2M1 V chunks per loading thread
+    // the block's per-channel V scales (or E8M0 bytes) and means, 2 D
+    // floats, each loading wave copying its quarter; then a 256-byte window
+    // of K scales from the block on, copied by every loading wave (same data)
     static constexpr int SV_OFF = K_TILE + V_TILE;
-    // each loading wave keeps a private 1 KiB copy of the block's per-channel
-    // scales and means and a 256-byte window of K scales (readers use wave 0's)
-    static constexpr int KS_OFF = SV_OFF + 4 * 1024;
-    static constexpr int STAGE = KS_OFF + 4 * 256;
+    static constexpr int SVM = 2 * D * 4;
+    static constexpr int KS_OFF = SV_OFF + SVM;
+    static constexpr int STAGE = KS_OFF + 256;
     static constexpr int KCH = D / 16;          // 16-byte chunks per K row
     static constexpr int NCHK = K_TILE / 16;    // 16-byte chunks per K (or V) tile
     static constexpr int LPT = NCHK / 256;      // chunks per loading thread (group 0 loads)
@@ -195,17 +197,21 @@ __device__ __forceinline__ uint32_t dma_offset(int w, int lane, int row_bytes) {
 // Every copy runs with all 64 lanes, so each loading wave issues exactly
 // NLD copies per block and the wait counts below are exact.  Buffer
 // descriptors cover one head: reads past it return zeros.
-template <int D, int MODE>
+template <int D, int MODE, bool W32 = false>
 struct Fp8Loader {
     using T = Fp8Tile<D>;
     static constexpr bool SAGE = MODE == REC_SAGE_F8 || MODE == REC_SAGE_I8;
     static constexpr bool FP4V = MODE == REC_VC4;
     static constexpr int NVC = FP4V ? T::LPTV : T::LPT;  // V copies per loading thread
-    static constexpr int NLD = T::LPT + NVC + (SAGE ? 1 : 2);
-    static constexpr int NC = D / 4;  // 16-byte chunks of D floats
+    // copies per loading thread and block: the K part (K8 tile, K scales)
+    // and the V part (V8 tile, per-channel scales and means)
+    static constexpr int NLD_K = T::LPT + 1;
+    static constexpr int NLD_V = NVC + (SAGE ? 0 : 1) + (W32 ? 1 : 0);
+    static constexpr int NLD = NLD_K + NLD_V;
     v4si rk, rv, rks;
     const float *vs, *vm;
-    uint32_t off_k, off_v, off_sv;
+    uint32_t off_k, off_v;
+    int sv_p;
     // 4-bit V-Smooth: K rows enter LDS reordered so that the S^T products
     // give lane group g the keys 32 g .. 32 g + 31 of the block (one 32-key
     // group, the k-block of the lane's scaled FP4 operand): LDS row
@@ -214,8 +220,22 @@ struct Fp8Loader {
     // slice 0's rows plus 8 s (D = 128) or 16 s (D = 64) -- 1024 s bytes
     // either way -- so one in-block offset (slice 0) serves every slice.
     uint32_t off_k4;
-    int w, lane;
-    __device__ __forceinline__ Fp8Loader(const AttnArgs& a, int bh, int w_, int lane_) : w(w_), lane(lane_) {
+    // 32x32 wave (Fp8Wave32): LDS row 32 t + 8 j + 4 h + i of a block holds
+    // key 64 (t % 2) + 16 j + 8 (t / 2) + 4 h + i, so that the 32 x 32 S^T
+    // tiles give lane half h, for k-step s of the P V product, the keys of V
+    // slots 64 s + 32 h .. + 31 in the slot order of the V codes.  A 4 KiB
+    // slice covers whole 32-row tiles; slice i's keys are slice 0's plus
+    // key_off32(i) (below), so one in-block offset serves every slice.
+    uint32_t off_k32;
+    __device__ __forceinline__ static constexpr int key_off32(int i) {
+        return 64 * ((i * (4096 / D) / 32) % 2) + 8 * ((i * (4096 / D) / 32) / 2);
+    }
+    int w, lane;  // w: the wave's index within its group of four
+    // 32x32 wave: the history of block means in LDS ([32][D] floats, slot
+    // kb % 32), which the V part also fills
+    VC_LDS float* hist;
+    __device__ __forceinline__ Fp8Loader(const AttnArgs& a, int bh, int w_, int lane_, VC_LDS float* hist_ = nullptr)
+        : w(w_ & 3), lane(lane_), hist(hist_) {
         const size_t Lp = (size_t)a.nb * BLK;
         rk = make_rsrc(a.k8 + (size_t)bh * Lp * D, (uint32_t)(Lp * D));
         const size_t vrow = FP4V ? BLK / 2 : BLK;  // bytes per channel row of a V block
@@ -236,26 +256,63 @@ struct Fp8Loader {
             const int key = 32 * ((r % 16) / 4) + 4 * (r / 16) + r % 4;
             off_k4 = (uint32_t)(key * D + ((cp ^ chunk_swizzle(r, cpr)) << 4));
         }
+        {
+            const int cpr = D / 16;
+            const int p = w * 64 + lane;
+            const int r = p / cpr, cp = p % cpr;        // LDS row (slice 0) and chunk position
+            const int t = r / 32, rr = r % 32;
+            const int key = 64 * (t % 2) + 8 * (t / 2) + 16 * (rr / 8) + 4 * ((rr / 4) % 2) + rr % 4;
+            off_k32 = (uint32_t)(key * D + ((cp ^ chunk_swizzle(r, cpr)) << 4));
+        }
         off_v = dma_offset(w, lane, FP4V ? BLK / 2 : BLK);
-        off_sv = (uint32_t)((lane % (2 * NC)) % NC) * 16;  // lanes past 2*NC repeat
+        // float p of the [scales | means] region: wave w's quarter, lanes
+        // past 2 D (D = 64) repeating the first half with the same data
+        sv_p = (w * 64 + lane) % (2 * D);
     }
-    __device__ __forceinline__ void issue(lds_u8* stage, int kb) const {
+    // The wave's LDS offset is made opaque at each issue so that the
+    // per-copy LDS addresses (four stages x every copy) are formed there by
+    // scalar adds instead of being kept in scalar registers for the whole
+    // kernel (which spills them into vector-register lanes).
+    // K part: K8 copies I0 .. I1 - 1 and, with KS, the K scales
+    template <int I0, int I1, bool KS>
+    __device__ __forceinline__ void issue_k_part(lds_u8* stage, int kb) const {
+        int wo = w * 1024;
+        asm volatile("" : "+s"(wo));
 #pragma unroll
-        for (int i = 0; i < T::LPT; i++) {
+        for (int i = I0; i < I1; i++) {
             if (FP4V)
-                lds_dma16(rk, stage + (i * 4 + w) * 1024, off_k4, kb * T::K_TILE + i * 1024);
+                lds_dma16(rk, stage + wo + i * 4096, off_k4, kb * T::K_TILE + i * 1024);
+            else if (W32)
+                lds_dma16(rk, stage + wo + i * 4096, off_k32, kb * T::K_TILE + key_off32(i) * D);
             else
-                lds_dma16(rk, stage + (i * 4 + w) * 1024, off_k, kb * T::K_TILE + i * 4096);
+                lds_dma16(rk, stage + wo + i * 4096, off_k, kb * T::K_TILE + i * 4096);
         }
+        if (KS) lds_dma4(rks, stage + T::KS_OFF, lane * 4, SAGE ? kb * 32 : kb * 4);
+    }
+    // V part: V8 copies I0 .. I1 - 1 and, with SV, the scales and means
+    template <int I0, int I1, bool SV>
+    __device__ __forceinline__ void issue_v_part(lds_u8* stage, int kb) const {
+        int wo = w * 1024;
+        asm volatile("" : "+s"(wo));
 #pragma unroll
-        for (int i = 0; i < NVC; i++)
-            lds_dma16(rv, stage + T::K_TILE + (i * 4 + w) * 1024, off_v,
-                      kb * (FP4V ? T::V4_TILE : T::V_TILE) + i * 4096);
-        if (!SAGE) {
-            const float* src = ((lane % (2 * NC)) < NC ? vs : vm) + (size_t)kb * D;
-            lds_dma16_flat(reinterpret_cast<const uint8_t*>(src) + off_sv, stage + T::SV_OFF + w * 1024);
+        for (int i = I0; i < I1; i++)
+            lds_dma16(rv, stage + T::K_TILE + wo + i * 4096, off_v, kb * (FP4V ? T::V4_TILE : T::V_TILE) + i * 4096);
+        if (SV && !SAGE) {
+            const float* src = (sv_p < D ? vs + sv_p : vm + (sv_p - D)) + (size_t)kb * D;
+            lds_dma4_flat(src, stage + T::SV_OFF + ((wo >> 2) % T::SVM));
         }
-        lds_dma4(rks, stage + T::KS_OFF + w * 256, lane * 4, SAGE ? kb * 32 : kb * 4);
+        if (SV && W32) {
+            // the block's means, float (w * 64 + lane) % D of history slot
+            // kb % 32 (at D = 64 all four waves copy the same 64 floats)
+            const float* src = vm + (size_t)kb * D + (sv_p % D);
+            lds_dma4_flat(src, reinterpret_cast<lds_u8*>(hist + (kb % 32) * D) + ((wo >> 2) % (D * 4)));
+        }
+    }
+    __device__ __forceinline__ void issue_k(lds_u8* stage, int kb) const { issue_k_part<0, T::LPT, true>(stage, kb); }
+    __device__ __forceinline__ void issue_v(lds_u8* stage, int kb) const { issue_v_part<0, NVC, true>(stage, kb); }
+    __device__ __forceinline__ void issue(lds_u8* stage, int kb) const {
+        issue_k(stage, kb);
+        issue_v(stage, kb);
     }
 };
 
@@ -292,6 +349,7 @@ struct Fp8Wave {
     // than its 8 registers); the INT8 SAGE instance, whose score products
     // need more registers, rebuilds it per block instead of spilling.
     static constexpr bool ONES_RESIDENT = MODE != REC_SAGE_I8;
+    static constexpr bool SPLIT = false;  // all copies by waves 0-3
     v8i ones8;
 
     // In-block key of score (kt, i) of this lane: 16 kt + 4 g + i, or for
@@ -764,9 +822,8 @@ struct Fp8Wave {
     // block kb (softmax, P V) until it reaches barrier kb + 2, so the ring
     // has four stages: block kb + 2 is copied, after barrier kb, into the
     // stage of block kb - 2, which both groups left before that barrier.
-    template <bool LOADER, bool LAG>
-    __device__ __forceinline__ void block(const Fp8Loader<D, MODE>& ld, int kb, const lds_u8* cur,
-                                          lds_u8* ahead) {
+    template <bool LOADER, bool LAG, class LD>
+    __device__ __forceinline__ void block(const LD& ld, int kb, const lds_u8* cur, lds_u8* ahead) {
         slot_qk(cur);
         if (LAG) block_barrier();
         if (LOADER) ld.issue(ahead, min(kb + 2, nb - 1));
@@ -788,13 +845,13 @@ struct Fp8Wave {
             if (DUMP)
                 wait_vmcnt<0>();
             else
-                wait_vmcnt<Fp8Loader<D, MODE>::NLD>();
+                wait_vmcnt<LD::NLD>();
         }
         if (!LAG) block_barrier();
     }
 
-    template <bool LOADER, bool LAG>
-    __device__ __forceinline__ void run(const Fp8Loader<D, MODE>& ld, lds_u8* const (&st)[4]) {
+    template <bool LOADER, bool LAG, class LD>
+    __device__ __forceinline__ void run(const LD& ld, lds_u8* const (&st)[4]) {
         for (int kb = 0; kb < nb; kb += 4) {
             block<LOADER, LAG>(ld, kb, st[0], st[2]);
             if (kb + 1 < nb) block<LOADER, LAG>(ld, kb + 1, st[1], st[3]);
@@ -802,12 +859,48 @@ struct Fp8Wave {
             if (kb + 3 < nb) block<LOADER, LAG>(ld, kb + 3, st[3], st[1]);
         }
     }
+
+    // O / l in the original row order; lane (col, g) holds channels
+    // 16 ct + 4 g + i (SAGE: O s_v / l with the per-channel V scale)
+    template <bool OUT_BF16>
+    __device__ __forceinline__ void store() {
+#pragma unroll
+        for (int qt = 0; qt < 2; qt++) {
+            const int row = q0 + 16 * qt + col;
+            if (row >= L) continue;
+            const float il = 1.0f / l[qt];
+            if (SAGE) {
+#pragma unroll
+                for (int ct = 0; ct < T::NCT; ct++) {
+                    const f32x4 sv = *reinterpret_cast<const f32x4*>(a.v_scale + (size_t)bh * D + 16 * ct + 4 * g);
+#pragma unroll
+                    for (int i = 0; i < 4; i++) O[qt][ct][i] = __fmul_rn(O[qt][ct][i], sv[i]);
+                }
+            }
+            if (OUT_BF16) {
+                uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + ((size_t)bh * L + row) * D;
+#pragma unroll
+                for (int ct = 0; ct < T::NCT; ct++) {
+                    uint32_t lo = pack_bf16x2(O[qt][ct][0] * il, O[qt][ct][1] * il);
+                    uint32_t hi = pack_bf16x2(O[qt][ct][2] * il, O[qt][ct][3] * il);
+                    *reinterpret_cast<uint2*>(o + 16 * ct + 4 * g) = make_uint2(lo, hi);
+                }
+            } else {
+                float* o = reinterpret_cast<float*>(a.out) + ((size_t)bh * L + row) * D;
+#pragma unroll
+                for (int ct = 0; ct < T::NCT; ct++)
+                    *reinterpret_cast<float4*>(o + 16 * ct + 4 * g) =
+                        make_float4(O[qt][ct][0] * il, O[qt][ct][1] * il, O[qt][ct][2] * il, O[qt][ct][3] * il);
+            }
+        }
+    }
 };
 
-template <int D, bool OUT_BF16, bool DUMP, bool SKIP, bool NAIVE, int MODE>
+// One workgroup: 8 waves, 256 queries of one head, the four-stage ring.
+// WV is the wave (Fp8Wave or Fp8Wave32), LD its loader.
+template <class WV, class LD, bool OUT_BF16>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fp8_kernel(AttnArgs a) {
-    constexpr bool SAGE = MODE == REC_SAGE_F8 || MODE == REC_SAGE_I8;
-    using T = Fp8Tile<D>;
+    using T = typename WV::T;
     __shared__ __attribute__((aligned(16))) uint8_t st0_[T::STAGE];
     __shared__ __attribute__((aligned(16))) uint8_t st1_[T::STAGE];
     __shared__ __attribute__((aligned(16))) uint8_t st2_[T::STAGE];
@@ -818,64 +911,42 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fp8_kernel(AttnArgs a) {
     const int bh = pid / a.nqt, qtile = pid % a.nqt;
     // wave index as a scalar (uniform) value
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    Fp8Wave<D, DUMP, SKIP, NAIVE, MODE> s(a, bh, qtile, w, lane);
-    const Fp8Loader<D, MODE> ld(a, bh, w, lane);
+    WV s(a, bh, qtile, w, lane);
+    const LD ld(a, bh, w, lane);
     const int nb = a.nb;
 
-    // Blocks 0 and 1 are in flight before the loop; block 0 is published by
-    // the first barrier.  The loading waves drain their copies past the end
-    // before they exit.
-    if (s.grp == 0) {
+    // Blocks 0 and 1 (and 2, for the V part of a split wave) are in flight
+    // before the loop; block 0 is published by the first barrier.  Every
+    // wave drains its copies past the end before it exits.
+    if (WV::SPLIT) {
+        if (s.grp == 0) {
+            ld.issue_k(st[0], 0);
+            ld.issue_k(st[1], min(1, nb - 1));
+            wait_vmcnt<LD::NLD_K>();
+        } else {
+            ld.issue_v(st[0], 0);
+            ld.issue_v(st[1], min(1, nb - 1));
+            ld.issue_v(st[2], min(2, nb - 1));
+            wait_vmcnt<2 * LD::NLD_V>();
+        }
+    } else if (s.grp == 0) {
         ld.issue(st[0], 0);
         ld.issue(st[1], min(1, nb - 1));
-        wait_vmcnt<Fp8Loader<D, MODE>::NLD>();
+        wait_vmcnt<LD::NLD>();
     }
     block_barrier();
-    if (s.grp == 0) {
+    if (s.grp == 0)
         s.template run<true, false>(ld, st);
-        wait_vmcnt<0>();
-    } else {
+    else
         s.template run<false, true>(ld, st);
-    }
-
-    // O / l, original row order; lane (col, g) holds channels 16 ct + 4 g + i
-    // (SAGE: O s_v / l with the per-channel V scale)
-#pragma unroll
-    for (int qt = 0; qt < 2; qt++) {
-        const int row = s.q0 + 16 * qt + s.col;
-        if (row >= s.L) continue;
-        const float il = 1.0f / s.l[qt];
-        if (SAGE) {
-#pragma unroll
-            for (int ct = 0; ct < T::NCT; ct++) {
-                const f32x4 sv = *reinterpret_cast<const f32x4*>(a.v_scale + (size_t)bh * D + 16 * ct + 4 * s.g);
-#pragma unroll
-                for (int i = 0; i < 4; i++) s.O[qt][ct][i] = __fmul_rn(s.O[qt][ct][i], sv[i]);
-            }
-        }
-        if (OUT_BF16) {
-            uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + ((size_t)bh * s.L + row) * D;
-#pragma unroll
-            for (int ct = 0; ct < T::NCT; ct++) {
-                uint32_t lo = pack_bf16x2(s.O[qt][ct][0] * il, s.O[qt][ct][1] * il);
-                uint32_t hi = pack_bf16x2(s.O[qt][ct][2] * il, s.O[qt][ct][3] * il);
-                *reinterpret_cast<uint2*>(o + 16 * ct + 4 * s.g) = make_uint2(lo, hi);
-            }
-        } else {
-            float* o = reinterpret_cast<float*>(a.out) + ((size_t)bh * s.L + row) * D;
-#pragma unroll
-            for (int ct = 0; ct < T::NCT; ct++)
-                *reinterpret_cast<float4*>(o + 16 * ct + 4 * s.g) =
-                    make_float4(s.O[qt][ct][0] * il, s.O[qt][ct][1] * il, s.O[qt][ct][2] * il,
-                                s.O[qt][ct][3] * il);
-        }
-    }
+    wait_vmcnt<0>();
+    s.template store<OUT_BF16>();
 }
 
 template <int D, bool OB, bool DUMP, bool SKIP, bool NAIVE, int MODE>
 hipError_t launch_t(const AttnArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL((attn_fp8_kernel<D, OB, DUMP, SKIP, NAIVE, MODE>), dim3(a.BH * a.nqt), dim3(NW * 64), 0,
-                       st, a);
+    hipLaunchKernelGGL((attn_fp8_kernel<Fp8Wave<D, DUMP, SKIP, NAIVE, MODE>, Fp8Loader<D, MODE>, OB>),
+                       dim3(a.BH * a.nqt), dim3(NW * 64), 0, st, a);
     return hipGetLastError();
 }
 

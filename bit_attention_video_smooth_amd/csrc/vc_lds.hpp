@@ -70,6 +70,13 @@ __device__ __forceinline__ void lds_dma16_flat(const void* g, const lds_u8* lds_
                  : "memory", "m0");
 }
 
+__device__ __forceinline__ void lds_dma4_flat(const void* g, const lds_u8* lds_wave_base) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+                 :: "s"(__builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base))),
+                    "v"(reinterpret_cast<uint64_t>(g))
+                 : "memory", "m0");
+}
+
 #pragma clang diagnostic pop
 
 // s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits

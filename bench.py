@@ -40,6 +40,7 @@ def parse():
     p.add_argument("--no-sage", action="store_true", help="skip the SAGE-style baseline leg")
     p.add_argument("--no-warm", action="store_true", help="skip the k-means warm-start leg")
     p.add_argument("--no-fp4", action="store_true", help="skip the 4-bit V-Smooth leg")
+    p.add_argument("--no-configs", action="store_true", help="skip timing the other workloads")
     p.add_argument("--v-scale-mode", type=int, default=0)
     p.add_argument("--skip-lambda", type=float, default=0.5,
                    help="Skip Softmax threshold of the extra, reported (not timed-step) attention run; 0: none")
@@ -52,6 +53,7 @@ def parse():
 # Sources the attention kernel is built from; the committed HBM-traffic
 # summary records their hash and is ignored once any of them changes.
 KERNEL_SOURCES = ["bit_attention_video_smooth_amd/csrc/vc_attn_fp8.hip",
+                  "bit_attention_video_smooth_amd/csrc/vc_attn_fp8w_kernel.hpp",
                   "bit_attention_video_smooth_amd/csrc/vc_attn_fp8_kernel.hpp",
                   "bit_attention_video_smooth_amd/csrc/vc_device.hpp",
                   "bit_attention_video_smooth_amd/csrc/vc_lds.hpp",
@@ -158,6 +160,14 @@ def main():
     attn_each = [e[1].elapsed_time(e[2]) for e in evs]
     attn_ms = float(np.mean(attn_each))
     print("step %.3f ms (prepare %.3f, attention %.3f)" % (ms_step, prep_ms, attn_ms), file=sys.stderr, flush=True)
+    h00 = (qn[0, 0].copy(), kn[0, 0].copy(), vn[0, 0].copy())
+    # head (0, 0) of the timed step's output and permutation, for the parity sample
+    out00 = out[0, 0].cpu().numpy()
+    perm00 = P.perm[0, 0].cpu().numpy()
+    codes00 = {n: getattr(P, n)[0, 0].cpu().numpy() for n in ("q8", "k8", "q_scale", "k_scale", "v_scale", "v_mean")}
+    codes00["v8"] = api.v_codes_natural(P.v8[0:1, 0:1]).cpu().numpy()[0, 0]
+    obj00 = float(P.kmeans_obj[0, 0].cpu())
+    dump00 = api.attention_dump(P, 0, 0)
     if args.v_scale_mode not in (0, 1):
         sys.exit("--v-scale-mode must be 0 or 1")
 
@@ -208,9 +218,14 @@ def main():
         _, _, pf = api.attention_dump(P, bh, qt)
         live = pf.view(256, nb, 128).any(2)
         rej = (~pb.view(256, nb, 128).any(2)) & live
+        # a wave (32 query rows) skips a block's bytes and P V only when all
+        # its rows reject it
+        wlive = live.view(8, 32, nb).any(1)
+        wrej = (rej | ~live).view(8, 32, nb).all(1) & wlive
         skip = {"lambda": args.skip_lambda, "ms": skip_ms, "speedup_vs_no_rejection": attn_ms / skip_ms,
                 "dense_equivalent_tflops": flop / skip_ms / 1e9,
                 "rejected_fraction_sample": float(rej.float().sum() / live.float().sum()),
+                "wave_rejected_fraction_sample": float(wrej.float().sum() / wlive.float().sum()),
                 "sample": "query tile %d of head %d (256 rows x %d blocks)" % (qt, bh, nb)}
         print("skip softmax lambda %g: %.3f ms" % (args.skip_lambda, skip_ms), file=sys.stderr, flush=True)
     bf16 = None
@@ -353,6 +368,20 @@ def main():
 
     clock = clock_under_load(lambda: api.attention(P, out=out), stream)
 
+    # the other workloads: prepare (with and without k-means) and attention
+    configs = None
+    if not args.no_configs:
+        del P, ws, out, q, k, v, qn, kn, vn
+        torch.cuda.empty_cache()
+        configs = {cfg.name: {"attention_ms": attn_ms, "tflops": attn_tflops_of(flop, attn_ms),
+                              "frac_fp8_peak": attn_tflops_of(flop, attn_ms) / FP8_PEAK_TFLOPS,
+                              "prepare_ms_with_kmeans": prep_ms, "prepare_ms_without_kmeans": quant_ms,
+                              "prepare_gbs_without_kmeans": quant_bytes / quant_ms / 1e6, "measured": "timed step"}}
+        for ci, c in enumerate(synth.CONFIGS):
+            if ci != args.config:
+                configs[c.name] = time_config(c, ci, stream)
+                print("config %s: %s" % (c.name, configs[c.name]), file=sys.stderr, flush=True)
+
     attn_tflops = flop / attn_ms / 1e9
     res = {
         "metric": "FP8 attention TFLOP/s (4*B*H*L^2*d) & % FP8 MFMA peak, Wan2.2-shaped L=75,600",
@@ -398,6 +427,7 @@ def main():
         "sage_baseline": sage,
         "fp4_v_smooth": fp4,
         "skip_softmax": skip,
+        "configs": configs,
         "grouping_schedule": grouping_schedule(prep_ms, quant_ms, attn_ms),
         "kmeans_warm_start": warm,
         "v_smooth_ablation": ablation,
@@ -406,8 +436,59 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu:
-        res["cpu_baseline"] = cpu_baseline(cfg, qn, kn, vn, args.cpu_rows)
+        res["cpu_baseline"] = cpu_baseline(cfg, h00, args.cpu_rows, perm00, codes00, out00, obj00, dump00, args.config)
     print(json.dumps(res))
+
+
+def attn_tflops_of(flop, ms):
+    return flop / ms / 1e9
+
+
+def time_config(c, ci, stream, reps=None):
+    """Prepare (seeded k-means, 8 rounds; and with the permutation passed
+    back in) and FP8 attention times of one more workload, on its own
+    seeded synthetic inputs; all buffers freed afterwards."""
+    import numpy as np
+    import torch
+
+    from bit_attention_video_smooth_amd import api, synth
+    B, H, L, d = c.B, c.H, c.L, c.d
+    qn, kn, vn = synth.make_inputs(c, ci, threads=16)
+    dev = lambda a: torch.from_numpy(a).view(torch.bfloat16).cuda()
+    q, k, v = dev(qn), dev(kn), dev(vn)
+    del qn, kn, vn
+    P = api.alloc_prepared(B, H, L, d)
+    ws = api.workspace(B, H, L, d)
+    out = torch.empty((B, H, L, d), dtype=torch.float32, device="cuda")
+    flop = c.attn_flop
+    n = reps or (3 if flop > 2e14 else 10)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def timed(fn, k):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(k):
+            ev[0].record(stream)
+            fn()
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            ts.append(ev[0].elapsed_time(ev[1]))
+        return float(np.median(ts))
+
+    p_km = timed(lambda: api.prepare(q, k, v, seed=ci, out=P, ws=ws), 3)
+    p_q = timed(lambda: api.prepare(q, k, v, perm_in=P.perm, out=P, ws=ws), 3)
+    a_ms = timed(lambda: api.attention(P, out=out), n)
+    nb = api.nblocks(L)
+    E = B * H * L * d
+    qbytes = 3 * E * 2 + 3 * E * 1 + B * H * nb * d * 8 + B * H * L * 4
+    r = {"B": B, "H": H, "L": L, "d": d, "attention_ms": a_ms, "tflops": attn_tflops_of(flop, a_ms),
+         "frac_fp8_peak": attn_tflops_of(flop, a_ms) / FP8_PEAK_TFLOPS, "prepare_ms_with_kmeans": p_km,
+         "prepare_ms_without_kmeans": p_q, "prepare_gbs_without_kmeans": qbytes / p_q / 1e6,
+         "measured": "median of %d attention launches, 3 prepares each" % n}
+    del P, ws, out, q, k, v
+    torch.cuda.empty_cache()
+    return r
 
 
 def clock_under_load(launch, stream, n=20):
@@ -458,18 +539,22 @@ def grouping_schedule(prep_ms, quant_ms, attn_ms, num_steps=40):
             "grouping_share_of_attention": n * (prep_ms - quant_ms) / (num_steps * attn_ms)}
 
 
-def cpu_baseline(cfg, qn, kn, vn, rows):
-    """The CPU oracle, as it stands, on a bounded sample of the same workload:
-    one head prepared with the identity permutation, then blockwise
-    attention for `rows` query rows against all L keys; throughput is that
-    sample's attention FLOP over the oracle's attention time."""
+def cpu_baseline(cfg, h00, rows, perm00, codes00, out00, obj00, dump00, seed):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload
+    -- head (0, 0), prepared with the permutation the GPU's k-means chose,
+    then blockwise attention for `rows` query rows against all L keys;
+    throughput is that sample's attention FLOP over the oracle's attention
+    time -- and the parity of the timed step on that sample: prepare codes
+    and scales, output rows against the oracle (end to end), ExpCast bytes
+    of query tile 0 given the kernel's own scores, and the k-means
+    objective against the oracle's k-means from the same seed."""
     import numpy as np
 
     import oracle
     L, d = cfg.L, cfg.d
-    perm = np.arange(L, dtype=np.int32)
+    qh, kh, vh = h00
     t0 = time.time()
-    P = oracle.prepare_head(qn[0, 0], kn[0, 0], vn[0, 0], perm)
+    P = oracle.prepare_head(qh, kh, vh, perm00)
     t_prep = time.time() - t0
     if rows <= 0:  # size the sample to about 12 s of oracle time
         probe = min(L, 4 * oracle.num_threads())
@@ -479,7 +564,7 @@ def cpu_baseline(cfg, qn, kn, vn, rows):
         rows = int(max(probe, min(L, 12.0 / max(per_row, 1e-9))))
     rows = min(rows, L)
     t0 = time.time()
-    oracle.attention_head(P, L, 8, rows=(0, rows))
+    ref = oracle.attention_head(P, L, 8, rows=(0, rows))
     t_attn = time.time() - t0
     fl = 4.0 * rows * L * d
     cpu = None
@@ -488,11 +573,34 @@ def cpu_baseline(cfg, qn, kn, vn, rows):
             cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
     except OSError:
         pass
+    # parity of the timed step on head (0, 0)
+    codes = {n: bool(np.array_equal(np.asarray(codes00[n]).view(np.uint8), np.asarray(P[n]).view(np.uint8)))
+             for n in ("q8", "k8", "v8", "q_scale", "k_scale", "v_scale", "v_mean")}
+    got = out00[:rows].astype(np.float64)
+    refd = ref.astype(np.float64)
+    rel = float(np.linalg.norm(got - refd) / np.linalg.norm(refd))
+    mab = float(np.abs(got - refd).max() / np.abs(refd).max())
+    _, s_k, b_k = dump00
+    nr = min(256, L)
+    S = s_k.cpu().numpy()[:nr]
+    _, by_o, _, _ = oracle.attention_head(P, L, 8, rows=(0, nr), want_bytes=True, scores=S)
+    by_k = b_k.cpu().numpy()[:nr, :L]
+    mism = float(np.mean(by_k != by_o[:, :L]))
+    t0 = time.time()
+    nb = oracle.nblocks(L)
+    _, _, obj_o = oracle.kmeans(vh, nb, 8, oracle.head_seed(seed, 0, 0, cfg.H))
+    t_km = time.time() - t0
+    parity = {"sample": "head (0,0)", "codes_and_scales_bit_exact": codes,
+              "output_rel_l2": rel, "output_max_abs_over_max": mab, "output_rows": rows,
+              "bar": "rel-L2 <= 1e-3, max-abs <= 1e-2 max|O| (end to end, oracle with exactly rounded scores)",
+              "byte_mismatch_given_kernel_scores": mism, "byte_sample": "query tile 0 (%d rows x %d keys)" % (nr, L),
+              "kmeans_objective_ratio": obj00 / float(obj_o), "kmeans_oracle_s": t_km}
     return {"value": fl / t_attn / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "cpu_model": cpu,
             "kind": "oracle",
-            "sample": "head (0,0) of %s: oracle prepare (identity permutation, %.2fs) then blockwise "
+            "sample": "head (0,0) of %s: oracle prepare (the GPU's k-means permutation, %.2fs) then blockwise "
                       "ExpCast attention for %d query rows x %d keys (%.2fs); k-means not included"
-                      % (cfg.name, t_prep, rows, L, t_attn)}
+                      % (cfg.name, t_prep, rows, L, t_attn),
+            "parity": parity}
 
 
 if __name__ == "__main__":

@@ -280,7 +280,7 @@ struct Fp8Wave32 {
     // Softmax of block kb (stage `cur`): the running max, the rescale of O
     // and of the pending row sums when a row's max rose, and the bytes.
     // Returns true when every row of the wave rejects the block (Skip
-    // Softmax; its bytes are then all 0).
+    // Softmax; the bytes are then not formed and P V is skipped).
     __device__ __forceinline__ bool slot_softmax(int kb, const lds_u8* cur) {
         const float ks = *reinterpret_cast<const VC_LDS float*>(cur + T::KS_OFF);
         cb = __fmul_rn(__fmul_rn(sq, ks), a.C0);
@@ -298,8 +298,13 @@ struct Fp8Wave32 {
         const bool partial = nvalid < BLK;
         if (partial) mask_scores(lim);
         softmax_max();
-        softmax_bytes(cscale);
-        if (partial) mask_bytes(lim);
+        // Skip Softmax: when every row of the wave rejects the block its
+        // bytes would all be 0 and nothing reads them (P V is skipped too)
+        const bool rejected = SKIP && !DUMP && __all(reject);
+        if (__builtin_expect(!rejected, 1)) {
+            softmax_bytes(cscale);
+            if (partial) mask_bytes(lim);
+        }
         if (dumping) {
 #pragma unroll
             for (int t = 0; t < 4; t++)
@@ -318,7 +323,7 @@ struct Fp8Wave32 {
 #pragma unroll
             for (int i = 0; i < 8; i++) W[i] *= alpha;
         }
-        return SKIP && !DUMP && __all(reject);
+        return rejected;
     }
 
     // Row sum and O += s_v (.) P V of block kb on the matrix cores.  O = P8
@@ -446,14 +451,18 @@ struct Fp8Wave32 {
         const bool rejected = slot_softmax(kb, cur);
         if (LAG) ld.template issue_v_part<C / 2, C / 2 + 1, false>(ahead3, vc);
         if (LOADER) ld.template issue_k_part<C / 2, C / 2 + 1, false>(ahead2, kc);
-        auto rest = [&]() {
+        if (SKIP) {
+            // one code path for the last copies: a branch around them doubles
+            // the loader code and the registers it holds
             if (LAG) ld.template issue_v_part<C / 2 + 1, C, true>(ahead3, vc);
             if (LOADER) ld.template issue_k_part<C / 2 + 1, C, true>(ahead2, kc);
-        };
-        if (__builtin_expect(!rejected, 1))
-            slot_pv(kb, cur, rest);
-        else
-            rest();
+            if (__builtin_expect(!rejected, 1)) slot_pv(kb, cur, [] {});
+        } else {
+            slot_pv(kb, cur, [&]() {
+                if (LAG) ld.template issue_v_part<C / 2 + 1, C, true>(ahead3, vc);
+                if (LOADER) ld.template issue_k_part<C / 2 + 1, C, true>(ahead2, kc);
+            });
+        }
         if ((kb & 15) == 15 || kb == nb - 1) flush_means(kb);
         if (LOADER) {
             if (DUMP)

@@ -36,13 +36,23 @@ __global__ __launch_bounds__(256) void k_colsum_partial(const uint16_t* __restri
     double acc[8];
 #pragma unroll
     for (int e = 0; e < 8; e++) acc[e] = 0.0;
-    for (int r = r0 + rs; r < r1; r += RPI) {
-        uint4 w = *reinterpret_cast<const uint4*>(base + (size_t)r * D + cc * 8);
-        uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+    // four rows per thread in flight: all loads of a step are issued before
+    // their sums
+    for (int r = r0 + rs; r < r1; r += 4 * RPI) {
+        uint4 w4[4];
 #pragma unroll
-        for (int e = 0; e < 4; e++) {
-            acc[2 * e] += (double)bf16_to_f32(ww[e] & 0xFFFFu);
-            acc[2 * e + 1] += (double)bf16_to_f32(ww[e] >> 16);
+        for (int u = 0; u < 4; u++) {
+            w4[u] = make_uint4(0, 0, 0, 0);  // rows past the chunk add 0
+            if (r + u * RPI < r1) w4[u] = *reinterpret_cast<const uint4*>(base + (size_t)(r + u * RPI) * D + cc * 8);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const uint32_t ww[4] = {w4[u].x, w4[u].y, w4[u].z, w4[u].w};
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                acc[2 * e] += (double)bf16_to_f32(ww[e] & 0xFFFFu);
+                acc[2 * e + 1] += (double)bf16_to_f32(ww[e] >> 16);
+            }
         }
     }
 #pragma unroll
@@ -158,15 +168,18 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(const uint16_t* __restric
 
 // ------------------------------------------------------------------------
 // V-Smooth residual quantisation of one permuted 128-token block.
-// Wave w holds keys 32 w .. 32 w + 31 of the block (slots in permuted order)
-// and lane l holds channels CPL l .. CPL l + CPL - 1 (CPL = D / 64), so each
-// key's row is one coalesced load across the wave and the values stay in
-// registers: per-channel fp64 sums (exact for bf16 inputs, so the order does
-// not matter) and maxima are combined over the four waves through LDS.  The
-// codes are channel-major in the slot order of the attention kernel's P V
-// operand, where the 32 keys of wave w fill slots 32 b + 8 w .. 32 b + 8 w +
-// 7 of every channel row (b = 0..3); they are assembled in an LDS tile and
-// the block's D x 128 bytes, contiguous in HBM, leave as 16-byte stores.
+// Wave w holds keys 32 w .. 32 w + 31 of the block (slots in permuted order).
+// A key row is R = D / 8 sixteen-byte chunks; lane l takes chunk l % R
+// (channels 8 (l % R) .. + 7) of its keys, so one load instruction moves
+// 64 / R whole rows.  The wave's 32 keys are 8 quads of consecutive keys;
+// lane l holds the quads g = l / R + (64 / R) u, i.e. its keys lie in
+// consecutive slots of the attention kernel's P V operand order, where the
+// keys 4 g .. 4 g + 3 of wave w fill slots 32 (g % 4) + 8 w + 4 (g / 4) + i
+// of every channel row.  Per-channel fp64 sums (exact for bf16 inputs, so
+// the order does not matter) and maxima are combined over the lanes of one
+// chunk with cross-lane exchanges and over the four waves through LDS.  The
+// codes are assembled channel-major in an LDS tile, and the block's D x 128
+// bytes, contiguous in HBM, leave as 16-byte stores.
 template <int D>
 __global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict__ v,
                                                       const int32_t* __restrict__ perm,
@@ -174,80 +187,100 @@ __global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict
                                                       float* __restrict__ vscale,
                                                       float* __restrict__ vmean, int L, int nb,
                                                       int mode) {
-    constexpr int CPL = D / 64;  // channels per lane
-    constexpr int KW = BLK / 4;  // keys per wave
-    constexpr int PITCH = BLK + 16;  // LDS row of one channel's codes, padded against bank conflicts
+    constexpr int R = D / 8;          // 16-byte chunks per key row
+    constexpr int G = 64 / R;         // key rows per load instruction
+    constexpr int NL = 32 / G;        // keys per lane
+    constexpr int PITCH = BLK + 16;   // LDS row of one channel's codes, padded against bank conflicts
+    static_assert(NL % 4 == 0, "whole key quads per lane");
     __shared__ double psum[4][D];
     __shared__ float pmax[4][D];
     __shared__ __attribute__((aligned(16))) uint8_t tile[D * PITCH];
     const int b = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63;
+    const int cc = lane % R, r = lane / R;
     const int i0 = b * BLK;
     const int n = min(BLK, L - i0);
-    const uint16_t* vb = v + (size_t)bh * L * D + CPL * lane;
-    const int32_t* pb = perm + (size_t)bh * L + i0 + KW * w;
-    const int nw = min(KW, max(0, n - KW * w));  // valid keys of this wave
-    float x[KW][CPL];
+    const int kw0 = 32 * w;  // the wave's first key within the block
+    // the wave's 32 permutation entries, one per lane of its lower half
+    int pv = 0;
+    if (lane < 32 && kw0 + lane < n) pv = perm[(size_t)bh * L + i0 + kw0 + lane];
+    const uint16_t* vb = v + (size_t)bh * L * D + 8 * cc;
+    float x[NL][8];
 #pragma unroll
-    for (int i = 0; i < KW; i++) {
-        if (i < nw) {
-            const int src = pb[i];  // uniform across the wave
-            if (CPL == 2) {
-                const uint32_t u = *reinterpret_cast<const uint32_t*>(vb + (size_t)src * D);
-                x[i][0] = bf16_to_f32(u & 0xFFFFu);
-                x[i][CPL - 1] = bf16_to_f32(u >> 16);
-            } else {
-                x[i][0] = bf16_to_f32(vb[(size_t)src * D]);
+    for (int j = 0; j < NL; j++) {
+        const int kl = 4 * (r + G * (j / 4)) + j % 4;  // key within the wave
+        const int src = __shfl(pv, kl);
+        if (kw0 + kl < n) {
+            const uint4 u = *reinterpret_cast<const uint4*>(vb + (size_t)src * D);
+            const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                x[j][2 * e] = bf16_to_f32(uu[e] & 0xFFFFu);
+                x[j][2 * e + 1] = bf16_to_f32(uu[e] >> 16);
             }
         } else {
 #pragma unroll
-            for (int e = 0; e < CPL; e++) x[i][e] = 0.0f;
+            for (int e = 0; e < 8; e++) x[j][e] = 0.0f;
         }
     }
+    double s[8];
 #pragma unroll
-    for (int e = 0; e < CPL; e++) {
-        double s4[4] = {0.0, 0.0, 0.0, 0.0};
+    for (int e = 0; e < 8; e++) {
+        s[e] = 0.0;
 #pragma unroll
-        for (int i = 0; i < KW; i++) s4[i % 4] += (double)x[i][e];  // padded keys add 0
-        psum[w][CPL * lane + e] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+        for (int j = 0; j < NL; j++) s[e] += (double)x[j][e];  // padded keys add 0
     }
-    __syncthreads();
-    float mu[CPL], inv[CPL];
 #pragma unroll
-    for (int e = 0; e < CPL; e++) {
-        const int c = CPL * lane + e;
+    for (int o = R; o < 64; o <<= 1)
+#pragma unroll
+        for (int e = 0; e < 8; e++) s[e] += __shfl_xor(s[e], o);
+    if (r == 0)
+#pragma unroll
+        for (int e = 0; e < 8; e++) psum[w][8 * cc + e] = s[e];
+    __syncthreads();
+    float mu[8], am[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+        const int c = 8 * cc + e;
         mu[e] = (float)((((psum[0][c] + psum[1][c]) + psum[2][c]) + psum[3][c]) / (double)n);
-        float am = 0.0f;
+        am[e] = 0.0f;
 #pragma unroll
-        for (int i = 0; i < KW; i++)
-            if (i < nw) am = fmaxf(am, fabsf(__fsub_rn(x[i][e], mu[e])));
-        pmax[w][c] = am;
+        for (int j = 0; j < NL; j++)
+            if (kw0 + 4 * (r + G * (j / 4)) + j % 4 < n) am[e] = fmaxf(am[e], fabsf(__fsub_rn(x[j][e], mu[e])));
     }
+#pragma unroll
+    for (int o = R; o < 64; o <<= 1)
+#pragma unroll
+        for (int e = 0; e < 8; e++) am[e] = fmaxf(am[e], __shfl_xor(am[e], o));
+    if (r == 0)
+#pragma unroll
+        for (int e = 0; e < 8; e++) pmax[w][8 * cc + e] = am[e];
     __syncthreads();
 #pragma unroll
-    for (int e = 0; e < CPL; e++) {
-        const int c = CPL * lane + e;
+    for (int e = 0; e < 8; e++) {
+        const int c = 8 * cc + e;
         const float A = fmaxf(fmaxf(pmax[0][c], pmax[1][c]), fmaxf(pmax[2][c], pmax[3][c]));
-        float s;
-        group_scale(A, mode, s, inv[e]);
-        const size_t gi = ((size_t)bh * nb + b) * D + c;
-        if (w == 0) {
+        float sc, inv;
+        group_scale(A, mode, sc, inv);
+        if (w == 0 && r == 0) {
+            const size_t gi = ((size_t)bh * nb + b) * D + c;
             vmean[gi] = mu[e];
-            vscale[gi] = s;
+            vscale[gi] = sc;
         }
-        uint8_t* out = tile + c * PITCH + 8 * w;
+        float y[NL];
 #pragma unroll
-        for (int bb = 0; bb < 4; bb++) {
-            // slots 32 bb + 8 w + j hold keys 32 w + 16 (j / 4) + 4 bb + j % 4
-            float y[8];
-#pragma unroll
-            for (int j = 0; j < 8; j++) {
-                const int i = 16 * (j / 4) + 4 * bb + j % 4;
-                y[j] = i < nw ? __fmul_rn(__fsub_rn(x[i][e], mu[e]), inv[e]) : 0.0f;  // padded slots: code 0
-            }
-            *reinterpret_cast<uint2*>(out + 32 * bb) =
-                make_uint2(e4m3_pk4(y[0], y[1], y[2], y[3]), e4m3_pk4(y[4], y[5], y[6], y[7]));
+        for (int j = 0; j < NL; j++) {
+            const bool ok = kw0 + 4 * (r + G * (j / 4)) + j % 4 < n;
+            y[j] = ok ? __fmul_rn(__fsub_rn(x[j][e], mu[e]), inv) : 0.0f;  // padded slots: code 0
         }
+        // quads r and r + G (D = 128) fill slots 32 r + 8 w .. + 7; quad r
+        // (D = 64) fills slots 32 (r % 4) + 8 w + 4 (r / 4) .. + 3
+        uint8_t* out = tile + c * PITCH + 32 * (r % 4) + 8 * w + 4 * (r / 4);
+        if (NL == 8)
+            *reinterpret_cast<uint2*>(out) = make_uint2(e4m3_pk4(y[0], y[1], y[2], y[3]),
+                                                        e4m3_pk4(y[4 % NL], y[5 % NL], y[6 % NL], y[7 % NL]));
+        else
+            *reinterpret_cast<uint32_t*>(out) = e4m3_pk4(y[0], y[1], y[2], y[3]);
     }
     // the block's D x 128 codes are contiguous in HBM: 16 bytes per lane
     __syncthreads();
@@ -269,9 +302,10 @@ __global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict
 // v_cvt_scalef32_pk_fp4_f32 (round to nearest even of x / 2^e, exact
 // scaling).  Output: codes [bh][nb][D][64] bytes, key kk of the block in
 // slot kk, slot 2 t in the low nibble of byte t; scales [bh][nb][D][4] bytes
-// e + 127.  The loads, the mean and the wave/key layout are those of
-// quant_v_kernel: wave w holds keys 32 w .. 32 w + 31, i.e. group w, so each
-// group's maximum stays inside one wave.
+// e + 127.  Wave w holds keys 32 w .. 32 w + 31, i.e. group w, so each
+// group's maximum stays inside one wave; lane l holds channels CPL l ..
+// CPL l + CPL - 1 (CPL = D / 64) of every key of its wave, one key row per
+// load across the wave.
 // ------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void quant_v4_kernel(const uint16_t* __restrict__ v,

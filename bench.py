@@ -366,7 +366,11 @@ def main():
         ablation["sage_per_channel"] = {"v_rel_err": float(sage_value_stats(SP, v)["v_rel_err"].mean())}
         del SP
 
-    clock = clock_under_load(lambda: api.attention(P, out=out), stream)
+    clock = clock_under_load(lambda: api.attention(P, out=out), stream, n=40)
+    ceiling = matrix_core_ceiling(stream)
+    print("matrix-core ceiling: %.0f TFLOP/s at %s MHz, %s W; attention at %s MHz, %s W"
+          % (ceiling["tflops"], ceiling["sclk_mhz"], ceiling["socket_power_w"], clock["sclk_mhz"],
+             clock["socket_power_w"]), file=sys.stderr, flush=True)
 
     # the other workloads: prepare (with and without k-means) and attention
     configs = None
@@ -406,6 +410,9 @@ def main():
                    "compute_units": torch.cuda.get_device_properties(0).multi_processor_count, **clock},
         "frac_fp8_peak_at_measured_clock": (attn_tflops / (FP8_PEAK_TFLOPS * clock["sclk_mhz"] / 2400.0)
                                             if clock.get("sclk_mhz") else None),
+        # the FP8 products alone (no memory traffic): what the matrix cores
+        # sustain on this machine, and the attention kernel's share of it
+        "matrix_core_ceiling": {**ceiling, "attention_frac_of_ceiling": attn_tflops / ceiling["tflops"]},
         "attention_other_v_scale_mode": {"v_scale_mode": 1 - args.v_scale_mode, "ms": other_ms,
                                          "tflops": flop / other_ms / 1e9,
                                          "frac_fp8_peak": flop / other_ms / 1e9 / FP8_PEAK_TFLOPS},
@@ -492,16 +499,17 @@ def time_config(c, ci, stream, reps=None):
 
 
 def clock_under_load(launch, stream, n=20):
-    """Shader clock and power cap read by rocm-smi while n attention launches
-    keep the GPU busy (queued first, so the reading falls inside them);
-    fields it could not read are None."""
+    """Shader clock and power cap (rocm-smi) and socket power (amd-smi) read
+    while n launches keep the GPU busy (queued first, so the readings fall
+    inside them); fields that could not be read are None."""
     import re
     import subprocess
 
     import torch
     for _ in range(n):
         launch()
-    info = {"sclk_mhz": None, "power_cap_w": None, "clock_source": "rocm-smi during %d attention launches" % n}
+    info = {"sclk_mhz": None, "power_cap_w": None, "socket_power_w": None,
+            "clock_source": "rocm-smi (clock, cap) and amd-smi (socket power) during %d launches" % n}
     try:
         # rocm-smi is a Python script: run it with this interpreter, not
         # through its "env python3" line, so no process in between replaces
@@ -519,10 +527,41 @@ def clock_under_load(launch, stream, n=20):
         m = re.search(r"Max Graphics Package Power \(W\):\s*([\d.]+)", txt, re.I)
         if m:
             info["power_cap_w"] = float(m.group(1))
+        amd = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
+        r = subprocess.run([sys.executable, amd, "metric", "--power"], capture_output=True, text=True, timeout=60)
+        m = re.search(r"SOCKET_POWER:\s*([\d.]+)", r.stdout)
+        if m:
+            info["socket_power_w"] = float(m.group(1))
     except (OSError, subprocess.SubprocessError):
         pass
     torch.cuda.synchronize()
     return info
+
+
+def matrix_core_ceiling(stream, blocks=1024, iters=5000, reps=40):
+    """FP8 rate, clock and socket power of the matrix cores alone: the
+    library's stream of independent 32x32x64 FP8 products from registers
+    (vc_debug_mfma_rate, no memory traffic), timed with HIP events on the
+    stream it runs on, then sampled like the attention kernel."""
+    import torch
+    from bit_attention_video_smooth_amd import _lib
+    out = torch.empty(blocks * 512, dtype=torch.float32, device="cuda")
+    launch = lambda: _lib.vc_debug_mfma_rate(blocks, iters, out, stream)
+    for _ in range(3):
+        launch()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        launch()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    flop = blocks * 8 * 4 * iters * 2 * 32 * 32 * 64
+    clock = clock_under_load(launch, stream, n=600)
+    return {"tflops": flop / ms / 1e9, "frac_fp8_peak": flop / ms / 1e9 / FP8_PEAK_TFLOPS,
+            "ms_per_launch": ms, "sclk_mhz": clock["sclk_mhz"], "socket_power_w": clock["socket_power_w"],
+            "kernel": "vc_debug_mfma_rate: %d workgroups x 8 waves x %d x 4 independent 32x32x64 FP8 products"
+                      % (blocks, iters)}
 
 
 def grouping_schedule(prep_ms, quant_ms, attn_ms, num_steps=40):

@@ -26,7 +26,7 @@ EXPORTS = ["vc_version", "vc_last_error", "vc_prepared_sizes", "vsmooth_workspac
            "vc_attention_fwd_dump",
            "vc_attention_fwd_bf16", "vc_sage_prepared_sizes", "vc_sage_workspace_bytes",
            "vc_sage_prepare", "vc_sage_attention_fwd", "vc_sage_attention_fwd_dump",
-           "vc_debug_expcast", "vc_debug_e4m3_encode", "vc_debug_mfma_fp8"]
+           "vc_debug_expcast", "vc_debug_e4m3_encode", "vc_debug_mfma_fp8", "vc_debug_mfma_rate"]
 
 VC_SAGE_QK_INT8 = 0
 VC_SAGE_QK_FP8 = 1
@@ -108,6 +108,7 @@ def load():
         L.vc_debug_expcast.argtypes = [P, P, P, i64, P, P]
         L.vc_debug_e4m3_encode.argtypes = [P, i64, P, P]
         L.vc_debug_mfma_fp8.argtypes = [P, P, P, i32, P]
+        L.vc_debug_mfma_rate.argtypes = [i32, i32, P, P]
         for n in EXPORTS:
             getattr(L, n).restype = ctypes.c_int if n != "vc_last_error" else ctypes.c_char_p
         _lib = L
@@ -243,3 +244,7 @@ def vc_debug_e4m3_encode(x, n, out, stream=None):
 
 def vc_debug_mfma_fp8(a, b, c, n_tiles, stream=None):
     _check(load().vc_debug_mfma_fp8(_ptr(a), _ptr(b), _ptr(c), n_tiles, _stream(stream)))
+
+
+def vc_debug_mfma_rate(blocks, iters, out, stream=None):
+    _check(load().vc_debug_mfma_rate(blocks, iters, _ptr(out), _stream(stream)))

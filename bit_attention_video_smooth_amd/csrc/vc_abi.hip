@@ -516,4 +516,12 @@ int vc_debug_mfma_fp8(const uint8_t* a, const uint8_t* b, float* c, int32_t n_ti
     return hip_status(vc::launch_debug_mfma_fp8(a, b, c, n_tiles, stream), "vc_debug_mfma_fp8");
 }
 
+int vc_debug_mfma_rate(int32_t blocks, int32_t iters, float* out, hipStream_t stream) {
+    if (blocks < 1 || blocks > (1 << 20)) return fail(VC_ERR_INVALID, "blocks=%d out of range [1, 2^20]", blocks);
+    if (iters < 1 || iters > (1 << 24)) return fail(VC_ERR_INVALID, "iters=%d out of range [1, 2^24]", iters);
+    int r;
+    if ((r = check_ptr(out, "out"))) return r;
+    return hip_status(vc::launch_debug_mfma_rate(blocks, iters, out, stream), "vc_debug_mfma_rate");
+}
+
 }  // extern "C"

@@ -1,6 +1,9 @@
 // vc_debug.hip -- checking aids: the ExpCast byte map and the E4M3 encoder
-// exactly as the production kernels use them, and one FP8 matrix-core
-// product per tile (to see how the hardware rounds a 128-term FP8 sum).
+// exactly as the production kernels use them, one FP8 matrix-core product
+// per tile (to see how the hardware rounds a 128-term FP8 sum), and a
+// stream of independent FP8 products with no memory traffic (the rate the
+// matrix cores sustain, and the clock and power they draw, when nothing else
+// runs).
 #include "vc_device.hpp"
 #include "vc_internal.hpp"
 
@@ -39,6 +42,30 @@ __global__ void debug_mfma_fp8_kernel(const uint8_t* __restrict__ A, const uint8
     for (int i = 0; i < 4; i++) C[((size_t)t * 16 + 4 * g + i) * 16 + r] = c[i];
 }
 
+// 8 waves per workgroup, each streaming 4 independent accumulations of
+// 32x32x64 FP8 products from registers for `iters` rounds; every lane then
+// writes the sum of its results, so no product is dead code.
+__global__ __launch_bounds__(512) void debug_mfma_rate_kernel(float* __restrict__ out, int iters) {
+    typedef float v16f __attribute__((ext_vector_type(16)));
+    v8i a, b;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {  // finite E4M3 codes: 0x38..0x3F and 0x30..0x37
+        a[i] = 0x38383838 ^ (int)((threadIdx.x & 7) * 0x01010101u);
+        b[i] = 0x30303030 + i * 0x01010101;
+    }
+    v16f c0 = {}, c1 = {}, c2 = {}, c3 = {};
+    for (int it = 0; it < iters; it++) {
+        c0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c0, 0, 0, 0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c1, 0, 0, 0, 0, 0, 0);
+        c2 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c2, 0, 0, 0, 0, 0, 0);
+        c3 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c3, 0, 0, 0, 0, 0, 0);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; e++) s += (c0[e] + c1[e]) + (c2[e] + c3[e]);
+    out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
 hipError_t launch_debug_expcast(const float* S, const float* c8, const float* krow, int64_t n,
                                 uint8_t* out, hipStream_t st) {
     if (n > 0)
@@ -51,6 +78,11 @@ hipError_t launch_debug_e4m3(const float* x, int64_t n, uint8_t* out, hipStream_
     if (n > 0)
         hipLaunchKernelGGL(debug_e4m3_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, x,
                            n, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_debug_mfma_rate(int blocks, int iters, float* out, hipStream_t st) {
+    hipLaunchKernelGGL(debug_mfma_rate_kernel, dim3(blocks), dim3(512), 0, st, out, iters);
     return hipGetLastError();
 }
 

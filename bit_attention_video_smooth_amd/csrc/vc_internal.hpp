@@ -106,6 +106,7 @@ hipError_t launch_debug_expcast(const float* S, const float* c8, const float* kr
 hipError_t launch_debug_e4m3(const float* x, int64_t n, uint8_t* out, hipStream_t st);
 hipError_t launch_debug_mfma_fp8(const uint8_t* a, const uint8_t* b, float* c, int n,
                                  hipStream_t st);
+hipError_t launch_debug_mfma_rate(int blocks, int iters, float* out, hipStream_t st);
 
 constexpr int ATTN_BM = 256;  // queries per workgroup of the attention kernels
 

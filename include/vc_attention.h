@@ -327,6 +327,17 @@ int vc_debug_e4m3_encode(const float* x, int64_t n, uint8_t* codes, hipStream_t 
 int vc_debug_mfma_fp8(const uint8_t* a, const uint8_t* b, float* c, int32_t n_tiles,
                       hipStream_t stream);
 
+/* The matrix-core rate with nothing else running: `blocks` workgroups of 8
+ * waves, each wave issuing 4 * iters independent 32x32x64 FP8 products
+ * (2 * 32 * 32 * 64 FLOP each) from registers, with no memory traffic until
+ * every lane writes one float of its results to out (device, caller-owned,
+ * blocks * 512 floats; the values carry no meaning).  Timing it gives the
+ * FP8 rate, clock and power the chip sustains on products alone, the
+ * ceiling against which the attention kernel's fraction of the published
+ * peak is read.  blocks in [1, 2^20], iters in [1, 2^24], else
+ * VC_ERR_INVALID.  A measurement aid. */
+int vc_debug_mfma_rate(int32_t blocks, int32_t iters, float* out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

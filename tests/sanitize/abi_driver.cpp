@@ -114,6 +114,9 @@ int main()
     EXPECT(vc_debug_expcast((const float*)M, (const float*)P, (const float*)P, 4, (uint8_t*)P, nullptr), VC_ERR_INVALID);
     EXPECT(vc_debug_e4m3_encode((const float*)P, 4, nullptr, nullptr), VC_ERR_INVALID);
     EXPECT(vc_debug_mfma_fp8((const uint8_t*)P, (const uint8_t*)P, (float*)P, -3, nullptr), VC_ERR_INVALID);
+    EXPECT(vc_debug_mfma_rate(0, 10, (float*)P, nullptr), VC_ERR_INVALID);
+    EXPECT(vc_debug_mfma_rate(16, 1 << 25, (float*)P, nullptr), VC_ERR_INVALID);
+    EXPECT(vc_debug_mfma_rate(16, 10, nullptr, nullptr), VC_ERR_INVALID);
 
     if (fails) {
         fprintf(stderr, "%d check(s) failed\n", fails);

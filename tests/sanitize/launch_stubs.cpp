@@ -17,4 +17,5 @@ hipError_t launch_attn_bf16(const AttnBf16Args&, int, int, hipStream_t) { return
 hipError_t launch_debug_expcast(const float*, const float*, const float*, int64_t, uint8_t*, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_debug_e4m3(const float*, int64_t, uint8_t*, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_debug_mfma_fp8(const uint8_t*, const uint8_t*, float*, int, hipStream_t) { return hipErrorNotSupported; }
+hipError_t launch_debug_mfma_rate(int, int, float*, hipStream_t) { return hipErrorNotSupported; }
 }  // namespace vc

@@ -148,6 +148,11 @@ def test_debug_entry_points_validate(lib):
     _lib.vc_debug_e4m3_encode(FAKE, 0, FAKE, 0)  # n == 0 is a no-op
     with pytest.raises(_lib.VCError):
         _lib.vc_debug_mfma_fp8(FAKE, 0, FAKE, 1, 0)
+    for blocks, iters, out in [(0, 10, FAKE), (1 << 21, 10, FAKE), (256, 0, FAKE), (256, 1 << 25, FAKE),
+                               (256, 10, 0)]:
+        with pytest.raises(_lib.VCError) as e:
+            _lib.vc_debug_mfma_rate(blocks, iters, out, 0)
+        assert e.value.code == _lib.VC_ERR_INVALID
 
 
 def _sprep(**over):

@@ -132,6 +132,20 @@ def test_fp8_matrix_core_sum_error_bound(api):
             assert frac == 1.0
 
 
+def test_mfma_rate_probe_runs(api):
+    # the bench's matrix-core ceiling: results are deterministic, finite and
+    # grow with the number of rounds (the values themselves carry no meaning)
+    from bit_attention_video_smooth_amd import _lib
+    outs = []
+    for iters in (1, 1, 3):
+        o = torch.empty(16 * 512, dtype=torch.float32, device="cuda")
+        _lib.vc_debug_mfma_rate(16, iters, o)
+        outs.append(o.cpu().numpy())
+    assert all(np.isfinite(o).all() for o in outs)
+    assert np.array_equal(outs[0], outs[1])
+    assert not np.array_equal(outs[0], outs[2])
+
+
 # -------------------------------------------------------------- prepare ----
 
 def _oracle_prep(q, k, v, perm, b, h, smooth_k=1, v_mode=0):

@@ -216,8 +216,9 @@ def main():
         bh, qt = (B * H) // 2, api.nblocks(L) // 4
         _, _, pb = api.attention_dump(P, bh, qt, skip_lambda=args.skip_lambda)
         _, _, pf = api.attention_dump(P, bh, qt)
-        live = pf.view(256, nb, 128).any(2)
-        rej = (~pb.view(256, nb, 128).any(2)) & live
+        # (any() of a uint8 tensor is uint8: compare first, so ~ is a logical not)
+        live = (pf.view(256, nb, 128) != 0).any(2)
+        rej = ~(pb.view(256, nb, 128) != 0).any(2) & live
         # a wave (32 query rows) skips a block's bytes and P V only when all
         # its rows reject it
         wlive = live.view(8, 32, nb).any(1)

@@ -367,7 +367,7 @@ def main():
         ablation["sage_per_channel"] = {"v_rel_err": float(sage_value_stats(SP, v)["v_rel_err"].mean())}
         del SP
 
-    clock = clock_under_load(lambda: api.attention(P, out=out), stream, n=40)
+    clock = clock_under_load(lambda: api.attention(P, out=out), stream, n=80)
     ceiling = matrix_core_ceiling(stream)
     print("matrix-core ceiling: %.0f TFLOP/s at %s MHz, %s W; attention at %s MHz, %s W"
           % (ceiling["tflops"], ceiling["sclk_mhz"], ceiling["socket_power_w"], clock["sclk_mhz"],
@@ -518,6 +518,13 @@ def clock_under_load(launch, stream, n=20):
         # exec would come after that process had opened the GPU)
         import shutil
         import sys
+        # socket power first: amd-smi reports a short running average, so it is
+        # read while the queued launches are certainly still running
+        amd = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
+        r = subprocess.run([sys.executable, amd, "metric", "--power"], capture_output=True, text=True, timeout=60)
+        m = re.search(r"SOCKET_POWER:\s*([\d.]+)", r.stdout)
+        if m:
+            info["socket_power_w"] = float(m.group(1))
         smi = shutil.which("rocm-smi") or "/opt/rocm/bin/rocm-smi"
         r = subprocess.run([sys.executable, smi, "--showclocks", "--showmaxpower"], capture_output=True, text=True,
                            timeout=30)
@@ -528,11 +535,6 @@ def clock_under_load(launch, stream, n=20):
         m = re.search(r"Max Graphics Package Power \(W\):\s*([\d.]+)", txt, re.I)
         if m:
             info["power_cap_w"] = float(m.group(1))
-        amd = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
-        r = subprocess.run([sys.executable, amd, "metric", "--power"], capture_output=True, text=True, timeout=60)
-        m = re.search(r"SOCKET_POWER:\s*([\d.]+)", r.stdout)
-        if m:
-            info["socket_power_w"] = float(m.group(1))
     except (OSError, subprocess.SubprocessError):
         pass
     torch.cuda.synchronize()
@@ -558,7 +560,7 @@ def matrix_core_ceiling(stream, blocks=1024, iters=5000, reps=40):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
     flop = blocks * 8 * 4 * iters * 2 * 32 * 32 * 64
-    clock = clock_under_load(launch, stream, n=600)
+    clock = clock_under_load(launch, stream, n=1200)
     return {"tflops": flop / ms / 1e9, "frac_fp8_peak": flop / ms / 1e9 / FP8_PEAK_TFLOPS,
             "ms_per_launch": ms, "sclk_mhz": clock["sclk_mhz"], "socket_power_w": clock["socket_power_w"],
             "kernel": "vc_debug_mfma_rate: %d workgroups x 8 waves x %d x 4 independent 32x32x64 FP8 products"

@@ -123,16 +123,28 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(const uint16_t* __restric
     const int i0 = b * BLK;
     const size_t Lp = (size_t)nb * BLK;
     const uint16_t* xb = x + (size_t)bh * L * D;
+    // Gather: the wave's rows are G w + r + G NCH j' ... (G = 64 / CPR rows per
+    // load instruction, r = lane / CPR): 32 permutation entries, one load by
+    // the lower half of the wave, handed to the chunks by lane exchanges
+    constexpr int G = 64 / CPR;
+    static_assert(G * NCH == 32, "32 rows per wave");
+    const int w = t >> 6, lane = t & 63;
+    int pv = 0;
+    if (GATHER) {
+        const int prow = G * w + lane % G + 256 / CPR * (lane / G);
+        if (lane < 32 && i0 + prow < L) pv = perm[(size_t)bh * L + i0 + prow];
+    }
     float vals[NCH][8];
     float amax = 0.0f;
 #pragma unroll
     for (int j = 0; j < NCH; j++) {
         const int ci = t + 256 * j, row = ci / CPR, cc = ci % CPR;
         const int slot = i0 + row;
+        const int psrc = GATHER ? __shfl(pv, lane / CPR + G * j) : 0;  // every lane takes part
         if (slot < L) {
-            const int src = GATHER ? perm[(size_t)bh * L + slot] : slot;
-            uint4 w = *reinterpret_cast<const uint4*>(xb + (size_t)src * D + cc * 8);
-            uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+            const int src = GATHER ? psrc : slot;
+            const uint4 u4 = *reinterpret_cast<const uint4*>(xb + (size_t)src * D + cc * 8);
+            uint32_t ww[4] = {u4.x, u4.y, u4.z, u4.w};
 #pragma unroll
             for (int e = 0; e < 4; e++) {
                 float lo = bf16_to_f32(ww[e] & 0xFFFFu), hi = bf16_to_f32(ww[e] >> 16);

@@ -93,6 +93,20 @@ def measured_traffic(workload):
         return None
 
 
+def skip_fractions(p_full, p_skip, nb):
+    """From the ExpCast bytes of one 256-query tile without and with Skip
+    Softmax ([256, nb*128] uint8): the fraction of (row, block) pairs that
+    have a nonzero byte without rejection and none with it, and the
+    fraction of (wave, block) pairs -- 32 rows, one matrix-core tile -- whose
+    rows all reject (the kernel skips bytes and P V only then)."""
+    # compare first: any() of a uint8 tensor is uint8, on which ~ is a bitwise not
+    live = (p_full.view(256, nb, 128) != 0).any(2)
+    rej = ~(p_skip.view(256, nb, 128) != 0).any(2) & live
+    wlive = live.view(8, 32, nb).any(1)
+    wrej = (rej | ~live).view(8, 32, nb).all(1) & wlive
+    return (float(rej.float().sum() / live.float().sum()), float(wrej.float().sum() / wlive.float().sum()))
+
+
 def copy_probe(mib):
     import torch
     n = (mib << 20) // 4
@@ -216,17 +230,11 @@ def main():
         bh, qt = (B * H) // 2, api.nblocks(L) // 4
         _, _, pb = api.attention_dump(P, bh, qt, skip_lambda=args.skip_lambda)
         _, _, pf = api.attention_dump(P, bh, qt)
-        # (any() of a uint8 tensor is uint8: compare first, so ~ is a logical not)
-        live = (pf.view(256, nb, 128) != 0).any(2)
-        rej = ~(pb.view(256, nb, 128) != 0).any(2) & live
-        # a wave (32 query rows) skips a block's bytes and P V only when all
-        # its rows reject it
-        wlive = live.view(8, 32, nb).any(1)
-        wrej = (rej | ~live).view(8, 32, nb).all(1) & wlive
+        row_frac, wave_frac = skip_fractions(pf, pb, nb)
         skip = {"lambda": args.skip_lambda, "ms": skip_ms, "speedup_vs_no_rejection": attn_ms / skip_ms,
                 "dense_equivalent_tflops": flop / skip_ms / 1e9,
-                "rejected_fraction_sample": float(rej.float().sum() / live.float().sum()),
-                "wave_rejected_fraction_sample": float(wrej.float().sum() / wlive.float().sum()),
+                "rejected_fraction_sample": row_frac,
+                "wave_rejected_fraction_sample": wave_frac,
                 "sample": "query tile %d of head %d (256 rows x %d blocks)" % (qt, bh, nb)}
         print("skip softmax lambda %g: %.3f ms" % (args.skip_lambda, skip_ms), file=sys.stderr, flush=True)
     bf16 = None

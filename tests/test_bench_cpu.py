@@ -51,3 +51,15 @@ def test_traffic_only_for_the_same_sources_and_workload(monkeypatch):
     assert bench.measured_traffic("tiny") is None
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 64)
     assert bench.measured_traffic(kv["workload"]) is None
+
+
+def test_skip_fractions_on_byte_dumps():
+    import torch
+    nb = 3
+    full = torch.ones((256, nb * 128), dtype=torch.uint8)
+    skip = full.clone()
+    skip[0:32, 128:256] = 0      # wave 0 rejects block 1 in every row
+    skip[32:40, 256:384] = 0     # 8 rows of wave 1 reject block 2
+    row, wave = bench.skip_fractions(full, skip, nb)
+    assert row == (32 + 8) / (256 * nb)
+    assert wave == 1 / (8 * nb)

@@ -61,5 +61,5 @@ def test_skip_fractions_on_byte_dumps():
     skip[0:32, 128:256] = 0      # wave 0 rejects block 1 in every row
     skip[32:40, 256:384] = 0     # 8 rows of wave 1 reject block 2
     row, wave = bench.skip_fractions(full, skip, nb)
-    assert row == (32 + 8) / (256 * nb)
-    assert wave == 1 / (8 * nb)
+    assert row == pytest.approx((32 + 8) / (256 * nb), rel=1e-6)
+    assert wave == pytest.approx(1 / (8 * nb), rel=1e-6)

@@ -249,9 +249,11 @@ def main():
         ev[1].record(stream)
         torch.cuda.synchronize()
         bf16_ms = ev[0].elapsed_time(ev[1]) / n16
+        bclock = clock_under_load(lambda: api.attention_bf16(q, k, v, out=ob), stream, n=48)
         bf16 = {"ms": bf16_ms, "tflops": flop / bf16_ms / 1e9,
                 "frac_bf16_peak": flop / bf16_ms / 1e9 / BF16_PEAK_TFLOPS,
-                "fp8_speedup_over_bf16": bf16_ms / attn_ms}
+                "fp8_speedup_over_bf16": bf16_ms / attn_ms,
+                "sclk_mhz": bclock["sclk_mhz"], "socket_power_w": bclock["socket_power_w"]}
         print("bf16 attention %.3f ms" % bf16_ms, file=sys.stderr, flush=True)
 
     # the FP8 path ExpCast replaces (fp32 exp2, then the E4M3 conversion), on

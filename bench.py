@@ -219,24 +219,29 @@ def main():
     # bytes are all zero with rejection but not without)
     skip = None
     if args.skip_lambda > 0:
-        api.attention(P, out=out, skip_lambda=args.skip_lambda)
-        torch.cuda.synchronize()
-        ev[0].record(stream)
-        for _ in range(args.steps):
-            api.attention(P, out=out, skip_lambda=args.skip_lambda)
-        ev[1].record(stream)
-        torch.cuda.synchronize()
-        skip_ms = ev[0].elapsed_time(ev[1]) / args.steps
         bh, qt = (B * H) // 2, api.nblocks(L) // 4
-        _, _, pb = api.attention_dump(P, bh, qt, skip_lambda=args.skip_lambda)
         _, _, pf = api.attention_dump(P, bh, qt)
-        row_frac, wave_frac = skip_fractions(pf, pb, nb)
-        skip = {"lambda": args.skip_lambda, "ms": skip_ms, "speedup_vs_no_rejection": attn_ms / skip_ms,
-                "dense_equivalent_tflops": flop / skip_ms / 1e9,
-                "rejected_fraction_sample": row_frac,
-                "wave_rejected_fraction_sample": wave_frac,
-                "sample": "query tile %d of head %d (256 rows x %d blocks)" % (qt, bh, nb)}
-        print("skip softmax lambda %g: %.3f ms" % (args.skip_lambda, skip_ms), file=sys.stderr, flush=True)
+
+        def skip_run(lam, n):
+            api.attention(P, out=out, skip_lambda=lam)
+            torch.cuda.synchronize()
+            ev[0].record(stream)
+            for _ in range(n):
+                api.attention(P, out=out, skip_lambda=lam)
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            ms = ev[0].elapsed_time(ev[1]) / n
+            _, _, pb = api.attention_dump(P, bh, qt, skip_lambda=lam)
+            row_frac, wave_frac = skip_fractions(pf, pb, nb)
+            return {"lambda": lam, "ms": ms, "speedup_vs_no_rejection": attn_ms / ms,
+                    "rejected_fraction_sample": row_frac, "wave_rejected_fraction_sample": wave_frac}
+
+        skip = skip_run(args.skip_lambda, args.steps)
+        skip.update({"dense_equivalent_tflops": flop / skip["ms"] / 1e9,
+                     "sample": "query tile %d of head %d (256 rows x %d blocks)" % (qt, bh, nb),
+                     # the threshold's range: a few launches each
+                     "sweep": [skip_run(lam, max(2, args.steps // 4)) for lam in (0.05, 0.3, 0.9)]})
+        print("skip softmax lambda %g: %.3f ms" % (args.skip_lambda, skip["ms"]), file=sys.stderr, flush=True)
     bf16 = None
     if not args.no_bf16:
         ob = torch.empty((B, H, L, d), dtype=torch.float32, device="cuda")

@@ -8,13 +8,15 @@
 // "Sparse Attention with Skip Softmax").  The same workgroup, LDS ring, copy
 // schedule and wave-group offset; only the wave's tiling differs.
 //
-// Why the larger product: on gfx950 a matrix-core instruction holds the
-// vector issue of its SIMD for about 16 cycles whatever its size, and the
-// kernel is bound by that issue port (products plus the softmax and
-// epilogue vector work of both waves of a SIMD).  A 32x32x64 FP8 product
+// Why the larger product: a matrix-core instruction holds the vector issue
+// of its SIMD for about 16 cycles whatever its size; a 32x32x64 FP8 product
 // does twice the work of a 16x16x128 one in 64 cycles and leaves about 12
-// vector instructions free beside it, against about 4 for the 16x16x128
-// form (measured), so the same block needs half the product issue slots.
+// vector instructions free beside it, against about 4 (measured), so a
+// block takes half the product instructions, and at d = 64 the scores are
+// one full k = 64 step instead of a half-empty 128-deep one.  (On the chip
+// both forms run at the same speed at d = 128: under this kernel the part
+// sits at its power limit, and the time follows the energy of the work --
+// products, LDS operand reads, copies -- more than its issue schedule.)
 //
 // Lane layout of a 32x32x64 product: A row m = lane % 32 and B column
 // n = lane % 32 take k bytes 32 (lane / 32) .. + 31 of the k-step; the 16
@@ -23,8 +25,9 @@
 // the row max needs one cross-lane swap.  The K rows are placed in LDS
 // (Fp8Loader<D, REC_VC, true>) so that lane half h's scores of key tiles
 // 2 s and 2 s + 1 are exactly the keys of V slots 64 s + 32 h .. + 31, i.e.
-// its ExpCast bytes are its B operand of k-step s of O^T = V8^T P^T, in the
-// slot order the preparation writes the V codes in (vkey_of_slot).
+// its ExpCast bytes are its A operand (row = its query) of k-step s of
+// O = P8 V8, in the slot order the preparation writes the V codes in
+// (vkey_of_slot).
 #pragma once
 
 #include "vc_attn_fp8_kernel.hpp"

@@ -134,31 +134,43 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(const uint16_t* __restric
         const int prow = G * w + lane % G + 256 / CPR * (lane / G);
         if (lane < 32 && i0 + prow < L) pv = perm[(size_t)bh * L + i0 + prow];
     }
+    // every row load is issued before any value is used: rows past the head
+    // (slot >= L) load a valid row (the last one, or row 0 through a zero
+    // permutation entry) and are zeroed afterwards, so no load sits behind a
+    // branch that the compiler would close with a wait
+    const int cc = t % CPR;  // the same chunk column for every j (256 % CPR == 0)
+    float kb8[8];
+    if (GATHER) {
+        const float4 k0 = *reinterpret_cast<const float4*>(kbar + (size_t)bh * D + cc * 8);
+        const float4 k1 = *reinterpret_cast<const float4*>(kbar + (size_t)bh * D + cc * 8 + 4);
+        kb8[0] = k0.x; kb8[1] = k0.y; kb8[2] = k0.z; kb8[3] = k0.w;
+        kb8[4] = k1.x; kb8[5] = k1.y; kb8[6] = k1.z; kb8[7] = k1.w;
+    }
+    uint4 raw[NCH];
+#pragma unroll
+    for (int j = 0; j < NCH; j++) {
+        const int row = (t + 256 * j) / CPR;
+        const int slot = i0 + row;
+        const int psrc = GATHER ? __shfl(pv, lane / CPR + G * j) : 0;  // every lane takes part
+        const int src = GATHER ? psrc : min(slot, L - 1);
+        raw[j] = *reinterpret_cast<const uint4*>(xb + (size_t)src * D + cc * 8);
+    }
     float vals[NCH][8];
     float amax = 0.0f;
 #pragma unroll
     for (int j = 0; j < NCH; j++) {
-        const int ci = t + 256 * j, row = ci / CPR, cc = ci % CPR;
-        const int slot = i0 + row;
-        const int psrc = GATHER ? __shfl(pv, lane / CPR + G * j) : 0;  // every lane takes part
-        if (slot < L) {
-            const int src = GATHER ? psrc : slot;
-            const uint4 u4 = *reinterpret_cast<const uint4*>(xb + (size_t)src * D + cc * 8);
-            uint32_t ww[4] = {u4.x, u4.y, u4.z, u4.w};
+        const bool ok = i0 + (t + 256 * j) / CPR < L;
+        const uint32_t ww[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-                float lo = bf16_to_f32(ww[e] & 0xFFFFu), hi = bf16_to_f32(ww[e] >> 16);
-                if (GATHER) {
-                    lo = __fsub_rn(lo, kbar[(size_t)bh * D + cc * 8 + 2 * e]);
-                    hi = __fsub_rn(hi, kbar[(size_t)bh * D + cc * 8 + 2 * e + 1]);
-                }
-                vals[j][2 * e] = lo;
-                vals[j][2 * e + 1] = hi;
-                amax = fmaxf(amax, fmaxf(fabsf(lo), fabsf(hi)));
+        for (int e = 0; e < 4; e++) {
+            float lo = bf16_to_f32(ww[e] & 0xFFFFu), hi = bf16_to_f32(ww[e] >> 16);
+            if (GATHER) {
+                lo = __fsub_rn(lo, kb8[2 * e]);
+                hi = __fsub_rn(hi, kb8[2 * e + 1]);
             }
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; e++) vals[j][e] = 0.0f;
+            vals[j][2 * e] = ok ? lo : 0.0f;
+            vals[j][2 * e + 1] = ok ? hi : 0.0f;
+            amax = fmaxf(amax, fmaxf(fabsf(vals[j][2 * e]), fabsf(vals[j][2 * e + 1])));
         }
     }
     const float A = block_max_256(amax, red4);
@@ -189,9 +201,11 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(const uint16_t* __restric
 // keys 4 g .. 4 g + 3 of wave w fill slots 32 (g % 4) + 8 w + 4 (g / 4) + i
 // of every channel row.  Per-channel fp64 sums (exact for bf16 inputs, so
 // the order does not matter) and maxima are combined over the lanes of one
-// chunk with cross-lane exchanges and over the four waves through LDS.  The
-// codes are assembled channel-major in an LDS tile, and the block's D x 128
-// bytes, contiguous in HBM, leave as 16-byte stores.
+// chunk with cross-lane exchanges and over the four waves through LDS; one
+// thread per channel then forms the mean and the scale, which the lanes read
+// back.  All row loads are issued before any is used.  The codes are
+// assembled channel-major in an LDS tile, and the block's D x 128 bytes,
+// contiguous in HBM, leave as 16-byte stores.
 template <int D>
 __global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict__ v,
                                                       const int32_t* __restrict__ perm,
@@ -206,6 +220,8 @@ __global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict
     static_assert(NL % 4 == 0, "whole key quads per lane");
     __shared__ double psum[4][D];
     __shared__ float pmax[4][D];
+    __shared__ __attribute__((aligned(16))) float cmu[D];
+    __shared__ __attribute__((aligned(16))) float cinv[D];
     __shared__ __attribute__((aligned(16))) uint8_t tile[D * PITCH];
     const int b = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63;
@@ -217,30 +233,33 @@ __global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict
     int pv = 0;
     if (lane < 32 && kw0 + lane < n) pv = perm[(size_t)bh * L + i0 + kw0 + lane];
     const uint16_t* vb = v + (size_t)bh * L * D + 8 * cc;
-    float x[NL][8];
+    // the raw bf16 rows (half the registers of their fp32 values; the
+    // conversion is a shift or a mask, repeated where a value is used)
+    uint32_t xr[NL][4];
 #pragma unroll
     for (int j = 0; j < NL; j++) {
         const int kl = 4 * (r + G * (j / 4)) + j % 4;  // key within the wave
         const int src = __shfl(pv, kl);
-        if (kw0 + kl < n) {
-            const uint4 u = *reinterpret_cast<const uint4*>(vb + (size_t)src * D);
-            const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                x[j][2 * e] = bf16_to_f32(uu[e] & 0xFFFFu);
-                x[j][2 * e + 1] = bf16_to_f32(uu[e] >> 16);
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; e++) x[j][e] = 0.0f;
-        }
+        // padded keys: entry 0, a valid row, zeroed once all loads are out
+        const uint4 u = *reinterpret_cast<const uint4*>(vb + (size_t)src * D);
+        xr[j][0] = u.x; xr[j][1] = u.y; xr[j][2] = u.z; xr[j][3] = u.w;
     }
+#pragma unroll
+    for (int j = 0; j < NL; j++) {
+        const bool ok = kw0 + 4 * (r + G * (j / 4)) + j % 4 < n;
+#pragma unroll
+        for (int i = 0; i < 4; i++) xr[j][i] = ok ? xr[j][i] : 0u;
+    }
+    auto X = [&](int j, int e) -> float {
+        const uint32_t wv = xr[j][e / 2];
+        return __uint_as_float((e & 1) ? (wv & 0xFFFF0000u) : (wv << 16));
+    };
     double s[8];
 #pragma unroll
     for (int e = 0; e < 8; e++) {
         s[e] = 0.0;
 #pragma unroll
-        for (int j = 0; j < NL; j++) s[e] += (double)x[j][e];  // padded keys add 0
+        for (int j = 0; j < NL; j++) s[e] += (double)X(j, e);  // padded keys add 0
     }
 #pragma unroll
     for (int o = R; o < 64; o <<= 1)
@@ -250,15 +269,31 @@ __global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict
 #pragma unroll
         for (int e = 0; e < 8; e++) psum[w][8 * cc + e] = s[e];
     __syncthreads();
+    // one thread per channel: the block mean (and, below, the scale), so
+    // each is formed once and the lanes read them back
+    const size_t g0 = ((size_t)bh * nb + b) * D;
+    if (t < D) {
+        const float m = (float)((((psum[0][t] + psum[1][t]) + psum[2][t]) + psum[3][t]) / (double)n);
+        cmu[t] = m;
+        vmean[g0 + t] = m;
+    }
+    __syncthreads();
     float mu[8], am[8];
+    {
+        const float4 m0 = *reinterpret_cast<const float4*>(cmu + 8 * cc);
+        const float4 m1 = *reinterpret_cast<const float4*>(cmu + 8 * cc + 4);
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            mu[e] = (&m0.x)[e];
+            mu[e + 4] = (&m1.x)[e];
+        }
+    }
 #pragma unroll
     for (int e = 0; e < 8; e++) {
-        const int c = 8 * cc + e;
-        mu[e] = (float)((((psum[0][c] + psum[1][c]) + psum[2][c]) + psum[3][c]) / (double)n);
         am[e] = 0.0f;
 #pragma unroll
         for (int j = 0; j < NL; j++)
-            if (kw0 + 4 * (r + G * (j / 4)) + j % 4 < n) am[e] = fmaxf(am[e], fabsf(__fsub_rn(x[j][e], mu[e])));
+            if (kw0 + 4 * (r + G * (j / 4)) + j % 4 < n) am[e] = fmaxf(am[e], fabsf(__fsub_rn(X(j, e), mu[e])));
     }
 #pragma unroll
     for (int o = R; o < 64; o <<= 1)
@@ -268,22 +303,32 @@ __global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict
 #pragma unroll
         for (int e = 0; e < 8; e++) pmax[w][8 * cc + e] = am[e];
     __syncthreads();
+    if (t < D) {
+        const float A = fmaxf(fmaxf(pmax[0][t], pmax[1][t]), fmaxf(pmax[2][t], pmax[3][t]));
+        float sc, iv;
+        group_scale(A, mode, sc, iv);
+        cinv[t] = iv;
+        vscale[g0 + t] = sc;
+    }
+    __syncthreads();
+    float inv[8];
+    {
+        const float4 i0v = *reinterpret_cast<const float4*>(cinv + 8 * cc);
+        const float4 i1v = *reinterpret_cast<const float4*>(cinv + 8 * cc + 4);
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            inv[e] = (&i0v.x)[e];
+            inv[e + 4] = (&i1v.x)[e];
+        }
+    }
 #pragma unroll
     for (int e = 0; e < 8; e++) {
         const int c = 8 * cc + e;
-        const float A = fmaxf(fmaxf(pmax[0][c], pmax[1][c]), fmaxf(pmax[2][c], pmax[3][c]));
-        float sc, inv;
-        group_scale(A, mode, sc, inv);
-        if (w == 0 && r == 0) {
-            const size_t gi = ((size_t)bh * nb + b) * D + c;
-            vmean[gi] = mu[e];
-            vscale[gi] = sc;
-        }
         float y[NL];
 #pragma unroll
         for (int j = 0; j < NL; j++) {
             const bool ok = kw0 + 4 * (r + G * (j / 4)) + j % 4 < n;
-            y[j] = ok ? __fmul_rn(__fsub_rn(x[j][e], mu[e]), inv) : 0.0f;  // padded slots: code 0
+            y[j] = ok ? __fmul_rn(__fsub_rn(X(j, e), mu[e]), inv[e]) : 0.0f;  // padded slots: code 0
         }
         // quads r and r + G (D = 128) fill slots 32 r + 8 w .. + 7; quad r
         // (D = 64) fills slots 32 (r % 4) + 8 w + 4 (r / 4) .. + 3
@@ -337,24 +382,27 @@ __global__ __launch_bounds__(256) void quant_v4_kernel(const uint16_t* __restric
     const int i0 = b * BLK;
     const int n = min(BLK, L - i0);
     const uint16_t* vb = v + (size_t)bh * L * D + CPL * lane;
-    const int32_t* pb = perm + (size_t)bh * L + i0 + KW * w;
     const int nw = min(KW, max(0, n - KW * w));
+    // the wave's 32 permutation entries, one per lane of its lower half
+    // (padded keys: entry 0, a valid row); every row load is issued before
+    // any is used, and padded keys are zeroed afterwards
+    int pv = 0;
+    if (lane < KW && lane < nw) pv = perm[(size_t)bh * L + i0 + KW * w + lane];
+    uint32_t raw[KW];
+#pragma unroll
+    for (int i = 0; i < KW; i++) {
+        const int src = __shfl(pv, i);
+        if (CPL == 2)
+            raw[i] = *reinterpret_cast<const uint32_t*>(vb + (size_t)src * D);
+        else
+            raw[i] = vb[(size_t)src * D];
+    }
     float x[KW][CPL];
 #pragma unroll
     for (int i = 0; i < KW; i++) {
-        if (i < nw) {
-            const int src = pb[i];
-            if (CPL == 2) {
-                const uint32_t u = *reinterpret_cast<const uint32_t*>(vb + (size_t)src * D);
-                x[i][0] = bf16_to_f32(u & 0xFFFFu);
-                x[i][CPL - 1] = bf16_to_f32(u >> 16);
-            } else {
-                x[i][0] = bf16_to_f32(vb[(size_t)src * D]);
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < CPL; e++) x[i][e] = 0.0f;
-        }
+        const uint32_t u = i < nw ? raw[i] : 0u;
+        x[i][0] = bf16_to_f32(u & 0xFFFFu);
+        if (CPL == 2) x[i][CPL - 1] = bf16_to_f32(u >> 16);
     }
 #pragma unroll
     for (int e = 0; e < CPL; e++) {

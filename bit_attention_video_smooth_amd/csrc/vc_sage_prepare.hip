@@ -101,18 +101,27 @@ __global__ __launch_bounds__(256) void sage_quant_k_kernel(const uint16_t* __res
     const int grp = blockIdx.x * 4 + w;
     const int row = grp * 16 + lane / 4;
     const int c0 = (lane % 4) * (D / 4);
+    // every load is issued before any value is used: a padded row loads the
+    // head's last row and is zeroed afterwards (code 0, no part in the amax)
+    const bool ok = row < L;
+    const size_t src = (size_t)bh * L + min(row, L - 1);
+    uint4 raw[NC];
+    float kb[NC][8];
+#pragma unroll
+    for (int j = 0; j < NC; j++) {
+        raw[j] = *reinterpret_cast<const uint4*>(k + src * D + c0 + 8 * j);
+        const float4 k0 = *reinterpret_cast<const float4*>(kbar + (size_t)bh * D + c0 + 8 * j);
+        const float4 k1 = *reinterpret_cast<const float4*>(kbar + (size_t)bh * D + c0 + 8 * j + 4);
+        kb[j][0] = k0.x; kb[j][1] = k0.y; kb[j][2] = k0.z; kb[j][3] = k0.w;
+        kb[j][4] = k1.x; kb[j][5] = k1.y; kb[j][6] = k1.z; kb[j][7] = k1.w;
+    }
     float x[NC][8];
     float A = 0.0f;
 #pragma unroll
     for (int j = 0; j < NC; j++) {
-        if (row < L) {
-            unpack8(*reinterpret_cast<const uint4*>(k + ((size_t)bh * L + row) * D + c0 + 8 * j), x[j]);
+        unpack8(raw[j], x[j]);
 #pragma unroll
-            for (int e = 0; e < 8; e++) x[j][e] = __fsub_rn(x[j][e], kbar[(size_t)bh * D + c0 + 8 * j + e]);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; e++) x[j][e] = 0.0f;  // padded rows: code 0, no part in the amax
-        }
+        for (int e = 0; e < 8; e++) x[j][e] = ok ? __fsub_rn(x[j][e], kb[j][e]) : 0.0f;
 #pragma unroll
         for (int e = 0; e < 8; e++) A = fmaxf(A, fabsf(x[j][e]));
     }
@@ -185,22 +194,24 @@ __global__ __launch_bounds__(256) void sage_quant_v_kernel(const uint16_t* __res
     const int w = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63;
     const int i0 = b * BLK + KW * w;
     const int nw = min(KW, max(0, L - i0));  // valid keys of this wave
-    const uint16_t* vb = v + ((size_t)bh * L + i0) * D + CPL * lane;
+    const uint16_t* vb = v + (size_t)bh * L * D + CPL * lane;
+    // every row load is issued before any is used: rows past the head load
+    // the last row and are zeroed afterwards
+    uint32_t raw[KW];
+#pragma unroll
+    for (int i = 0; i < KW; i++) {
+        const size_t row = (size_t)min(i0 + i, L - 1);
+        if (CPL == 2)
+            raw[i] = *reinterpret_cast<const uint32_t*>(vb + row * D);
+        else
+            raw[i] = vb[row * D];
+    }
     float x[KW][CPL];
 #pragma unroll
     for (int i = 0; i < KW; i++) {
-        if (i < nw) {
-            if (CPL == 2) {
-                const uint32_t u = *reinterpret_cast<const uint32_t*>(vb + (size_t)i * D);
-                x[i][0] = bf16_to_f32(u & 0xFFFFu);
-                x[i][CPL - 1] = bf16_to_f32(u >> 16);
-            } else {
-                x[i][0] = bf16_to_f32(vb[(size_t)i * D]);
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < CPL; e++) x[i][e] = 0.0f;
-        }
+        const uint32_t u = i < nw ? raw[i] : 0u;
+        x[i][0] = bf16_to_f32(u & 0xFFFFu);
+        if (CPL == 2) x[i][CPL - 1] = bf16_to_f32(u >> 16);
     }
 #pragma unroll
     for (int e = 0; e < CPL; e++) {

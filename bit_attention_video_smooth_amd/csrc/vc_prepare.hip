@@ -76,6 +76,11 @@ __global__ void k_mean_finalize(const double* __restrict__ partial, float* __res
     kbar[(size_t)bh * D + c] = smooth ? (float)(s / (double)L) : 0.0f;
 }
 
+// A permutation entry as a row index: entries outside 0 .. L-1 (a caller's
+// perm_in that is not a permutation) are clamped, so a gather never reads
+// outside its head; the codes are then unspecified.
+__device__ __forceinline__ int clamp_row(int r, int L) { return min(max(r, 0), L - 1); }
+
 // Scale of a quantisation group from its amax A (same rule for every group):
 // mode 0: s = fp32(A / 448), inv = fp32(448 / A); mode 1: s = 2^e with e the
 // least integer such that A <= 448 * 2^e, inv = 2^-e.  A < 2^-100: both 0.
@@ -132,7 +137,7 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(const uint16_t* __restric
     int pv = 0;
     if (GATHER) {
         const int prow = G * w + lane % G + 256 / CPR * (lane / G);
-        if (lane < 32 && i0 + prow < L) pv = perm[(size_t)bh * L + i0 + prow];
+        if (lane < 32 && i0 + prow < L) pv = clamp_row(perm[(size_t)bh * L + i0 + prow], L);
     }
     // every row load is issued before any value is used: rows past the head
     // (slot >= L) load a valid row (the last one, or row 0 through a zero
@@ -231,7 +236,7 @@ __global__ __launch_bounds__(256) void quant_v_kernel(const uint16_t* __restrict
     const int kw0 = 32 * w;  // the wave's first key within the block
     // the wave's 32 permutation entries, one per lane of its lower half
     int pv = 0;
-    if (lane < 32 && kw0 + lane < n) pv = perm[(size_t)bh * L + i0 + kw0 + lane];
+    if (lane < 32 && kw0 + lane < n) pv = clamp_row(perm[(size_t)bh * L + i0 + kw0 + lane], L);
     const uint16_t* vb = v + (size_t)bh * L * D + 8 * cc;
     // the raw bf16 rows (half the registers of their fp32 values; the
     // conversion is a shift or a mask, repeated where a value is used)
@@ -387,7 +392,7 @@ __global__ __launch_bounds__(256) void quant_v4_kernel(const uint16_t* __restric
     // (padded keys: entry 0, a valid row); every row load is issued before
     // any is used, and padded keys are zeroed afterwards
     int pv = 0;
-    if (lane < KW && lane < nw) pv = perm[(size_t)bh * L + i0 + KW * w + lane];
+    if (lane < KW && lane < nw) pv = clamp_row(perm[(size_t)bh * L + i0 + KW * w + lane], L);
     uint32_t raw[KW];
 #pragma unroll
     for (int i = 0; i < KW; i++) {

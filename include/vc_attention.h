@@ -133,7 +133,9 @@ int vsmooth_workspace_bytes(const vc_shape* shape, const vsmooth_params* params,
  * q, k, v: bf16 [B,H,L,d].  perm_in: NULL or int32 [B,H,L] (each row a
  * permutation of 0..L-1; copied to out->perm; it may be out->perm itself,
  * to keep the permutation of an earlier call across denoising steps, as the
- * MarkTechPost abstract describes).  ws: ws_bytes >=
+ * MarkTechPost abstract describes; it is not checked: entries outside
+ * 0..L-1 are clamped into that range when rows are gathered, so no memory
+ * outside the head is read, and the codes are then unspecified).  ws: ws_bytes >=
  * vsmooth_workspace_bytes().  Padded slots (>= L) get code 0. */
 int vsmooth_prepare(const vc_shape* shape, const vsmooth_params* params, const void* q,
                     const void* k, const void* v, const int32_t* perm_in,

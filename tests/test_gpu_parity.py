@@ -573,3 +573,31 @@ def test_attention_single_partial_block(api):
     perm = synth.random_perms(B, H, L, 94)
     P = api.prepare(dev_bf16(q), dev_bf16(k), dev_bf16(v), perm_in=torch.from_numpy(perm).cuda())
     _check_attention(api, P, q, k, v, perm, 8, 0, "attention L=127")
+
+
+def test_prepare_clamps_permutation_entries(api):
+    """perm_in is not checked on the host; entries outside 0..L-1 are clamped
+    where rows are gathered.  A row with out-of-range entries gives exactly
+    the codes of its clamped copy (8- and 4-bit residuals), i.e. every gather
+    stayed inside the head."""
+    B, H, L, d = 1, 2, 300, 128
+    q, k, v = _inputs(B, H, L, d, 95, None)
+    perm = synth.random_perms(B, H, L, 96)
+    bad = perm.copy()
+    bad[0, 0, 3] = -7
+    bad[0, 1, 150] = L + 11
+    bad[0, 1, 299] = 2 ** 30
+    clamped = np.clip(bad, 0, L - 1).astype(np.int32)
+    qd, kd, vd = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    for v_format in (0, 1):
+        pb = api.prepare(qd, kd, vd, perm_in=torch.from_numpy(bad).cuda(), v_format=v_format)
+        pc = api.prepare(qd, kd, vd, perm_in=torch.from_numpy(clamped).cuda(), v_format=v_format)
+        torch.cuda.synchronize()
+        for name in ("q8", "k8", "v8", "q_scale", "k_scale", "v_scale", "v_mean"):
+            x, y = getattr(pb, name).reshape(-1), getattr(pc, name).reshape(-1)
+            if name == "v8" and v_format == 1:
+                # the 4-bit residual fills the first half of the buffer
+                n4 = B * H * ((L + 127) // 128) * d * 64
+                x, y = x[:n4], y[:n4]
+            assert torch.equal(x, y), (v_format, name)
+        assert torch.equal(pb.perm.cpu(), torch.from_numpy(bad).reshape(pb.perm.shape)), "perm_in is copied as given"

@@ -288,10 +288,21 @@ __global__ __launch_bounds__(1024) void km_scan(int32_t* __restrict__ cnt, int32
     // cluster totals; each thread owns a contiguous range of clusters
     const int per = (k + 1023) / 1024;
     const int c0 = t * per, c1 = min(k, c0 + per);
+    // (the chunk loops take eight entries per step, all loads issued before
+    // their use, so they do not wait on one load at a time)
+    constexpr int U = 8;
     int local = 0;
     for (int c = c0; c < c1; c++) {
         int s = 0;
-        for (int ch = 0; ch < nchunk; ch++) s += base[(size_t)ch * k + c];
+        int ch = 0;
+        for (; ch + U <= nchunk; ch += U) {
+            int x[U];
+#pragma unroll
+            for (int u = 0; u < U; u++) x[u] = base[(size_t)(ch + u) * k + c];
+#pragma unroll
+            for (int u = 0; u < U; u++) s += x[u];
+        }
+        for (; ch < nchunk; ch++) s += base[(size_t)ch * k + c];
         counts[(size_t)bh * k + c] = s;
         local += s;
     }
@@ -307,7 +318,18 @@ __global__ __launch_bounds__(1024) void km_scan(int32_t* __restrict__ cnt, int32
     int run = part[t] - local;
     for (int c = c0; c < c1; c++) {
         starts[(size_t)bh * k + c] = run;
-        for (int ch = 0; ch < nchunk; ch++) {
+        int ch = 0;
+        for (; ch + U <= nchunk; ch += U) {
+            int x[U];
+#pragma unroll
+            for (int u = 0; u < U; u++) x[u] = base[(size_t)(ch + u) * k + c];
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                base[(size_t)(ch + u) * k + c] = run;
+                run += x[u];
+            }
+        }
+        for (; ch < nchunk; ch++) {
             const int x = base[(size_t)ch * k + c];
             base[(size_t)ch * k + c] = run;
             run += x;

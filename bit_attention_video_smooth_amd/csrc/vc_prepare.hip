@@ -70,9 +70,22 @@ __global__ void k_mean_finalize(const double* __restrict__ partial, float* __res
                                 int nsplit, int smooth) {
     const int bh = blockIdx.x, c = threadIdx.x;
     if (c >= D) return;
+    // eight partials per step, loaded before they are added (the same order
+    // of additions; fp64 sums of bf16 data are exact in any order anyway)
+    constexpr int U = 8;
     double s = 0.0;
-    if (smooth)
-        for (int i = 0; i < nsplit; i++) s += partial[((size_t)bh * nsplit + i) * D + c];
+    if (smooth) {
+        const double* p = partial + (size_t)bh * nsplit * D + c;
+        int i = 0;
+        for (; i + U <= nsplit; i += U) {
+            double x[U];
+#pragma unroll
+            for (int u = 0; u < U; u++) x[u] = p[(size_t)(i + u) * D];
+#pragma unroll
+            for (int u = 0; u < U; u++) s += x[u];
+        }
+        for (; i < nsplit; i++) s += p[(size_t)i * D];
+    }
     kbar[(size_t)bh * D + c] = smooth ? (float)(s / (double)L) : 0.0f;
 }
 

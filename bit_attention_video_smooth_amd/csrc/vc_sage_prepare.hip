@@ -148,11 +148,20 @@ __global__ __launch_bounds__(256) void v_absmax_partial(const uint16_t* __restri
     float m[8];
 #pragma unroll
     for (int e = 0; e < 8; e++) m[e] = 0.0f;
-    for (int r = r0 + rs; r < r1; r += RPI) {
-        float x[8];
-        unpack8(*reinterpret_cast<const uint4*>(v + ((size_t)bh * L + r) * D + cc * 8), x);
+    // four rows per thread in flight, all loaded before use: rows past the
+    // chunk load its last row again (a max does not change)
+    for (int r = r0 + rs; r < r1; r += 4 * RPI) {
+        uint4 w4[4];
 #pragma unroll
-        for (int e = 0; e < 8; e++) m[e] = fmaxf(m[e], fabsf(x[e]));
+        for (int u = 0; u < 4; u++)
+            w4[u] = *reinterpret_cast<const uint4*>(v + ((size_t)bh * L + min(r + u * RPI, r1 - 1)) * D + cc * 8);
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            float x[8];
+            unpack8(w4[u], x);
+#pragma unroll
+            for (int e = 0; e < 8; e++) m[e] = fmaxf(m[e], fabsf(x[e]));
+        }
     }
 #pragma unroll
     for (int e = 0; e < 8; e++) red[rs][cc * 8 + e] = m[e];
@@ -169,8 +178,19 @@ __global__ void v_scale_finalize(const float* __restrict__ part, float* __restri
                                  float* __restrict__ vinv, int nvchunk) {
     const int bh = blockIdx.x, c = threadIdx.x;
     if (c >= D) return;
+    // eight chunk maxima per step, loaded before use
+    constexpr int U = 8;
+    const float* p = part + (size_t)bh * nvchunk * D + c;
     float A = 0.0f;
-    for (int i = 0; i < nvchunk; i++) A = fmaxf(A, part[((size_t)bh * nvchunk + i) * D + c]);
+    int i = 0;
+    for (; i + U <= nvchunk; i += U) {
+        float x[U];
+#pragma unroll
+        for (int u = 0; u < U; u++) x[u] = p[(size_t)(i + u) * D];
+#pragma unroll
+        for (int u = 0; u < U; u++) A = fmaxf(A, x[u]);
+    }
+    for (; i < nvchunk; i++) A = fmaxf(A, p[(size_t)i * D]);
     float s, inv;
     sage_scale(A, 448.0f, s, inv);
     vscale[(size_t)bh * D + c] = s;

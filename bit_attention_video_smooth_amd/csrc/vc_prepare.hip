@@ -26,24 +26,28 @@ __global__ __launch_bounds__(256) void k_colsum_partial(const uint16_t* __restri
                                                         double* __restrict__ partial, int L,
                                                         int nsplit) {
     constexpr int CPR = D / 8;        // 16-byte chunks per row
-    constexpr int RPI = 256 / CPR;    // rows per iteration
+    constexpr int RPI = 256 / CPR;    // rows per load instruction of the workgroup
+    constexpr int CH = 4 * RPI;       // rows per chunk: four loads per thread
     __shared__ double red[RPI][D + 1];
     const int split = blockIdx.x, bh = blockIdx.y;
     const int t = threadIdx.x, cc = t % CPR, rs = t / CPR;
-    const int chunk = (L + nsplit - 1) / nsplit;
-    const int r0 = split * chunk, r1 = min(L, r0 + chunk);
     const uint16_t* base = k + (size_t)bh * L * D;
     double acc[8];
 #pragma unroll
     for (int e = 0; e < 8; e++) acc[e] = 0.0;
-    // four rows per thread in flight: all loads of a step are issued before
-    // their sums
-    for (int r = r0 + rs; r < r1; r += 4 * RPI) {
+    // the head's chunks of CH rows are dealt round-robin to its splits, so
+    // at any time the splits of a head read one contiguous window of it (as
+    // a copy would) rather than nsplit distant streams; the four loads of a
+    // chunk are issued before their sums (fp64 sums of bf16 values are exact,
+    // so the order of the additions does not matter)
+    const int nch = (L + CH - 1) / CH;
+    for (int c = split; c < nch; c += nsplit) {
+        const int r = c * CH + rs;
         uint4 w4[4];
 #pragma unroll
         for (int u = 0; u < 4; u++) {
-            w4[u] = make_uint4(0, 0, 0, 0);  // rows past the chunk add 0
-            if (r + u * RPI < r1) w4[u] = *reinterpret_cast<const uint4*>(base + (size_t)(r + u * RPI) * D + cc * 8);
+            w4[u] = make_uint4(0, 0, 0, 0);  // rows past the head add 0
+            if (r + u * RPI < L) w4[u] = *reinterpret_cast<const uint4*>(base + (size_t)(r + u * RPI) * D + cc * 8);
         }
 #pragma unroll
         for (int u = 0; u < 4; u++) {

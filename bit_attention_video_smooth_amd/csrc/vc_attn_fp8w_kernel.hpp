@@ -72,7 +72,7 @@ __device__ __forceinline__ void split_bf16x8(const float (&x)[8], v8bf16& hi, v8
     }
 }
 
-template <int D, bool DUMP, bool SKIP, bool NAIVE>
+template <int D, bool DUMP, bool SKIP, bool NAIVE, int NWV>
 struct Fp8Wave32 {
     using T = Fp8Tile<D>;
     static constexpr int KS = D / 64;   // k-steps of S^T (64 channels each)
@@ -116,7 +116,7 @@ struct Fp8Wave32 {
         n = lane & 31;
         h = lane >> 5;
         grp = w >> 2;
-        q0 = qtile * ATTN_BM + w * QW;
+        q0 = qtile * (NWV * QW) + w * QW;
         L = a.L;
         nb = a.nb;
         Lp = (size_t)nb * BLK;
@@ -269,7 +269,7 @@ struct Fp8Wave32 {
     // in lane half h.  One LDS round trip per wave (its own 32 floats; a
     // wave's LDS accesses complete in order, so the reads see the write).
     __device__ __forceinline__ void to_rows(float x, float (&out)[16]) const {
-        __shared__ float xb[NW * 32];
+        __shared__ float xb[NWV * 32];
         VC_LDS float* b = (VC_LDS float*)xb + w * 32;
         b[n] = x;  // lanes n and n + 32 store the same value
 #pragma unroll
@@ -467,11 +467,16 @@ struct Fp8Wave32 {
             });
         }
         if ((kb & 15) == 15 || kb == nb - 1) flush_means(kb);
-        if (LOADER) {
-            if (DUMP)
-                wait_vmcnt<0>();
-            else
-                wait_vmcnt<LD::NLD_K>();
+        if (!LAG) {
+            // the K loaders wait for their part of block kb + 1; a third
+            // group (waves 8-11), which copies nothing, passes the barrier at
+            // the same point of its block
+            if (LOADER) {
+                if (DUMP)
+                    wait_vmcnt<0>();
+                else
+                    wait_vmcnt<LD::NLD_K>();
+            }
             block_barrier();
         }
     }
@@ -510,11 +515,17 @@ struct Fp8Wave32 {
     }
 };
 
-// One workgroup: 8 waves (Fp8Wave32), 256 queries of one head, the
-// four-stage ring and the history of block means.
-template <int D, bool OUT_BF16, bool DUMP, bool SKIP, bool NAIVE>
-__global__ __launch_bounds__(NW * 64, 2) void attn_fp8w_kernel(AttnArgs a) {
-    using WV = Fp8Wave32<D, DUMP, SKIP, NAIVE>;
+// One workgroup: NWV waves (Fp8Wave32), 32 NWV queries of one head, the
+// four-stage ring and the history of block means.  NWV = 8: two groups of
+// four waves, one per SIMD each (the K loaders and the lagging V loaders).
+// NWV = 12 (d = 64, where registers allow three waves per SIMD): a third
+// group that copies nothing and keeps the first group's schedule; every
+// wave passes one barrier per block either way, and the third group leaves
+// each stage no later than the first, so the ring's reuse rules hold as
+// they are.  A wave's arithmetic does not depend on NWV.
+template <int D, bool OUT_BF16, bool DUMP, bool SKIP, bool NAIVE, int NWV>
+__global__ __launch_bounds__(NWV * 64, NWV / 4) void attn_fp8w_kernel(AttnArgs a) {
+    using WV = Fp8Wave32<D, DUMP, SKIP, NAIVE, NWV>;
     using LD = Fp8Loader<D, REC_VC, true>;
     using T = Fp8Tile<D>;
     __shared__ __attribute__((aligned(16))) uint8_t st0_[T::STAGE];
@@ -529,7 +540,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fp8w_kernel(AttnArgs a) {
     // wave index as a scalar (uniform) value
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     // history slots not yet copied hold zeros (their W is zero too)
-    for (int i = threadIdx.x; i < WV::NHIST * D; i += NW * 64) hist_[i] = 0.f;
+    for (int i = threadIdx.x; i < WV::NHIST * D; i += NWV * 64) hist_[i] = 0.f;
     WV s(a, bh, qtile, w, lane, (const VC_LDS float*)hist_);
     const LD ld(a, bh, w, lane, (VC_LDS float*)hist_);
     const int nb = a.nb;
@@ -541,7 +552,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fp8w_kernel(AttnArgs a) {
         ld.issue_k(st[0], 0);
         ld.issue_k(st[1], min(1, nb - 1));
         wait_vmcnt<LD::NLD_K>();
-    } else {
+    } else if (s.grp == 1) {
         ld.issue_v(st[0], 0);
         ld.issue_v(st[1], min(1, nb - 1));
         ld.issue_v(st[2], min(2, nb - 1));
@@ -550,16 +561,35 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fp8w_kernel(AttnArgs a) {
     block_barrier();
     if (s.grp == 0)
         s.template run<true, false>(ld, st);
-    else
+    else if (s.grp == 1)
         s.template run<false, true>(ld, st);
+    else
+        s.template run<false, false>(ld, st);
     wait_vmcnt<0>();
     s.template store<OUT_BF16>();
 }
 
+template <int D, bool OB, bool DUMP, bool SKIP, bool NAIVE, int NWV>
+hipError_t launch_w32_n(const AttnArgs& a, hipStream_t st) {
+    AttnArgs b = a;
+    b.nqt = (a.L + NWV * QW - 1) / (NWV * QW);
+    hipLaunchKernelGGL((attn_fp8w_kernel<D, OB, DUMP, SKIP, NAIVE, NWV>), dim3(b.BH * b.nqt), dim3(NWV * 64), 0, st,
+                       b);
+    return hipGetLastError();
+}
+
+// d = 64 runs 12-wave workgroups of 384 queries when the grid fills the chip
+// several times over (three waves per SIMD issue the vector work of the
+// softmax faster; a few workgroups alone are quicker at 8 waves), except with
+// the score dump (which addresses 256-query tiles, as the ABI defines them)
+// and with Skip Softmax (whose rejection state does not fit the 168
+// registers of three waves per SIMD without spilling inside the block loop)
 template <int D, bool OB, bool DUMP, bool SKIP, bool NAIVE>
 hipError_t launch_w32(const AttnArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL((attn_fp8w_kernel<D, OB, DUMP, SKIP, NAIVE>), dim3(a.BH * a.nqt), dim3(NW * 64), 0, st, a);
-    return hipGetLastError();
+    if constexpr (D == 64 && !DUMP && !SKIP) {
+        if ((int64_t)a.BH * a.nqt >= 1024) return launch_w32_n<D, OB, DUMP, SKIP, NAIVE, 12>(a, st);
+    }
+    return launch_w32_n<D, OB, DUMP, SKIP, NAIVE, 8>(a, st);
 }
 
 }  // namespace

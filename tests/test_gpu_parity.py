@@ -519,6 +519,43 @@ def test_dump_instances_compute_what_plain_ones_do(api, d):
         assert torch.equal(a, b), name
 
 
+# ------------------------------------ d = 64 at 12 waves per workgroup --
+
+def test_d64_wide_workgroups_match_eight_wave_instance(api):
+    """At d = 64 a grid of at least 1024 256-query workgroups runs 12-wave
+    workgroups of 384 queries (three waves per SIMD); each wave computes what
+    it computes in the 8-wave instance, so the whole output must equal the
+    8-wave (dump) instance's bit for bit, for ExpCast and exp-then-cast bytes
+    and both output types, with ragged last query tiles of both sizes and a
+    partial last key block.  The last 384-query tile of the last head is then
+    held to the oracle: bytes bit-exact given the kernel's scores, the
+    given-S bar, one-code flips only."""
+    B, H, L, d = 1, 64, 4100, 64          # 64 * ceil(4100 / 256) = 1088 >= 1024
+    q, k, v = _inputs(B, H, L, d, 123, None)
+    perm = synth.random_perms(B, H, L, 124)
+    P = api.prepare(dev_bf16(q), dev_bf16(k), dev_bf16(v), perm_in=torch.from_numpy(perm).cuda())
+    for pc in (0, 1):
+        b = api.attention_dump(P, H - 1, 0, prob_cast=pc)[0]   # fp32 output of the 8-wave instance
+        for od in (torch.float32, torch.bfloat16):
+            a = api.attention(P, prob_cast=pc, out_dtype=od)
+            torch.cuda.synchronize()
+            assert torch.equal(a, b.to(od)), (pc, od)      # bf16 output: bf16 of the fp32 output
+    out = api.attention(P).cpu().numpy()
+    r0 = (L - 1) // 384 * 384                 # 3840: the last 384-query tile, 260 rows
+    o = _oracle_prep(q, k, v, perm, 0, H - 1)
+    # the kernel's scores and bytes of those rows: 256-query dump tiles 15 and 16
+    Ss, Ps = [], []
+    for qt in (15, 16):
+        _, S, Pb = api.attention_dump(P, H - 1, qt)
+        n = min(L, qt * 256 + 256) - qt * 256
+        Ss.append(S.cpu().numpy()[:n])
+        Ps.append(Pb.cpu().numpy()[:n])
+    S = np.concatenate(Ss)[r0 - 15 * 256:]
+    Pb = np.concatenate(Ps)[r0 - 15 * 256:]
+    ref, refS, delta, flips = explain_vsmooth_rows(o, L, (r0, L), S, Pb)
+    check_explained("d64 wide tile", out[0, H - 1, r0:], ref, refS, delta, flips)
+
+
 # ------------------------------------------------------- extreme inputs --
 
 def _extreme_inputs(case, L=700, d=128, seed=91):
